@@ -1,0 +1,390 @@
+// Host side of the C ABI in include/gdn.h: validation, buffer layouts, saved-set tagging and the
+// launch sequence of each call. No device memory is allocated or freed here and nothing
+// synchronises; every launch goes to the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+int launch_write_tag(void* dst, const uint64_t* words, void* stream);
+}
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int kChunk = 64;
+constexpr size_t kAlign = 256;
+constexpr size_t kTagBytes = 256;
+constexpr uint64_t kMagic = 0x31564153'4e4447ULL; // "GDNSAV1"
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Sizes {
+  int64_t T;
+  int N, H, HV, D, NT;
+};
+
+// Validates the descriptor and its host cu_seqlens; fills sizes. Returns GDN_OK or an error.
+int check_problem(const gdn_problem* p, Sizes* s) {
+  if (!p) return fail(GDN_EINVAL, "problem descriptor is NULL");
+  if (p->n_seqs < 1) return fail(GDN_EINVAL, "n_seqs must be >= 1 (got %d)", p->n_seqs);
+  if (p->h_qk < 1 || p->h_v < 1) return fail(GDN_EINVAL, "head counts must be >= 1");
+  if (p->h_v % p->h_qk != 0) return fail(GDN_EINVAL, "h_v (%d) must be a multiple of h_qk (%d)", p->h_v, p->h_qk);
+  if (p->d != 64 && p->d != 128) return fail(GDN_EUNSUPPORTED, "d must be 64 or 128 (got %d)", p->d);
+  if (p->dtype != GDN_DTYPE_BF16 && p->dtype != GDN_DTYPE_F32)
+    return fail(GDN_EUNSUPPORTED, "unsupported dtype %d", p->dtype);
+  if (p->save_mode != GDN_SAVE_LIGHT && p->save_mode != GDN_SAVE_FULL)
+    return fail(GDN_EINVAL, "save_mode must be light (0) or full (1)");
+  if (!p->cu_seqlens_host) return fail(GDN_EINVAL, "cu_seqlens_host is NULL");
+  const int32_t* cu = p->cu_seqlens_host;
+  if (cu[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0] must be 0");
+  int64_t nt = 0;
+  for (int n = 0; n < p->n_seqs; ++n) {
+    if (cu[n + 1] < cu[n]) return fail(GDN_EINVAL, "cu_seqlens decreases at %d", n);
+    nt += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+  }
+  if ((int64_t)cu[p->n_seqs] != p->n_tokens)
+    return fail(GDN_EINVAL, "cu_seqlens[N] = %d but n_tokens = %lld", cu[p->n_seqs], (long long)p->n_tokens);
+  if (nt > (int64_t)0x7fffffff / 64) return fail(GDN_EINVAL, "too many chunks");
+  if ((int64_t)p->n_seqs * p->h_qk > (int64_t)0x0fffffff) return fail(GDN_EINVAL, "too many documents x heads");
+  s->T = p->n_tokens;
+  s->N = p->n_seqs;
+  s->H = p->h_qk;
+  s->HV = p->h_v;
+  s->D = p->d;
+  s->NT = (int)nt;
+  return GDN_OK;
+}
+
+struct SavedLayout {
+  size_t akk, gcum, gamma, htape, vnew, w, u, aqk, total;
+};
+
+SavedLayout saved_layout(const Sizes& s, int full) {
+  SavedLayout L{};
+  size_t off = kTagBytes;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.akk = take((size_t)s.T * s.HV * kChunk * 2);
+  L.gcum = take((size_t)s.T * s.HV * 4);
+  L.gamma = take((size_t)s.NT * s.HV * 4);
+  if (full) {
+    L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
+    L.vnew = take((size_t)s.T * s.HV * s.D * 2);
+    L.w = take((size_t)s.T * s.HV * s.D * 2);
+    L.u = take((size_t)s.T * s.HV * s.D * 2);
+    L.aqk = take((size_t)s.T * s.HV * kChunk * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+struct WorkLayout {
+  size_t seq_c0, c_t0, c_len, seq_order, status, rk, rq, qk, htape, dstape, dqacc, dkacc, total;
+};
+
+WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
+  WorkLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.seq_c0 = take((size_t)(s.N + 1) * 4);
+  L.c_t0 = take((size_t)s.NT * 4);
+  L.c_len = take((size_t)s.NT * 4);
+  L.seq_order = take((size_t)s.N * 4);
+  L.status = take(4);
+  L.rk = take((size_t)s.T * s.H * 4);
+  L.rq = take((size_t)s.T * s.H * 4);
+  L.qk = take((size_t)s.NT * s.H * kChunk * kChunk * 2);
+  if (op == GDN_OP_BWD) {
+    if (!full) L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
+    L.dstape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
+    if (!deterministic) {
+      L.dqacc = take((size_t)s.T * s.H * s.D * 4);
+      L.dkacc = take((size_t)s.T * s.H * s.D * 4);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+uint64_t fnv(uint64_t h, const void* data, size_t n) {
+  const unsigned char* b = (const unsigned char*)data;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= b[i];
+    h *= 1099511628211ULL;
+  }
+  return h;
+}
+
+uint64_t problem_hash(const gdn_problem* p) {
+  uint64_t h = 1469598103934665603ULL;
+  const int32_t f[] = {p->n_seqs, p->h_qk, p->h_v, p->d, p->dtype, p->l2norm_qk, p->has_h0, p->save_mode};
+  h = fnv(h, f, sizeof f);
+  h = fnv(h, &p->n_tokens, sizeof p->n_tokens);
+  h = fnv(h, p->cu_seqlens_host, sizeof(int32_t) * (size_t)(p->n_seqs + 1));
+  return h;
+}
+
+// Saved buffers written by gdn_fwd / gdn_fwd_recompute in this process, with the hash of the
+// problem they were written for. gdn_bwd refuses a buffer that is not listed under the hash of
+// its own problem.
+std::mutex g_reg_mu;
+std::unordered_map<const void*, uint64_t> g_registry;
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int check_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(GDN_EINVAL, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(GDN_EINVAL, "%s is not 16-byte aligned", name);
+  return GDN_OK;
+}
+
+#define CHECK(x)                     \
+  do {                               \
+    const int rc_ = (x);             \
+    if (rc_ != GDN_OK) return rc_;   \
+  } while (0)
+
+#define LAUNCH(x)                                                                        \
+  do {                                                                                   \
+    const int e_ = (x);                                                                  \
+    if (e_ != 0) return fail(GDN_EHIP, "%s: %s", #x, hipGetErrorString((hipError_t)e_)); \
+  } while (0)
+
+void fill_common(gdn::Args& a, const Sizes& s, const gdn_problem* p) {
+  std::memset(&a, 0, sizeof a);
+  a.N = s.N;
+  a.H = s.H;
+  a.HV = s.HV;
+  a.G = s.HV / s.H;
+  a.D = s.D;
+  a.NT = s.NT;
+  a.T = s.T;
+  a.dtype = p->dtype;
+  a.l2norm = p->l2norm_qk ? 1 : 0;
+  a.has_h0 = p->has_h0 ? 1 : 0;
+  a.want_ht = p->want_ht ? 1 : 0;
+  a.full = p->save_mode == GDN_SAVE_FULL ? 1 : 0;
+}
+
+void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
+  char* b = (char*)ws;
+  a.seq_c0 = (int*)(b + W.seq_c0);
+  a.c_t0 = (int*)(b + W.c_t0);
+  a.c_len = (int*)(b + W.c_len);
+  a.seq_order = (int*)(b + W.seq_order);
+  a.status = (int*)(b + W.status);
+  a.rk = (float*)(b + W.rk);
+  a.rq = (float*)(b + W.rq);
+  a.qk = (uint16_t*)(b + W.qk);
+  if (W.htape) a.htape = (uint16_t*)(b + W.htape);
+  if (W.dstape) a.dstape = (uint16_t*)(b + W.dstape);
+  if (W.dqacc) a.dqacc = (float*)(b + W.dqacc);
+  if (W.dkacc) a.dkacc = (float*)(b + W.dkacc);
+}
+
+void bind_saved(gdn::Args& a, const SavedLayout& L, void* saved) {
+  char* b = (char*)saved;
+  a.akk = (uint16_t*)(b + L.akk);
+  a.gcum = (float*)(b + L.gcum);
+  a.gamma = (float*)(b + L.gamma);
+  if (L.htape) {
+    a.htape = (uint16_t*)(b + L.htape);
+    a.vnew = (uint16_t*)(b + L.vnew);
+    a.w = (uint16_t*)(b + L.w);
+    a.u = (uint16_t*)(b + L.u);
+    a.aqk = (uint16_t*)(b + L.aqk);
+  }
+}
+
+int check_inputs(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                 const float* beta, const int32_t* cu, const float* h0) {
+  CHECK(check_ptr(q, "q"));
+  CHECK(check_ptr(k, "k"));
+  CHECK(check_ptr(v, "v"));
+  CHECK(check_ptr(g, "g"));
+  CHECK(check_ptr(beta, "beta"));
+  CHECK(check_ptr(cu, "cu_seqlens"));
+  if (p->has_h0) CHECK(check_ptr(h0, "h0"));
+  return GDN_OK;
+}
+
+// Forward and recompute share everything but o/ht.
+int forward_common(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const int32_t* cu, const float* h0, void* o, float* ht, void* saved,
+                   void* workspace, size_t workspace_bytes, void* stream, bool write_o) {
+  Sizes s;
+  CHECK(check_problem(p, &s));
+  CHECK(check_inputs(p, q, k, v, g, beta, cu, h0));
+  if (write_o) {
+    CHECK(check_ptr(o, "o"));
+    if (p->want_ht) CHECK(check_ptr(ht, "ht"));
+  }
+  CHECK(check_ptr(saved, "saved"));
+  CHECK(check_ptr(workspace, "workspace"));
+  const int full = p->save_mode == GDN_SAVE_FULL;
+  const WorkLayout W = work_layout(s, write_o ? GDN_OP_FWD : GDN_OP_RECOMPUTE, full, p->deterministic);
+  if (workspace_bytes < W.total)
+    return fail(GDN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
+  const SavedLayout L = saved_layout(s, full);
+  gdn::Args a;
+  fill_common(a, s, p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu;
+  a.h0 = p->has_h0 ? h0 : nullptr;
+  a.o = o;
+  a.ht = (write_o && p->want_ht) ? ht : nullptr;
+  if (!write_o) a.want_ht = 0;
+  bind_workspace(a, W, workspace);
+  bind_saved(a, L, saved);
+
+  LAUNCH(gdn::launch_tables(a, stream));
+  LAUNCH(gdn::launch_intra(a, 0, stream));
+  if (write_o) LAUNCH(gdn::launch_walk_fwd(a, 1, full, stream));
+  else if (full) LAUNCH(gdn::launch_walk_fwd(a, 0, 1, stream));
+  if (full) LAUNCH(gdn::launch_wy_full(a, stream));
+  const uint64_t h = problem_hash(p);
+  const uint64_t words[4] = {kMagic, (uint64_t)GDN_ABI_VERSION, (uint64_t)p->save_mode, h};
+  LAUNCH(gdn::launch_write_tag(saved, words, stream));
+  {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    g_registry[saved] = h;
+  }
+  g_err.clear();
+  return GDN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t gdn_saved_bytes(const gdn_problem* p) {
+  Sizes s;
+  if (check_problem(p, &s) != GDN_OK) return 0;
+  return saved_layout(s, p->save_mode == GDN_SAVE_FULL).total;
+}
+
+size_t gdn_workspace_bytes(const gdn_problem* p, int op) {
+  Sizes s;
+  if (check_problem(p, &s) != GDN_OK) return 0;
+  if (op != GDN_OP_FWD && op != GDN_OP_RECOMPUTE && op != GDN_OP_BWD) {
+    fail(GDN_EINVAL, "unknown op %d", op);
+    return 0;
+  }
+  return work_layout(s, op, p->save_mode == GDN_SAVE_FULL, p->deterministic).total;
+}
+
+int gdn_fwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g, const float* beta,
+            const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* saved, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  return forward_common(p, q, k, v, g, beta, cu_seqlens, h0, o, ht, saved, workspace, workspace_bytes, stream,
+                        true);
+}
+
+int gdn_fwd_recompute(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const int32_t* cu_seqlens, const float* h0, void* saved, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return forward_common(p, q, k, v, g, beta, cu_seqlens, h0, nullptr, nullptr, saved, workspace, workspace_bytes,
+                        stream, false);
+}
+
+int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g, const float* beta,
+            const int32_t* cu_seqlens, const float* h0, const void* saved, const void* dO, const float* dht,
+            void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  Sizes s;
+  CHECK(check_problem(p, &s));
+  CHECK(check_inputs(p, q, k, v, g, beta, cu_seqlens, h0));
+  CHECK(check_ptr(saved, "saved"));
+  CHECK(check_ptr(dO, "dO"));
+  if (dht) CHECK(check_ptr(dht, "dht"));
+  CHECK(check_ptr(dq, "dq"));
+  CHECK(check_ptr(dk, "dk"));
+  CHECK(check_ptr(dv, "dv"));
+  CHECK(check_ptr(dg, "dg"));
+  CHECK(check_ptr(dbeta, "dbeta"));
+  if (p->has_h0) CHECK(check_ptr(dh0, "dh0"));
+  CHECK(check_ptr(workspace, "workspace"));
+  {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    auto it = g_registry.find(saved);
+    if (it == g_registry.end())
+      return fail(GDN_ESAVED, "saved buffer was not written by gdn_fwd/gdn_fwd_recompute in this process");
+    if (it->second != problem_hash(p))
+      return fail(GDN_ESAVED, "saved buffer was written for a different problem or save_mode");
+  }
+  const int full = p->save_mode == GDN_SAVE_FULL;
+  const WorkLayout W = work_layout(s, GDN_OP_BWD, full, p->deterministic);
+  if (workspace_bytes < W.total)
+    return fail(GDN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
+  const SavedLayout L = saved_layout(s, full);
+  gdn::Args a;
+  fill_common(a, s, p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.h0 = p->has_h0 ? h0 : nullptr;
+  a.dO = dO;
+  a.dht = dht;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.dbeta = dbeta;
+  a.dh0 = p->has_h0 ? dh0 : nullptr;
+  bind_workspace(a, W, workspace);
+  bind_saved(a, L, const_cast<void*>(saved));
+  if (!full) a.htape = (uint16_t*)((char*)workspace + W.htape);
+
+  LAUNCH(gdn::launch_tables(a, stream));
+  LAUNCH(gdn::launch_intra(a, 1, stream));
+  if (!full) LAUNCH(gdn::launch_walk_fwd(a, 0, 1, stream));
+  LAUNCH(gdn::launch_walk_bwd(a, stream));
+  if (!p->deterministic) {
+    LAUNCH(gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
+    LAUNCH(gdn::launch_fill_zero(a.dkacc, (size_t)s.T * s.H * s.D, stream));
+  }
+  LAUNCH(gdn::launch_chunk_grad(a, p->deterministic, stream));
+  if (!p->deterministic) LAUNCH(gdn::launch_finalize_qk(a, stream));
+  g_err.clear();
+  return GDN_OK;
+}
+
+const char* gdn_last_error(void) { return g_err.c_str(); }
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+} // extern "C"

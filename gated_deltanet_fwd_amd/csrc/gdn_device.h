@@ -1,0 +1,127 @@
+// Device-side building blocks for the gfx950 (CDNA4) kernels: bf16 MFMA tiles, io loads,
+// wave shuffles. Wave size is 64; every kernel runs 256 threads = 4 waves.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;        // chunk length (tokens)
+constexpr int NTHREADS = 256; // threads per workgroup
+constexpr int PAD = 8;        // bf16 elements of row padding in LDS tiles (keeps 16-byte rows aligned)
+
+// v_mfma_f32_16x16x32_bf16: C[16x16] += A[16x32] B[32x16].
+// Lane l holds A[l % 16][(l / 16) * 8 + e] and B[(l / 16) * 8 + e][l % 16] for e = 0..7, and
+// C[(l / 16) * 4 + i][l % 16] for i = 0..3 (layout checked on gfx950 by a lane probe).
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.f;
+  return z;
+}
+
+// Fragment read from an LDS tile stored row-major with `stride` elements per row:
+// 8 consecutive elements of row `row` starting at column `col` (16-byte aligned).
+__device__ __forceinline__ bf16x8 lds8(const bf16* base, int stride, int row, int col) {
+  return *reinterpret_cast<const bf16x8*>(base + row * stride + col);
+}
+
+// Store 4 values of one column, rows r..r+3, into an LDS tile stored transposed
+// (tile[col][row]): one 8-byte write.
+__device__ __forceinline__ void lds_store4_t(bf16* base, int stride, int col, int row, float a, float b, float c,
+                                             float d) {
+  bf16x4 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  v[2] = (bf16)c;
+  v[3] = (bf16)d;
+  *reinterpret_cast<bf16x4*>(base + col * stride + row) = v;
+}
+
+// ---------------------------------------------------------------------------------------
+// io dtype access (bf16 or f32)
+
+template <typename T>
+struct IO;
+
+template <>
+struct IO<bf16> {
+  static __device__ __forceinline__ void load8f(const bf16* p, float out[8]) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
+  }
+  static __device__ __forceinline__ bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  static __device__ __forceinline__ float load1(const bf16* p) { return (float)*p; }
+  static __device__ __forceinline__ void store1(bf16* p, float x) { *p = (bf16)x; }
+};
+
+template <>
+struct IO<float> {
+  static __device__ __forceinline__ void load8f(const float* p, float out[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+  static __device__ __forceinline__ bf16x8 load8(const float* p) {
+    float f[8];
+    load8f(p, f);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)f[e];
+    return r;
+  }
+  static __device__ __forceinline__ float load1(const float* p) { return *p; }
+  static __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
+};
+
+// Sum over the 16 lanes that share l / 16 (the lanes of one MFMA output row group).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
+// Chain index -> (document rank, q/k head, v head within the group, value tile), with
+// workgroups that read the same q/k tiles placed on the same XCD. Workgroups are dealt to
+// the 8 XCDs round-robin by workgroup id, so a group of GS chains (one q/k head of one
+// document: its G value heads times the value tiles) gets ids that agree mod 8; groups are
+// taken 8 at a time in longest-document-first order.
+struct ChainMap {
+  int rank, j, gi, tile;
+  bool valid;
+};
+__device__ __forceinline__ ChainMap decode_chain(int b, int N, int H, int G, int ntile) {
+  const int GS = G * ntile;
+  const int sg = b / (8 * GS);
+  const int rem = b - sg * 8 * GS;
+  const int x = rem & 7;
+  const int s = rem >> 3;
+  const long group = (long)sg * 8 + x; // (rank, j) in rank-major order
+  ChainMap m;
+  m.valid = group < (long)N * H;
+  const int grp = (int)group;
+  m.rank = grp / H;
+  m.j = grp - m.rank * H;
+  m.gi = s / ntile;
+  m.tile = s - m.gi * ntile;
+  return m;
+}
+
+} // namespace gdn

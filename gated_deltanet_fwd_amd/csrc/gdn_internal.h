@@ -1,0 +1,74 @@
+// Internal (host + device) description of one call: sizes and every device pointer the
+// kernels touch. Passed to kernels by value.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct Args {
+  // sizes
+  int N, H, HV, G, D, NT;
+  int64_t T;
+  int dtype; // 0 bf16, 1 f32 (io tensors)
+  int l2norm, has_h0, want_ht, full;
+  // inputs
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const int32_t* cu;
+  const float* h0;
+  const void* dO;
+  const float* dht;
+  // outputs
+  void* o;
+  float* ht;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;
+  // saved set
+  uint16_t* akk;   // bf16 [T, HV, 64]: row i of the chunk's (I + L)^-1 at the token of row i
+  float* gcum;     // f32  [T, HV]: in-chunk inclusive cumulative log decay
+  float* gamma;    // f32  [NT, HV]: exp(gcum of the chunk's last token)
+  uint16_t* htape; // bf16 [NT, HV, d(value), d(key)]: state at each chunk start, transposed
+  uint16_t* vnew;  // bf16 [T, HV, d]: R = U - W S (full form only)
+  uint16_t* w;     // bf16 [T, HV, d] (full form only)
+  uint16_t* u;     // bf16 [T, HV, d] (full form only)
+  uint16_t* aqk;   // bf16 [T, HV, 64]: decayed, masked q.k (full form only)
+  // workspace
+  int* seq_c0;     // [N + 1] first chunk of each document
+  int* c_t0;       // [NT] first token of each chunk
+  int* c_len;      // [NT] valid tokens of each chunk (1..64)
+  int* seq_order;  // [N] documents, longest first
+  int* status;     // [1] nonzero if the device tables disagree with the host's chunk count
+  float* rk;       // [T, H] inverse L2 norms of k rows (1 when the norm is off)
+  float* rq;       // [T, H] inverse L2 norms of q rows
+  uint16_t* qk;    // bf16 [NT, H, 64, 64] normalised q.k per chunk (row-major fwd, transposed bwd)
+  uint16_t* dstape;// bf16 [NT, HV, d(value), d(key)]: gradient of each chunk's end state, transposed
+  float* dqacc;    // f32 [T, H, d] (atomic reduction only)
+  float* dkacc;    // f32 [T, H, d] (atomic reduction only)
+};
+
+// Value-column tile width of the forward state walk (columns of S per workgroup).
+constexpr int WALK_DVT = 32;
+// Value-column tile width of the reverse walk.
+constexpr int BWALK_DVT = 32;
+
+int chain_blocks(const Args& a, int ntile);
+
+// Launchers (defined in the .hip translation units). Each returns a hipError_t as int.
+int launch_tables(const Args& a, void* stream);
+int launch_intra(const Args& a, int bwd_prep, void* stream);
+int launch_walk_fwd(const Args& a, int write_o, int write_tape, void* stream);
+int launch_wy_full(const Args& a, void* stream);
+int launch_walk_bwd(const Args& a, void* stream);
+int launch_chunk_grad(const Args& a, int deterministic, void* stream);
+int launch_fill_zero(float* p, size_t n, void* stream);
+int launch_finalize_qk(const Args& a, void* stream);
+
+} // namespace gdn
