@@ -6,9 +6,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
+#include <map>
 #include <mutex>
 #include <string>
 #include <unordered_map>
+#include <vector>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -171,9 +174,43 @@ int check_ptr(const void* ptr, const char* name) {
     if (rc_ != GDN_OK) return rc_;   \
   } while (0)
 
-#define LAUNCH(x)                                                                        \
+// Optional kernel timing for benchmarks: while enabled, each launch is bracketed by two
+// hipEvents recorded on the call's stream; gdn_timing_collect waits for them and sums the
+// elapsed time per kernel name.
+std::atomic<int> g_timing_on{0};
+std::mutex g_timing_mu;
+struct PendingEvent {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::vector<PendingEvent> g_pending;
+std::map<std::string, std::pair<double, int>> g_totals;
+
+hipEvent_t timing_begin(void* stream) {
+  if (!g_timing_on.load(std::memory_order_relaxed)) return nullptr;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  hipEventRecord(e, (hipStream_t)stream);
+  return e;
+}
+
+void timing_end(const char* name, hipEvent_t start, void* stream) {
+  if (!start) return;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    hipEventDestroy(start);
+    return;
+  }
+  hipEventRecord(e, (hipStream_t)stream);
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_pending.push_back({name, start, e});
+}
+
+#define LAUNCH(name, x)                                                                  \
   do {                                                                                   \
+    hipEvent_t t0_ = timing_begin(stream);                                               \
     const int e_ = (x);                                                                  \
+    timing_end(name, t0_, stream);                                                       \
     if (e_ != 0) return fail(GDN_EHIP, "%s: %s", #x, hipGetErrorString((hipError_t)e_)); \
   } while (0)
 
@@ -223,13 +260,20 @@ void bind_saved(gdn::Args& a, const SavedLayout& L, void* saved) {
   }
 }
 
+// Per-token tensors may be NULL when there are no tokens.
+int check_tok(const void* ptr, const char* name, int64_t T) {
+  if (T == 0 && !ptr) return GDN_OK;
+  return check_ptr(ptr, name);
+}
+
 int check_inputs(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
                  const float* beta, const int32_t* cu, const float* h0) {
-  CHECK(check_ptr(q, "q"));
-  CHECK(check_ptr(k, "k"));
-  CHECK(check_ptr(v, "v"));
-  CHECK(check_ptr(g, "g"));
-  CHECK(check_ptr(beta, "beta"));
+  const int64_t T = p->n_tokens;
+  CHECK(check_tok(q, "q", T));
+  CHECK(check_tok(k, "k", T));
+  CHECK(check_tok(v, "v", T));
+  CHECK(check_tok(g, "g", T));
+  CHECK(check_tok(beta, "beta", T));
   CHECK(check_ptr(cu, "cu_seqlens"));
   if (p->has_h0) CHECK(check_ptr(h0, "h0"));
   return GDN_OK;
@@ -243,7 +287,7 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
   CHECK(check_problem(p, &s));
   CHECK(check_inputs(p, q, k, v, g, beta, cu, h0));
   if (write_o) {
-    CHECK(check_ptr(o, "o"));
+    CHECK(check_tok(o, "o", s.T));
     if (p->want_ht) CHECK(check_ptr(ht, "ht"));
   }
   CHECK(check_ptr(saved, "saved"));
@@ -268,14 +312,14 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
   bind_workspace(a, W, workspace);
   bind_saved(a, L, saved);
 
-  LAUNCH(gdn::launch_tables(a, stream));
-  LAUNCH(gdn::launch_intra(a, 0, stream));
-  if (write_o) LAUNCH(gdn::launch_walk_fwd(a, 1, full, stream));
-  else if (full) LAUNCH(gdn::launch_walk_fwd(a, 0, 1, stream));
-  if (full) LAUNCH(gdn::launch_wy_full(a, stream));
+  LAUNCH("gdn_tables", gdn::launch_tables(a, stream));
+  LAUNCH("gdn_intra", gdn::launch_intra(a, 0, stream));
+  if (write_o) LAUNCH("gdn_walk_fwd", gdn::launch_walk_fwd(a, 1, full, stream));
+  else if (full) LAUNCH("gdn_walk_tape", gdn::launch_walk_fwd(a, 0, 1, stream));
+  if (full) LAUNCH("gdn_wy_full", gdn::launch_wy_full(a, stream));
   const uint64_t h = problem_hash(p);
   const uint64_t words[4] = {kMagic, (uint64_t)GDN_ABI_VERSION, (uint64_t)p->save_mode, h};
-  LAUNCH(gdn::launch_write_tag(saved, words, stream));
+  LAUNCH("gdn_write_tag", gdn::launch_write_tag(saved, words, stream));
   {
     std::lock_guard<std::mutex> lk(g_reg_mu);
     g_registry[saved] = h;
@@ -326,13 +370,13 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   CHECK(check_problem(p, &s));
   CHECK(check_inputs(p, q, k, v, g, beta, cu_seqlens, h0));
   CHECK(check_ptr(saved, "saved"));
-  CHECK(check_ptr(dO, "dO"));
+  CHECK(check_tok(dO, "dO", s.T));
   if (dht) CHECK(check_ptr(dht, "dht"));
-  CHECK(check_ptr(dq, "dq"));
-  CHECK(check_ptr(dk, "dk"));
-  CHECK(check_ptr(dv, "dv"));
-  CHECK(check_ptr(dg, "dg"));
-  CHECK(check_ptr(dbeta, "dbeta"));
+  CHECK(check_tok(dq, "dq", s.T));
+  CHECK(check_tok(dk, "dk", s.T));
+  CHECK(check_tok(dv, "dv", s.T));
+  CHECK(check_tok(dg, "dg", s.T));
+  CHECK(check_tok(dbeta, "dbeta", s.T));
   if (p->has_h0) CHECK(check_ptr(dh0, "dh0"));
   CHECK(check_ptr(workspace, "workspace"));
   {
@@ -369,18 +413,57 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   bind_saved(a, L, const_cast<void*>(saved));
   if (!full) a.htape = (uint16_t*)((char*)workspace + W.htape);
 
-  LAUNCH(gdn::launch_tables(a, stream));
-  LAUNCH(gdn::launch_intra(a, 1, stream));
-  if (!full) LAUNCH(gdn::launch_walk_fwd(a, 0, 1, stream));
-  LAUNCH(gdn::launch_walk_bwd(a, stream));
+  LAUNCH("gdn_tables", gdn::launch_tables(a, stream));
+  LAUNCH("gdn_intra_bwd", gdn::launch_intra(a, 1, stream));
+  if (!full) LAUNCH("gdn_walk_tape", gdn::launch_walk_fwd(a, 0, 1, stream));
+  LAUNCH("gdn_walk_bwd", gdn::launch_walk_bwd(a, stream));
   if (!p->deterministic) {
-    LAUNCH(gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
-    LAUNCH(gdn::launch_fill_zero(a.dkacc, (size_t)s.T * s.H * s.D, stream));
+    LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
+    LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dkacc, (size_t)s.T * s.H * s.D, stream));
   }
-  LAUNCH(gdn::launch_chunk_grad(a, p->deterministic, stream));
-  if (!p->deterministic) LAUNCH(gdn::launch_finalize_qk(a, stream));
+  LAUNCH("gdn_chunk_grad", gdn::launch_chunk_grad(a, p->deterministic, stream));
+  if (!p->deterministic) LAUNCH("gdn_finalize_qk", gdn::launch_finalize_qk(a, stream));
   g_err.clear();
   return GDN_OK;
+}
+
+void gdn_timing_enable(int on) { g_timing_on.store(on ? 1 : 0); }
+
+int gdn_timing_collect(int max, const char** names, double* total_ms, int* launches) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (const PendingEvent& p : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.stop) == hipSuccess && hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+      auto& t = g_totals[p.name];
+      t.first += ms;
+      t.second += 1;
+    }
+    hipEventDestroy(p.start);
+    hipEventDestroy(p.stop);
+  }
+  g_pending.clear();
+  int i = 0;
+  for (const auto& kv : g_totals) {
+    if (i >= max) break;
+    static thread_local std::vector<std::string> keep;
+    if ((int)keep.size() < max) keep.resize(max);
+    keep[i] = kv.first;
+    if (names) names[i] = keep[i].c_str();
+    if (total_ms) total_ms[i] = kv.second.first;
+    if (launches) launches[i] = kv.second.second;
+    ++i;
+  }
+  return (int)g_totals.size();
+}
+
+void gdn_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (const PendingEvent& p : g_pending) {
+    hipEventDestroy(p.start);
+    hipEventDestroy(p.stop);
+  }
+  g_pending.clear();
+  g_totals.clear();
 }
 
 const char* gdn_last_error(void) { return g_err.c_str(); }

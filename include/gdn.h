@@ -127,6 +127,16 @@ const char* gdn_last_error(void);
 /* GDN_ABI_VERSION of the loaded library. */
 int gdn_abi_version(void);
 
+/* Kernel timing, for benchmarks. While enabled (on = 1), every kernel launch of the library is
+ * bracketed by two hipEvents recorded on the call's stream (no synchronisation at launch).
+ * gdn_timing_collect waits for all recorded events, adds their elapsed times to per-kernel
+ * totals and returns the number of distinct kernels; for the first `max` (in name order) it
+ * fills names (valid until the next collect on this thread), total_ms and launch counts (any
+ * array may be NULL). gdn_timing_reset drops totals and pending events. */
+void gdn_timing_enable(int on);
+int gdn_timing_collect(int max, const char** names, double* total_ms, int* launches);
+void gdn_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 oracle, plus bitwise invariants.
+
+Tolerances are the pages' accuracy budget (tests/golden/tolerance.json): rel-RMS <= 1e-2 and
+max-abs <= 2e-2 * max|ref| per tensor. Small cases compare every element; the full-size
+workloads run on the GPU exactly as the benchmark launches them and compare sampled documents
+and q/k-head groups, which the oracle computes independently of the rest.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_fwd_amd as G
+import synthetic as syn
+from parity_util import assert_close, host_inputs, oracle_bwd, oracle_fwd, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _dev(inp):
+    return {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+
+
+def _run(w, inp, save_mode=G.SAVE_LIGHT, det=None, bwd=True, recompute=False, poison=False, l2norm=None):
+    p = G.problem_for(w, save_mode=save_mode, deterministic=det, l2norm=l2norm)
+    a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
+    fill = float("nan") if poison else 0.0
+    o = torch.full_like(inp["v"], fill)
+    ht = torch.full((w.N, w.HV, w.d, w.d), fill, dtype=torch.float32, device=DEV) if w.want_ht else None
+    saved = torch.full((G.gdn_saved_bytes(p),), 255 if poison else 0, dtype=torch.uint8, device=DEV)
+    ws = torch.full((G.gdn_workspace_bytes(p, G.OP_FWD),), 255 if poison else 0, dtype=torch.uint8, device=DEV)
+    o, ht, saved = G.gdn_fwd(p, *a, h0=inp["h0"], o=o, ht=ht, saved=saved, workspace=ws)
+    out = dict(o=o, ht=ht, saved=saved, p=p)
+    if recompute:
+        saved2 = torch.full_like(saved, 255 if poison else 0)
+        ws2 = torch.full((G.gdn_workspace_bytes(p, G.OP_RECOMPUTE),), 255 if poison else 0, dtype=torch.uint8,
+                         device=DEV)
+        G.gdn_fwd_recompute(p, *a, h0=inp["h0"], saved=saved2, workspace=ws2)
+        out["saved_recompute"] = saved2
+    if bwd:
+        grads = dict(dq=torch.full_like(inp["q"], fill), dk=torch.full_like(inp["k"], fill),
+                     dv=torch.full_like(inp["v"], fill), dg=torch.full_like(inp["g"], fill),
+                     dbeta=torch.full_like(inp["beta"], fill),
+                     dh0=torch.full_like(inp["h0"], fill) if inp["h0"] is not None else None)
+        wsb = torch.full((G.gdn_workspace_bytes(p, G.OP_BWD),), 255 if poison else 0, dtype=torch.uint8, device=DEV)
+        G.gdn_bwd(p, *a, out.get("saved_recompute", saved), inp["dO"], h0=inp["h0"], dht=inp["dht"], grads=grads,
+                  workspace=wsb)
+        out.update(grads)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_all(w, inp, out, docs=None, heads=None, bwd=True, l2norm=None):
+    """Compare o, ht and the gradients on the sampled documents x q/k heads."""
+    l2 = w.l2norm if l2norm is None else l2norm
+    Gg = w.HV // w.H
+    h, ti, vh = host_inputs(inp, docs, heads, Gg)
+    hq = list(range(w.H)) if heads is None else list(heads)
+    dsel = list(range(w.N)) if docs is None else list(docs)
+    o_ref, ht_ref = oracle_fwd(h, l2)
+    assert_close("o", out["o"].index_select(0, ti)[:, vh], o_ref)
+    if out.get("ht") is not None:
+        assert_close("ht", out["ht"][dsel][:, vh], ht_ref)
+    if not bwd:
+        return
+    ref = oracle_bwd(h, l2)
+    assert_close("dq", out["dq"].index_select(0, ti)[:, hq], ref["dq"])
+    assert_close("dk", out["dk"].index_select(0, ti)[:, hq], ref["dk"])
+    assert_close("dv", out["dv"].index_select(0, ti)[:, vh], ref["dv"])
+    assert_close("dg", out["dg"].index_select(0, ti)[:, vh], ref["dg"])
+    assert_close("dbeta", out["dbeta"].index_select(0, ti)[:, vh], ref["dbeta"])
+    if out.get("dh0") is not None:
+        assert_close("dh0", out["dh0"][dsel][:, vh], ref["dh0"])
+
+
+# ------------------------------------------------------------------------------------------
+# small cases, every element
+
+
+@pytest.mark.parametrize("det", [True, False])
+@pytest.mark.parametrize("mode", [G.SAVE_LIGHT, G.SAVE_FULL])
+def test_tiny(det, mode):
+    w = syn.WORKLOADS["tiny"]
+    inp = _dev(syn.make_inputs(w))
+    out = _run(w, inp, save_mode=mode, det=det)
+    _check_all(w, inp, out)
+
+
+def test_tiny_prenormalised_without_kernel_norm():
+    """q, k L2-normalised on the host (same eps), kernel norm off: matches the oracle with the norm off."""
+    w = syn.WORKLOADS["tiny"]
+    inp = syn.make_inputs(w)
+    for name in ("q", "k"):
+        x = inp[name].double()
+        inp[name] = (x / torch.sqrt((x * x).sum(-1, keepdim=True) + 1e-6)).float()
+    inp = _dev(inp)
+    out = _run(w, inp, l2norm=False)
+    _check_all(w, inp, out, l2norm=False)
+
+
+EDGE = [
+    syn.custom("edge_tails", [1, 63, 64, 65, 127, 129, 0, 200], 2, 6, 128, "bf16", has_h0=True, want_ht=True,
+               has_dht=True),
+    syn.custom("edge_d64_f32", [70, 5, 130], 2, 4, 64, "f32", has_h0=True, want_ht=True, has_dht=True, seed=8),
+    syn.custom("edge_g1", [64, 64, 1], 3, 3, 128, "bf16", seed=9),
+    syn.custom("edge_g4_h0", [100, 33], 1, 4, 64, "bf16", has_h0=True, want_ht=True, seed=10),
+    syn.custom("edge_empty_docs", [0, 0, 17, 0], 1, 3, 128, "bf16", has_h0=True, want_ht=True, has_dht=True,
+               seed=11),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=[w.name for w in EDGE])
+@pytest.mark.parametrize("det", [True, False])
+def test_edge_cases(w, det):
+    inp = _dev(syn.make_inputs(w))
+    out = _run(w, inp, det=det)
+    _check_all(w, inp, out)
+
+
+def test_all_documents_empty():
+    w = syn.custom("all_empty", [0, 0], 1, 2, 64, "bf16", has_h0=True, want_ht=True, has_dht=True)
+    inp = _dev(syn.make_inputs(w))
+    out = _run(w, inp)
+    assert torch.equal(out["ht"], inp["h0"])
+    assert torch.equal(out["dh0"], inp["dht"])
+
+
+def test_light_equals_full_bitwise():
+    w = EDGE[0]
+    inp = _dev(syn.make_inputs(w))
+    a = _run(w, inp, save_mode=G.SAVE_LIGHT, det=True)
+    b = _run(w, inp, save_mode=G.SAVE_FULL, det=True)
+    for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_recompute_saved_set_bitwise_and_ckpt():
+    w = EDGE[0]
+    inp = _dev(syn.make_inputs(w))
+    a = _run(w, inp, det=True)
+    b = _run(w, inp, det=True, recompute=True)
+    assert torch.equal(b["saved"], b["saved_recompute"])
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_deterministic_bitwise_repeat_and_nan_poison():
+    """Deterministic mode is bitwise reproducible, also when every output, the saved set and the
+    workspaces start out NaN-filled (nothing reads a buffer before writing it)."""
+    w = EDGE[0]
+    inp = _dev(syn.make_inputs(w))
+    a = _run(w, inp, det=True)
+    b = _run(w, inp, det=True, poison=True)
+    for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.isfinite(b[k]).all(), k
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_atomic_close_to_deterministic():
+    w = EDGE[0]
+    inp = _dev(syn.make_inputs(w))
+    a = _run(w, inp, det=True)
+    b = _run(w, inp, det=False, poison=True)
+    assert torch.equal(a["dh0"], b["dh0"])  # same reverse-walk kernel in both modes
+    for k in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert_close(k, b[k], a[k])
+
+
+def test_saved_set_refused_for_other_problem():
+    w = EDGE[0]
+    inp = _dev(syn.make_inputs(w))
+    a = _run(w, inp, bwd=False)
+    p2 = G.problem_for(w, save_mode=G.SAVE_FULL)
+    with pytest.raises(G.GdnError) as e:
+        G.gdn_bwd(p2, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"], a["saved"], inp["dO"],
+                  h0=inp["h0"], dht=inp["dht"])
+    assert e.value.code == G.GDN_ESAVED
+
+
+# ------------------------------------------------------------------------------------------
+# full-size workloads, sampled
+
+
+def _big(name):
+    w = syn.WORKLOADS[name]
+    torch.cuda.empty_cache()
+    return w, syn.make_inputs(w, device=DEV)
+
+
+def test_single8k_fwd():
+    w, inp = _big("single8k")
+    out = _run(w, inp, bwd=False)
+    _check_all(w, inp, out, heads=[0, 15], bwd=False)
+
+
+def test_pack262k_fwd_bwd_atomic():
+    w, inp = _big("pack262k")
+    out = _run(w, inp, det=False)
+    for k in ("o", "dq", "dk", "dv", "dg", "dbeta"):
+        assert torch.isfinite(out[k]).all(), k
+    _check_all(w, inp, out, docs=[3], heads=[2, 7, 13])
+
+
+def test_pack262k_deterministic_repeat():
+    w, inp = _big("pack262k")
+    a = _run(w, inp, det=True)
+    dq, dk = a["dq"].clone(), a["dk"].clone()
+    del a
+    b = _run(w, inp, det=True)
+    assert torch.equal(dq, b["dq"]) and torch.equal(dk, b["dk"])
+    _check_all(w, inp, b, docs=[3], heads=[5])
+
+
+def test_cp4share_h0_ht_dh0():
+    w, inp = _big("cp4share")
+    out = _run(w, inp)
+    _check_all(w, inp, out, docs=[1], heads=[0, 9])
+
+
+def test_short512_ckpt_deterministic():
+    w, inp = _big("short512")
+    out = _run(w, inp, det=True, recompute=True)
+    assert torch.equal(out["saved"], out["saved_recompute"])
+    lens = np.asarray(w.lengths)
+    docs = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] + list(range(0, w.N, 64))))
+    _check_all(w, inp, out, docs=docs, heads=[3, 12])

@@ -1,0 +1,166 @@
+"""Host-side checks of the C ABI that need no GPU: exports, byte queries, validation errors.
+
+No call here reaches a kernel launch: every invalid call is rejected by host validation, which
+runs before the first launch.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_fwd_amd as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    return G.load_library()
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    declared = set(re.findall(r"^[A-Za-z_][\w \*]*?\b(gdn_\w+)\s*\(", hdr, flags=re.M))
+    assert {"gdn_fwd", "gdn_bwd", "gdn_fwd_recompute", "gdn_saved_bytes", "gdn_workspace_bytes"} <= declared
+    lib = _lib()
+    for name in sorted(declared):
+        assert hasattr(lib, name), "libgdn.so does not export %s" % name
+    assert lib.gdn_abi_version() == 1
+
+
+def _prob(lengths, H=16, HV=48, d=128, save_mode=G.SAVE_LIGHT, **kw):
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return G.Problem(cu, H, HV, d, save_mode=save_mode, **kw)
+
+
+def test_saved_bytes_match_pages():
+    """Light and full saved sets at the pages' shape (HV = 48, d = 128, 64-token chunks, all chunks
+    full) match the README saved-set table's per-token figures."""
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "saved_set_bytes.json")))
+    lengths = [98304, 65536, 57344, 40960]
+    T = sum(lengths)
+    light = G.gdn_saved_bytes(_prob(lengths, HV=gold["HV"], d=gold["d"]))
+    full = G.gdn_saved_bytes(_prob(lengths, HV=gold["HV"], d=gold["d"], save_mode=G.SAVE_FULL))
+    assert (light - 256) == gold["light_bytes_per_token"] * T
+    assert (full - light) == gold["full_extra_bytes_per_token"] * T
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("lengths,H,HV,d", [([1, 63, 65, 0, 129], 2, 6, 128), ([70], 1, 1, 64), ([3, 4], 4, 8, 64)])
+def test_saved_and_workspace_formula(lengths, H, HV, d):
+    T = sum(lengths)
+    NT = sum((L + 63) // 64 for L in lengths)
+    light = 256 + _align(T * HV * 64 * 2) + _align(T * HV * 4) + _align(NT * HV * 4)
+    assert G.gdn_saved_bytes(_prob(lengths, H, HV, d)) == light
+    full = light + _align(NT * HV * d * d * 2) + 3 * _align(T * HV * d * 2) + _align(T * HV * 64 * 2)
+    assert G.gdn_saved_bytes(_prob(lengths, H, HV, d, save_mode=G.SAVE_FULL)) == full
+    wf = G.gdn_workspace_bytes(_prob(lengths, H, HV, d), G.OP_FWD)
+    wb = G.gdn_workspace_bytes(_prob(lengths, H, HV, d), G.OP_BWD)
+    wb_atomic = G.gdn_workspace_bytes(_prob(lengths, H, HV, d, deterministic=False), G.OP_BWD)
+    assert wf >= NT * H * 64 * 64 * 2
+    assert wb >= wf + 2 * NT * HV * d * d * 2
+    assert wb_atomic >= wb + 2 * T * H * d * 4
+
+
+@pytest.mark.parametrize("bad,fragment", [
+    (dict(HV=47), "multiple"),
+    (dict(d=96), "64 or 128"),
+    (dict(lengths=[5, -1]), "decreases"),
+    (dict(H=0), "head counts"),
+])
+def test_invalid_problem_rejected(bad, fragment):
+    kw = dict(lengths=[10, 20], H=16, HV=48, d=128)
+    kw.update(bad)
+    lengths = kw.pop("lengths")
+    if min(lengths) < 0:
+        cu = np.array([0, 5, 4], np.int32)
+        p = G.Problem(cu, kw["H"], kw["HV"], kw["d"])
+    else:
+        p = _prob(lengths, **kw)
+    assert _lib().gdn_saved_bytes(p.ref()) == 0
+    assert fragment in _lib().gdn_last_error().decode()
+
+
+def test_n_tokens_mismatch_rejected():
+    p = _prob([10, 20])
+    p.st.n_tokens = 31
+    assert _lib().gdn_saved_bytes(p.ref()) == 0
+    assert "n_tokens" in _lib().gdn_last_error().decode()
+
+
+class _Fake:
+    """Stands in for a device tensor: an aligned address that is never dereferenced."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _fake(i=1, misalign=0):
+    return _Fake(0x100000 * i + misalign)
+
+
+def _call_fwd(p, q=None, workspace_bytes=None, **over):
+    lib = _lib()
+    args = dict(q=_fake(1), k=_fake(2), v=_fake(3), g=_fake(4), beta=_fake(5), cu=_fake(6), h0=None, o=_fake(7),
+                ht=None, saved=_fake(8), ws=_fake(9))
+    args.update(over)
+    if q is not None:
+        args["q"] = q
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    nbytes = workspace_bytes if workspace_bytes is not None else G.gdn_workspace_bytes(p, G.OP_FWD)
+    return lib.gdn_fwd(p.ref(), P(args["q"]), P(args["k"]), P(args["v"]), P(args["g"]), P(args["beta"]),
+                       P(args["cu"]), P(args["h0"]), P(args["o"]), P(args["ht"]), P(args["saved"]), P(args["ws"]),
+                       nbytes, None)
+
+
+def test_fwd_rejects_null_and_misaligned_pointers():
+    p = _prob([100, 28])
+    class Null:
+        def data_ptr(self):
+            return 0
+    assert _call_fwd(p, q=Null()) == G.GDN_EINVAL
+    assert "q is NULL" in _lib().gdn_last_error().decode()
+    assert _call_fwd(p, q=_fake(1, misalign=4)) == G.GDN_EINVAL
+    assert "aligned" in _lib().gdn_last_error().decode()
+
+
+def test_fwd_rejects_missing_h0_and_ht():
+    p = _prob([100], has_h0=True)
+    assert _call_fwd(p) == G.GDN_EINVAL and "h0" in _lib().gdn_last_error().decode()
+    p = _prob([100], want_ht=True)
+    assert _call_fwd(p) == G.GDN_EINVAL and "ht" in _lib().gdn_last_error().decode()
+
+
+def test_fwd_rejects_small_workspace():
+    p = _prob([100, 28])
+    need = G.gdn_workspace_bytes(p, G.OP_FWD)
+    assert _call_fwd(p, workspace_bytes=need - 1) == G.GDN_EWORKSPACE
+
+
+def test_bwd_rejects_unknown_saved_buffer():
+    p = _prob([100, 28])
+    lib = _lib()
+    f = [ctypes.c_void_p(_fake(i).data_ptr()) for i in range(1, 20)]
+    rc = lib.gdn_bwd(p.ref(), f[0], f[1], f[2], f[3], f[4], f[5], None, f[6], f[7], None, f[8], f[9], f[10], f[11],
+                     f[12], None, f[13], G.gdn_workspace_bytes(p, G.OP_BWD), None)
+    assert rc == G.GDN_ESAVED
+
+
+def test_binding_refuses_without_library(tmp_path):
+    with pytest.raises(OSError):
+        G._lib_backup = G._lib
+        try:
+            G._lib = None
+            G.load_library(str(tmp_path / "missing.so"))
+        finally:
+            G._lib = G._lib_backup
