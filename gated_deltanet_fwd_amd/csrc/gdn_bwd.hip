@@ -144,7 +144,27 @@ int launch_wy_full(const Args& a, void* stream) {
 
 // ---------------------------------------------------------------------------------------
 // Reverse walk, one workgroup per (document, value head, value tile), chunks in reverse.
-// Writes the end-state gradient of every chunk (bf16, transposed) and dh0.
+// Writes the end-state gradient of every chunk (bf16, transposed) and dh0. The next chunk's
+// inputs are prefetched into registers; K, Q, A and dO are staged row-major and read transposed
+// with transpose-reads where a contraction runs over tokens.
+template <int D, int DVT>
+struct BWalkSmem {
+  static constexpr int SK = D + 16;
+  static constexpr int SA = CH + 16;
+  static constexpr int SST = D + PAD;
+  static constexpr int STK = CH + PAD;
+  static constexpr int SDO = DVT + PAD;
+  bf16 sK[CH * SK];
+  bf16 sQ[CH * SK];
+  bf16 sA[CH * SA];
+  bf16 sdST[DVT * SST];
+  bf16 sdO[CH * SDO];
+  bf16 sdOp[CH * SDO];
+  bf16 sdRT[DVT * STK];
+  bf16 sYT[DVT * STK];
+  float sG[CH], sB[CH], srk[CH];
+};
+
 template <int D, int DVT, typename TI>
 __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
   if (a.status[0]) return;
@@ -159,22 +179,51 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
   constexpr int NCT = DVT / 16;
   constexpr int NRT = D / 64;
   constexpr int KS = D / 32;
-  constexpr int STK = CH + PAD;
-  constexpr int SST = D + PAD;
-  __shared__ __attribute__((aligned(16))) bf16 sKT[D * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sQT[D * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sAT[CH * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sdST[DVT * SST];
-  __shared__ __attribute__((aligned(16))) bf16 sdOT[DVT * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sdOpT[DVT * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sdRT[DVT * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sYT[DVT * STK];
-  __shared__ float sG[CH], sB[CH], srk[CH], srq[CH];
+  using SM = BWalkSmem<D, DVT>;
+  constexpr int SK = SM::SK, SA = SM::SA, SST = SM::SST, STK = SM::STK, SDO = SM::SDO;
+  constexpr int VPR = DVT / 8;
+  __shared__ __attribute__((aligned(16))) SM sm;
   const TI* kp = (const TI*)a.k;
   const TI* qp = (const TI*)a.q;
   const TI* dop = (const TI*)a.dO;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* qkt = reinterpret_cast<const bf16*>(a.qk);
+  const int ar = 16 * w + lr;
+
+  // ---- prefetch registers
+  bf16x8 nk[KS], nq[KS], na[2], np[2], ndo;
+  float ng = 0.f, nb = 0.f, nrk = 0.f, ngam = 0.f, nsc = 0.f;
+  int nlen = 0, nt0 = 0;
+  auto prefetch = [&](int c) {
+    nlen = a.c_len[c];
+    nt0 = a.c_t0[c];
+    const bool ok = ar < nlen;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      nk[ks] = ok ? IO<TI>::load8(kp + ((size_t)(nt0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
+      nq[ks] = ok ? IO<TI>::load8(qp + ((size_t)(nt0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      na[k2] = ok ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(nt0 + ar) * a.HV + h) * CH + k2 * 32 + lg * 8)
+                  : zero8();
+      np[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.H + j) * CH * CH + ar * CH + k2 * 32 + lg * 8);
+    }
+    if (tid < CH * VPR) {
+      const int r = tid / VPR, pc = tid % VPR;
+      const bool rok = r < nlen;
+      ndo = rok ? IO<TI>::load8(dop + ((size_t)(nt0 + r) * a.HV + h) * D + col0 + pc * 8) : zero8();
+      // scale of row r in Qh^T diag(b) dO: exp(gcum) * rq
+      nsc = rok ? __expf(a.gcum[(size_t)(nt0 + r) * a.HV + h]) * a.rq[(size_t)(nt0 + r) * a.H + j] : 0.f;
+    }
+    if (tid < CH) {
+      const bool rok = tid < nlen;
+      ng = rok ? a.gcum[(size_t)(nt0 + tid) * a.HV + h] : 0.f;
+      nb = rok ? a.beta[(size_t)(nt0 + tid) * a.HV + h] : 0.f;
+      nrk = rok ? a.rk[(size_t)(nt0 + tid) * a.H + j] : 0.f;
+    }
+    ngam = a.gamma[(size_t)c * a.HV + h];
+  };
 
   f32x4 dS[NRT][NCT];
 #pragma unroll
@@ -190,102 +239,75 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
-      lds_store4_t(sdST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, dS[rt][ct][0], dS[rt][ct][1],
+      lds_store4_t(sm.sdST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, dS[rt][ct][0], dS[rt][ct][1],
                    dS[rt][ct][2], dS[rt][ct][3]);
-  __syncthreads();
+  if (c_begin < c_end) prefetch(c_end - 1);
 
   for (int c = c_end - 1; c >= c_begin; --c) {
-    const int len = a.c_len[c], t0 = a.c_t0[c];
-    if (tid < CH) {
-      const int r = tid;
-      const bool ok = r < len;
-      sG[r] = ok ? a.gcum[(size_t)(t0 + r) * a.HV + h] : 0.f;
-      sB[r] = ok ? a.beta[(size_t)(t0 + r) * a.HV + h] : 0.f;
-      srk[r] = ok ? a.rk[(size_t)(t0 + r) * a.H + j] : 0.f;
-      srq[r] = ok ? a.rq[(size_t)(t0 + r) * a.H + j] : 0.f;
-    }
-    for (int idx = tid; idx < CH * (D / 8); idx += NTHREADS) {
-      const int r = idx & 63, pc = idx >> 6;
-      bf16x8 kv = zero8(), qv = zero8();
-      if (r < len) {
-        kv = IO<TI>::load8(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
-        qv = IO<TI>::load8(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sKT[(pc * 8 + e) * STK + r] = kv[e];
-        sQT[(pc * 8 + e) * STK + r] = qv[e];
-      }
-    }
-    for (int idx = tid; idx < CH * (CH / 8); idx += NTHREADS) {
-      const int r = idx & 63, pc = idx >> 6;
-      const bf16x8 av =
-          r < len ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) : zero8();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sAT[(pc * 8 + e) * STK + r] = av[e];
-    }
-    const int ar = 16 * w + lr;
-    const bool arok = ar < len;
+    const int len = nlen;
+    const float gam = ngam;
     bf16x8 fk[KS], fpt[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      fk[ks] = arok ? IO<TI>::load8(kp + ((size_t)(t0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
+    for (int ks = 0; ks < KS; ++ks) {
+      fk[ks] = nk[ks];
+      *reinterpret_cast<bf16x8*>(sm.sK + ar * SK + ks * 32 + lg * 8) = nk[ks];
+      *reinterpret_cast<bf16x8*>(sm.sQ + ar * SK + ks * 32 + lg * 8) = nq[ks];
+    }
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-      fpt[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.H + j) * CH * CH + ar * CH + k2 * 32 + lg * 8);
-    float dov[NCT][4];
+    for (int k2 = 0; k2 < 2; ++k2) {
+      fpt[k2] = np[k2];
+      *reinterpret_cast<bf16x8*>(sm.sA + ar * SA + k2 * 32 + lg * 8) = na[k2];
+    }
+    if (tid < CH * VPR) {
+      const int r = tid / VPR, pc = tid % VPR;
+      *reinterpret_cast<bf16x8*>(sm.sdO + r * SDO + pc * 8) = ndo;
+      bf16x8 sc;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i;
-        dov[ct][i] = r < len ? IO<TI>::load1(dop + ((size_t)(t0 + r) * a.HV + h) * D + col0 + 16 * ct + lr) : 0.f;
-      }
-    const float gam = a.gamma[(size_t)c * a.HV + h];
+      for (int e = 0; e < 8; ++e) sc[e] = (bf16)(nsc * (float)ndo[e]);
+      *reinterpret_cast<bf16x8*>(sm.sdOp + r * SDO + pc * 8) = sc;
+    }
+    if (tid < CH) {
+      sm.sG[tid] = ng;
+      sm.sB[tid] = nb;
+      sm.srk[tid] = nrk;
+    }
+    if (c - 1 >= c_begin) prefetch(c - 1);
     __syncthreads();
 
     {
       bf16* tp = reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D + (size_t)col0 * D;
       for (int idx = tid; idx < DVT * (D / 8); idx += NTHREADS) {
         const int cc = idx / (D / 8), pc = idx % (D / 8);
-        *reinterpret_cast<bf16x8*>(tp + (size_t)cc * D + pc * 8) = lds8(sdST, SST, cc, pc * 8);
+        *reinterpret_cast<bf16x8*>(tp + (size_t)cc * D + pc * 8) = lds8(sm.sdST, SST, cc, pc * 8);
       }
     }
-    float brow[4];
+    {
+      const float gr = sm.sG[ar];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) brow[i] = expf(sG[16 * w + lg * 4 + i]);
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      lds_store4_t(sdOT, STK, 16 * ct + lr, 16 * w + lg * 4, dov[ct][0], dov[ct][1], dov[ct][2], dov[ct][3]);
-      float t[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t[i] = brow[i] * srq[16 * w + lg * 4 + i] * dov[ct][i];
-      lds_store4_t(sdOpT, STK, 16 * ct + lr, 16 * w + lg * 4, t[0], t[1], t[2], t[3]);
+        for (int e = 0; e < 8; ++e) {
+          const int ii = k2 * 32 + lg * 8 + e;
+          fpt[k2][e] = (ii >= ar) ? (bf16)(__expf(sm.sG[ii] - gr) * (float)fpt[k2][e]) : (bf16)0.f;
+        }
     }
+    const float glast = sm.sG[len - 1];
+    float dec[4], ybr[4];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ii = k2 * 32 + lg * 8 + e;
-        fpt[k2][e] = (ii >= ar) ? (bf16)(expf(sG[ii] - sG[ar]) * (float)fpt[k2][e]) : (bf16)0.f;
-      }
-    __syncthreads();
-
-    const float glast = sG[len - 1];
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + lg * 4 + i;
+      dec[i] = __expf(glast - sm.sG[r]) * sm.srk[r];
+      ybr[i] = sm.sB[r] * __expf(sm.sG[r]) * sm.srk[r];
+    }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 kd = zero4(), pd = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kd = mfma(fk[ks], lds8(sdST, SST, 16 * ct + lr, ks * 32 + lg * 8), kd);
+      for (int ks = 0; ks < KS; ++ks) kd = mfma(fk[ks], lds8(sm.sdST, SST, 16 * ct + lr, ks * 32 + lg * 8), kd);
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) pd = mfma(fpt[k2], lds8(sdOT, STK, 16 * ct + lr, k2 * 32 + lg * 8), pd);
-      float dr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i;
-        dr[i] = pd[i] + expf(glast - sG[r]) * srk[r] * kd[i];
-      }
-      lds_store4_t(sdRT, STK, 16 * ct + lr, 16 * w + lg * 4, dr[0], dr[1], dr[2], dr[3]);
+      for (int k2 = 0; k2 < 2; ++k2) pd = mfma(fpt[k2], lds_tr8(sm.sdO, SDO, k2 * 32, 16 * ct), pd);
+      lds_store4_t(sm.sdRT, STK, 16 * ct + lr, 16 * w + lg * 4, pd[0] + dec[0] * kd[0], pd[1] + dec[1] * kd[1],
+                   pd[2] + dec[2] * kd[2], pd[3] + dec[3] * kd[3]);
     }
     __syncthreads();
 #pragma unroll
@@ -293,14 +315,9 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
       f32x4 y = zero4();
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
-        y = mfma(lds8(sAT, STK, 16 * w + lr, k2 * 32 + lg * 8), lds8(sdRT, STK, 16 * ct + lr, k2 * 32 + lg * 8), y);
-      float t[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i;
-        t[i] = sB[r] * brow[i] * srk[r] * y[i];
-      }
-      lds_store4_t(sYT, STK, 16 * ct + lr, 16 * w + lg * 4, t[0], t[1], t[2], t[3]);
+        y = mfma(lds_tr8(sm.sA, SA, k2 * 32, 16 * w), lds8(sm.sdRT, STK, 16 * ct + lr, k2 * 32 + lg * 8), y);
+      lds_store4_t(sm.sYT, STK, 16 * ct + lr, 16 * w + lg * 4, ybr[0] * y[0], ybr[1] * y[1], ybr[2] * y[2],
+                   ybr[3] * y[3]);
     }
     __syncthreads();
 #pragma unroll
@@ -310,10 +327,9 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
         f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          a1 = mfma(lds8(sQT, STK, 16 * (w * NRT + rt) + lr, k2 * 32 + lg * 8),
-                    lds8(sdOpT, STK, 16 * ct + lr, k2 * 32 + lg * 8), a1);
-          a2 = mfma(lds8(sKT, STK, 16 * (w * NRT + rt) + lr, k2 * 32 + lg * 8),
-                    lds8(sYT, STK, 16 * ct + lr, k2 * 32 + lg * 8), a2);
+          a1 = mfma(lds_tr8(sm.sQ, SK, k2 * 32, 16 * (w * NRT + rt)), lds_tr8(sm.sdOp, SDO, k2 * 32, 16 * ct), a1);
+          a2 = mfma(lds_tr8(sm.sK, SK, k2 * 32, 16 * (w * NRT + rt)), lds8(sm.sYT, STK, 16 * ct + lr, k2 * 32 + lg * 8),
+                    a2);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) dS[rt][ct][i] = __builtin_fmaf(gam, dS[rt][ct][i], a1[i] - a2[i]);
@@ -323,7 +339,7 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        lds_store4_t(sdST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, dS[rt][ct][0], dS[rt][ct][1],
+        lds_store4_t(sm.sdST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, dS[rt][ct][0], dS[rt][ct][1],
                      dS[rt][ct][2], dS[rt][ct][3]);
   }
   if (a.dh0) {
@@ -356,46 +372,55 @@ int launch_walk_bwd(const Args& a, void* stream) {
 // Chunk gradients. DET: one workgroup per (chunk, q/k head) looping over its G value heads,
 // summing dQh/dKh in registers in a fixed order, then the L2-norm backward. Otherwise one
 // workgroup per (chunk, value head) adding dQh/dKh into FP32 accumulators with atomics.
+//
+// 8 waves: wave w owns rows 16*(w%4).. of every 64-row product and half w/4 of its columns.
+// The state and adjoint tapes stream through LDS in 32-column value slices (the next slice is
+// prefetched into registers); every tile is stored once and read in the other orientation with
+// transpose-reads. The value-dimension contractions feed dQh and dKh directly through row-scaled
+// A fragments: diag(b) dO S^T, diag(exp(G_last - G)) R dSn^T and -diag(beta b) dX S^T.
+constexpr int GRAD_THREADS = 512;
+
 template <int D>
 struct GradSmem {
-  static constexpr int SK = D + PAD, STK = CH + PAD, DC = 32, SDC = DC + PAD;
-  // persistent
+  static constexpr int SK = D + 16;  // K, Q rows; S^T, dSn^T slice rows
+  static constexpr int SA = CH + 16; // A rows and token-indexed transposed tiles
+  static constexpr int DC = 32;      // value columns per slice
+  static constexpr int SDO = DC + 16;
+  static constexpr int SV = DC + PAD;
   bf16 sK[CH * SK];
-  bf16 sKT[D * STK];
-  bf16 sQT[D * STK];
-  bf16 sA[CH * STK];
-  bf16 sAT[CH * STK];
-  bf16 sPT[CH * STK];
-  float srk[CH], srq[CH], sG[CH], sB[CH];
-  float sZ[CH], sDb[CH], sDbeta[CH];
+  bf16 sQ[CH * SK];
+  bf16 sA[CH * SA];
+  float sG[CH], sB[CH], srk[CH], srq[CH];
+  float sRow[2][4][CH];
   float sred[8];
-  // per value-column slice, reused for the per-head tail
   union U {
-    struct B {
-      bf16 sS_tr[DC * SK];
-      bf16 sdS_tr[DC * SK];
-      bf16 sS_rm[D * SDC];
-      bf16 sdS_rm[D * SDC];
-      bf16 sdO_rm[CH * SDC];
-      bf16 sdO_tr[DC * STK];
-      bf16 sX_tr[DC * STK];
-      bf16 sX_rm[CH * SDC];
-      bf16 sR_rm[CH * SDC];
-      bf16 sdR_tr[DC * STK];
-      bf16 sdR_rm[CH * SDC];
-      bf16 sdX_rm[CH * SDC];
+    struct Sl {
+      bf16 sS[DC * SK];
+      bf16 sdS[DC * SK];
+      bf16 sdO[CH * SDO];
+      bf16 sV[CH * SV];
+      bf16 sXT[DC * SA];
+      bf16 sdRT[DC * SA];
+      bf16 sRT[DC * SA];
+      bf16 sdXT[DC * SA];
     } b;
-    struct C {
+    struct Tl {
       float sM[CH][CH + 1];
-      bf16 sT1[CH * STK];
-      bf16 sT2[CH * STK];
-      bf16 sT3[CH * STK];
+      bf16 sT1t[CH * SA];
+      bf16 sT2[CH * SA];
+      bf16 sT3[CH * SA];
     } t;
   } u;
 };
 
+__device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)(s * (float)v[e]);
+  return v;
+}
+
 template <int D, typename TI, bool DET>
-__global__ __launch_bounds__(NTHREADS) void k_chunk_grad(Args a) {
+__global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   if (a.status[0]) return;
   const int c = blockIdx.x;
   const int len = a.c_len[c];
@@ -405,10 +430,14 @@ __global__ __launch_bounds__(NTHREADS) void k_chunk_grad(Args a) {
   const int h_first = DET ? j * a.G : (int)blockIdx.y;
   const int h_count = DET ? a.G : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rt = w & 3, half = w >> 2;
   const int lr = lane & 15, lg = lane >> 4;
+  const int row0 = 16 * rt;      // rows of this wave's product tiles
+  const int arow = row0 + lr;    // row of this lane's A fragments
   using SM = GradSmem<D>;
-  constexpr int SK = SM::SK, STK = SM::STK, DC = SM::DC, SDC = SM::SDC;
-  constexpr int KS = D / 32, NDT = D / 16, NDC = D / DC;
+  constexpr int SK = SM::SK, SA = SM::SA, DC = SM::DC, SDO = SM::SDO, SV = SM::SV;
+  constexpr int KS = D / 32, NDC = D / DC;
+  constexpr int NT2 = D / 32;    // 16-wide key-dim column tiles per wave (half of D/16)
   __shared__ __attribute__((aligned(16))) SM sm;
   const TI* kp = (const TI*)a.k;
   const TI* qp = (const TI*)a.q;
@@ -417,366 +446,366 @@ __global__ __launch_bounds__(NTHREADS) void k_chunk_grad(Args a) {
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* htape = reinterpret_cast<const bf16*>(a.htape);
   const bf16* dstape = reinterpret_cast<const bf16*>(a.dstape);
+  const bf16* qkt = reinterpret_cast<const bf16*>(a.qk);
 
-  // ---- q/k tiles, norms, Kk = Kh Kh^T and Qk = Qh Kh^T (C layout, rows 16w..)
-  if (tid < CH) {
-    const bool ok = tid < len;
-    sm.srk[tid] = ok ? a.rk[(size_t)(t0 + tid) * a.H + j] : 0.f;
-    sm.srq[tid] = ok ? a.rq[(size_t)(t0 + tid) * a.H + j] : 0.f;
-  }
-  for (int idx = tid; idx < CH * (D / 8); idx += NTHREADS) {
-    const int r = idx & 63, pc = idx >> 6;
+  // ---- K, Q rows and their norms; Kk = Kh Kh^T, Qk = Qh Kh^T on this wave's tiles
+  for (int idx = tid; idx < CH * (D / 8); idx += GRAD_THREADS) {
+    const int r = idx / (D / 8), pc = idx % (D / 8);
     bf16x8 kv = zero8(), qv = zero8();
     if (r < len) {
       kv = IO<TI>::load8(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
       qv = IO<TI>::load8(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
     }
     *reinterpret_cast<bf16x8*>(sm.sK + r * SK + pc * 8) = kv;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sm.sKT[(pc * 8 + e) * STK + r] = kv[e];
-      sm.sQT[(pc * 8 + e) * STK + r] = qv[e];
-    }
+    *reinterpret_cast<bf16x8*>(sm.sQ + r * SK + pc * 8) = qv;
+  }
+  if (tid < CH) {
+    const bool ok = tid < len;
+    sm.srk[tid] = ok ? a.rk[(size_t)(t0 + tid) * a.H + j] : 0.f;
+    sm.srq[tid] = ok ? a.rq[(size_t)(t0 + tid) * a.H + j] : 0.f;
   }
   __syncthreads();
-  f32x4 Kk[4], Qk[4];
+  f32x4 Kk[2], Qk[2];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) Kk[ct] = Qk[ct] = zero4();
+  for (int c2 = 0; c2 < 2; ++c2) {
+    Kk[c2] = Qk[c2] = zero4();
+    const int ct = 2 * half + c2;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 ak = lds8(sm.sK, SK, 16 * w + lr, ks * 32 + lg * 8);
-    // Q rows as an A fragment: Q[r][d..d+7] = Q^T[d..d+7][r], gathered from the transposed tile
-    bf16x8 aq;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) aq[e] = sm.sQT[(ks * 32 + lg * 8 + e) * STK + 16 * w + lr];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 bk = lds8(sm.sK, SK, 16 * ct + lr, ks * 32 + lg * 8);
-      Kk[ct] = mfma(ak, bk, Kk[ct]);
-      Qk[ct] = mfma(aq, bk, Qk[ct]);
+      Kk[c2] = mfma(lds8(sm.sK, SK, arow, ks * 32 + lg * 8), bk, Kk[c2]);
+      Qk[c2] = mfma(lds8(sm.sQ, SK, arow, ks * 32 + lg * 8), bk, Qk[c2]);
     }
-  }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-      Kk[ct][i] *= sm.srk[r] * sm.srk[cc];
-      Qk[ct][i] *= sm.srq[r] * sm.srk[cc];
+      const int r = row0 + lg * 4 + i, cc = 16 * ct + lr;
+      Kk[c2][i] *= sm.srk[r] * sm.srk[cc];
+      Qk[c2][i] *= sm.srq[r] * sm.srk[cc];
     }
-
-  f32x4 dQacc[NDT], dKacc[NDT];
+  }
+  float rk_r[4], rq_r[4];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) dQacc[t] = dKacc[t] = zero4();
+  for (int i = 0; i < 4; ++i) {
+    rk_r[i] = sm.srk[row0 + lg * 4 + i];
+    rq_r[i] = sm.srq[row0 + lg * 4 + i];
+  }
+
+  f32x4 dQacc[NT2], dKacc[NT2];
+#pragma unroll
+  for (int t = 0; t < NT2; ++t) dQacc[t] = dKacc[t] = zero4();
+
+  // slice prefetch registers
+  bf16x8 nS, ndS, nx; // S^T / dSn^T piece; dO piece (threads < 256) or V piece (threads >= 256)
+  auto prefetch = [&](int h, int cv) {
+    const int dvl = tid / (D / 8), pc = tid % (D / 8); // 32 rows x D/8 pieces = 512 (D = 128)
+    if (dvl < DC) {
+      const size_t off = ((size_t)c * a.HV + h) * D * D + (size_t)(cv * DC + dvl) * D + pc * 8;
+      nS = *reinterpret_cast<const bf16x8*>(htape + off);
+      ndS = *reinterpret_cast<const bf16x8*>(dstape + off);
+    }
+    const int u = tid & 255, r = u >> 2, pv = u & 3;
+    const TI* src = tid < 256 ? dop : vp;
+    nx = r < len ? IO<TI>::load8(src + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + pv * 8) : zero8();
+  };
 
   for (int hh = 0; hh < h_count; ++hh) {
     const int h = h_first + hh;
-    __syncthreads(); // previous head's tail is done with the shared buffers
+    __syncthreads(); // the previous head's tail is done with the shared tiles
+    {
+      const int r = tid >> 3, pc = tid & 7;
+      const bf16x8 av =
+          r < len ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) : zero8();
+      *reinterpret_cast<bf16x8*>(sm.sA + r * SA + pc * 8) = av;
+    }
     if (tid < CH) {
       const bool ok = tid < len;
       sm.sG[tid] = ok ? a.gcum[(size_t)(t0 + tid) * a.HV + h] : 0.f;
       sm.sB[tid] = ok ? a.beta[(size_t)(t0 + tid) * a.HV + h] : 0.f;
     }
-    for (int idx = tid; idx < CH * (CH / 8); idx += NTHREADS) {
-      const int r = idx & 63, pc = idx >> 6;
-      const bf16x8 av =
-          r < len ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) : zero8();
-      *reinterpret_cast<bf16x8*>(sm.sA + r * STK + pc * 8) = av;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.sAT[(pc * 8 + e) * STK + r] = av[e];
-    }
     const float gam = a.gamma[(size_t)c * a.HV + h];
+    bf16x8 fpt[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+      fpt[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.H + j) * CH * CH + arow * CH + k2 * 32 + lg * 8);
+    prefetch(h, 0);
     __syncthreads();
     const float glast = sm.sG[len - 1];
-    float brow[4], beta_r[4], rk_r[4], rq_r[4], dec_r[4];
+    {
+      const float ga = sm.sG[arow];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ii = k2 * 32 + lg * 8 + e;
+          fpt[k2][e] = (ii >= arow) ? (bf16)(__expf(sm.sG[ii] - ga) * (float)fpt[k2][e]) : (bf16)0.f;
+        }
+    }
+    // per-row factors: this lane's C rows (r) and A-fragment row (arow)
+    float brow[4], beta_r[4], dec_r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + lg * 4 + i;
-      brow[i] = expf(sm.sG[r]);
+      const int r = row0 + lg * 4 + i;
+      brow[i] = __expf(sm.sG[r]);
       beta_r[i] = sm.sB[r];
-      rk_r[i] = sm.srk[r];
-      rq_r[i] = sm.srq[r];
-      dec_r[i] = expf(glast - sm.sG[r]);
+      dec_r[i] = __expf(glast - sm.sG[r]);
     }
-    // P^T (transposed, decayed, masked) from the fp32 Qk tile
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      float t[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-        t[i] = r >= cc ? expf(sm.sG[r] - sm.sG[cc]) * Qk[ct][i] : 0.f;
-      }
-      lds_store4_t(sm.sPT, STK, 16 * ct + lr, 16 * w + lg * 4, t[0], t[1], t[2], t[3]);
-    }
+    const float a_b = __expf(sm.sG[arow]);
+    const float a_dec = __expf(glast - sm.sG[arow]);
+    const float a_nbb = -sm.sB[arow] * a_b;
 
-    f32x4 dOS[NDT], RdS[NDT], dXS[NDT], dP[4], dA[4];
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) dOS[t] = RdS[t] = dXS[t] = zero4();
-#pragma unroll
-    for (int t = 0; t < 4; ++t) dP[t] = dA[t] = zero4();
-    float zpart[4] = {0.f, 0.f, 0.f, 0.f}, dbx[4] = {0.f, 0.f, 0.f, 0.f}, dbr[4] = {0.f, 0.f, 0.f, 0.f};
+    float zp[4] = {0.f, 0.f, 0.f, 0.f}, dbx[4] = {0.f, 0.f, 0.f, 0.f}, dbr[4] = {0.f, 0.f, 0.f, 0.f},
+          dbo[4] = {0.f, 0.f, 0.f, 0.f};
     float sdot = 0.f;
+    f32x4 dP[2], dA[2];
+    dP[0] = dP[1] = dA[0] = dA[1] = zero4();
 
     for (int cv = 0; cv < NDC; ++cv) {
       auto& B = sm.u.b;
-      __syncthreads(); // previous slice's readers are done
-      // state slice S[:, cv*DC + dvl] and dSn slice, both from transposed bf16 tapes
-      for (int idx = tid; idx < DC * (D / 8); idx += NTHREADS) {
-        const int dvl = idx & (DC - 1), pc = idx / DC;
-        const size_t off = ((size_t)c * a.HV + h) * D * D + (size_t)(cv * DC + dvl) * D + pc * 8;
-        const bf16x8 sv = *reinterpret_cast<const bf16x8*>(htape + off);
-        const bf16x8 dv = *reinterpret_cast<const bf16x8*>(dstape + off);
-        *reinterpret_cast<bf16x8*>(B.sS_tr + dvl * SK + pc * 8) = sv;
-        *reinterpret_cast<bf16x8*>(B.sdS_tr + dvl * SK + pc * 8) = dv;
+      __syncthreads(); // readers of the previous slice are done
+      {
+        const int dvl = tid / (D / 8), pc = tid % (D / 8);
+        if (dvl < DC) {
+          *reinterpret_cast<bf16x8*>(B.sS + dvl * SK + pc * 8) = nS;
+          *reinterpret_cast<bf16x8*>(B.sdS + dvl * SK + pc * 8) = ndS;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          B.sS_rm[(pc * 8 + e) * SDC + dvl] = sv[e];
-          B.sdS_rm[(pc * 8 + e) * SDC + dvl] = dv[e];
-          sdot += (float)sv[e] * (float)dv[e];
+          for (int e = 0; e < 8; ++e) sdot += (float)nS[e] * (float)ndS[e];
         }
+        const int u = tid & 255, r = u >> 2, pv = u & 3;
+        if (tid < 256) *reinterpret_cast<bf16x8*>(B.sdO + r * SDO + pv * 8) = nx;
+        else *reinterpret_cast<bf16x8*>(B.sV + r * SV + pv * 8) = nx;
       }
-      for (int idx = tid; idx < CH * (DC / 8); idx += NTHREADS) {
-        const int r = idx & 63, pc = idx >> 6;
-        const bf16x8 ov =
-            r < len ? IO<TI>::load8(dop + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + pc * 8) : zero8();
-        *reinterpret_cast<bf16x8*>(B.sdO_rm + r * SDC + pc * 8) = ov;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) B.sdO_tr[(pc * 8 + e) * STK + r] = ov[e];
-      }
-      float vv[2][4];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + lg * 4 + i;
-          vv[ct][i] = r < len ? IO<TI>::load1(vp + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + 16 * ct + lr) : 0.f;
-        }
+      if (cv + 1 < NDC) prefetch(h, cv + 1);
       __syncthreads();
 
-      f32x4 ksv[2], kdv[2], pdv[2];
+      // this wave's 16 x 16 tile of the slice: rows row0.., slice columns 16*half..
+      const int cs = 16 * half;
+      f32x4 ksv = zero4(), kdv = zero4(), qsv = zero4(), pdv = zero4();
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        ksv[ct] = kdv[ct] = pdv[ct] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ak = lds8(sm.sK, SK, 16 * w + lr, ks * 32 + lg * 8);
-          ksv[ct] = mfma(ak, lds8(B.sS_tr, SK, 16 * ct + lr, ks * 32 + lg * 8), ksv[ct]);
-          kdv[ct] = mfma(ak, lds8(B.sdS_tr, SK, 16 * ct + lr, ks * 32 + lg * 8), kdv[ct]);
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          pdv[ct] = mfma(lds8(sm.sPT, STK, 16 * w + lr, k2 * 32 + lg * 8),
-                         lds8(B.sdO_tr, STK, 16 * ct + lr, k2 * 32 + lg * 8), pdv[ct]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 bS = lds8(B.sS, SK, cs + lr, ks * 32 + lg * 8);
+        const bf16x8 fk = lds8(sm.sK, SK, arow, ks * 32 + lg * 8);
+        ksv = mfma(fk, bS, ksv);
+        qsv = mfma(lds8(sm.sQ, SK, arow, ks * 32 + lg * 8), bS, qsv);
+        kdv = mfma(fk, lds8(B.sdS, SK, cs + lr, ks * 32 + lg * 8), kdv);
       }
-      float xu[2][4];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        float x[4], dr[4];
+      for (int k2 = 0; k2 < 2; ++k2) pdv = mfma(fpt[k2], lds_tr8(B.sdO, SDO, k2 * 32, cs), pdv);
+      float xu[4], x[4], dr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-          xu[ct][i] = vv[ct][i] - brow[i] * rk_r[i] * ksv[ct][i];
-          x[i] = beta_r[i] * xu[ct][i];
-          dr[i] = pdv[ct][i] + dec_r[i] * rk_r[i] * kdv[ct][i];
-          B.sX_rm[r * SDC + cc] = (bf16)x[i];
-          B.sdR_rm[r * SDC + cc] = (bf16)dr[i];
-        }
-        lds_store4_t(B.sX_tr, STK, 16 * ct + lr, 16 * w + lg * 4, x[0], x[1], x[2], x[3]);
-        lds_store4_t(B.sdR_tr, STK, 16 * ct + lr, 16 * w + lg * 4, dr[0], dr[1], dr[2], dr[3]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lg * 4 + i, cc = cs + lr;
+        const float vv = (float)B.sV[r * SV + cc];
+        const float dov = (float)B.sdO[r * SDO + cc];
+        xu[i] = vv - brow[i] * rk_r[i] * ksv[i];
+        x[i] = beta_r[i] * xu[i];
+        dr[i] = pdv[i] + dec_r[i] * rk_r[i] * kdv[i];
+        dbo[i] += rq_r[i] * qsv[i] * dov;
       }
+      lds_store4_t(B.sXT, SA, cs + lr, row0 + lg * 4, x[0], x[1], x[2], x[3]);
+      lds_store4_t(B.sdRT, SA, cs + lr, row0 + lg * 4, dr[0], dr[1], dr[2], dr[3]);
       __syncthreads();
 
+      f32x4 R = zero4(), dX = zero4();
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        R = mfma(lds8(sm.sA, SA, arow, k2 * 32 + lg * 8), lds8(B.sXT, SA, cs + lr, k2 * 32 + lg * 8), R);
+        dX = mfma(lds_tr8(sm.sA, SA, k2 * 32, row0), lds8(B.sdRT, SA, cs + lr, k2 * 32 + lg * 8), dX);
+      }
       TI* dvp = (TI*)a.dv;
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f32x4 R = zero4(), dX = zero4();
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          R = mfma(lds8(sm.sA, STK, 16 * w + lr, k2 * 32 + lg * 8), lds8(B.sX_tr, STK, 16 * ct + lr, k2 * 32 + lg * 8),
-                   R);
-          dX = mfma(lds8(sm.sAT, STK, 16 * w + lr, k2 * 32 + lg * 8),
-                    lds8(B.sdR_tr, STK, 16 * ct + lr, k2 * 32 + lg * 8), dX);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-          B.sR_rm[r * SDC + cc] = (bf16)R[i];
-          B.sdX_rm[r * SDC + cc] = (bf16)dX[i];
-          zpart[i] += rk_r[i] * kdv[ct][i] * R[i];
-          dbx[i] += xu[ct][i] * dX[i];
-          dbr[i] -= beta_r[i] * rk_r[i] * ksv[ct][i] * dX[i];
-          if (r < len) IO<TI>::store1(dvp + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + cc, beta_r[i] * dX[i]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lg * 4 + i, cc = cs + lr;
+        zp[i] += rk_r[i] * kdv[i] * R[i];
+        dbx[i] += xu[i] * dX[i];
+        dbr[i] -= beta_r[i] * rk_r[i] * ksv[i] * dX[i];
+        if (r < len) IO<TI>::store1(dvp + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + cc, beta_r[i] * dX[i]);
       }
+      lds_store4_t(B.sRT, SA, cs + lr, row0 + lg * 4, R[0], R[1], R[2], R[3]);
+      lds_store4_t(B.sdXT, SA, cs + lr, row0 + lg * 4, dX[0], dX[1], dX[2], dX[3]);
       __syncthreads();
 
+      // value-dimension contractions over this slice (32 = one MFMA k-step)
+      const bf16x8 aO = lds8(B.sdO, SDO, arow, lg * 8);
+      const bf16x8 aOb = scale8(aO, a_b);
+      const bf16x8 aR = scale8(lds_tr8(B.sRT, SA, 0, row0), a_dec);
+      const bf16x8 aX = scale8(lds_tr8(B.sdXT, SA, 0, row0), a_nbb);
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-        const bf16x8 bS = lds8(B.sS_rm, SDC, 16 * t + lr, lg * 8);
-        dOS[t] = mfma(lds8(B.sdO_rm, SDC, 16 * w + lr, lg * 8), bS, dOS[t]);
-        dXS[t] = mfma(lds8(B.sdX_rm, SDC, 16 * w + lr, lg * 8), bS, dXS[t]);
-        RdS[t] = mfma(lds8(B.sR_rm, SDC, 16 * w + lr, lg * 8), lds8(B.sdS_rm, SDC, 16 * t + lr, lg * 8), RdS[t]);
+      for (int t = 0; t < NT2; ++t) {
+        const int dcol = 16 * (half * NT2 + t);
+        const bf16x8 bS = lds_tr8(B.sS, SK, 0, dcol);
+        dQacc[t] = mfma(aOb, bS, dQacc[t]);
+        dKacc[t] = mfma(aX, bS, dKacc[t]);
+        dKacc[t] = mfma(aR, lds_tr8(B.sdS, SK, 0, dcol), dKacc[t]);
       }
+      const bf16x8 adR = lds_tr8(B.sdRT, SA, 0, row0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        dP[t] = mfma(lds8(B.sdO_rm, SDC, 16 * w + lr, lg * 8), lds8(B.sR_rm, SDC, 16 * t + lr, lg * 8), dP[t]);
-        dA[t] = mfma(lds8(B.sdR_rm, SDC, 16 * w + lr, lg * 8), lds8(B.sX_rm, SDC, 16 * t + lr, lg * 8), dA[t]);
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int ct = 2 * half + c2;
+        dP[c2] = mfma(aO, lds_tr8(B.sRT, SA, 0, 16 * ct), dP[c2]);
+        dA[c2] = mfma(adR, lds_tr8(B.sXT, SA, 0, 16 * ct), dA[c2]);
       }
     }
 
     // ---- per-head tail
-    auto& Tt = sm.u.t;
-    // row sums over the 16 lanes of a row group; block sum of <dSn, S>
+    auto& T = sm.u.t;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      zpart[i] = sum16(zpart[i]);
+      zp[i] = sum16(zp[i]);
       dbx[i] = sum16(dbx[i]);
       dbr[i] = sum16(dbr[i]);
+      dbo[i] = sum16(dbo[i]);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sdot += __shfl_xor(sdot, off);
-    __syncthreads(); // all slice readers done: the union switches to the tail layout
+    __syncthreads(); // slice tiles are dead: the union switches to the tail layout
     if (lane == 0) sm.sred[w] = sdot;
-    // dQk (masked dP o Gam) scaled two ways, dGam from dP, and dA
-    float dgam[4][4], gmat[4][4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      float tq[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-        const bool lo = r >= cc;
-        const float gm = lo ? expf(sm.sG[r] - sm.sG[cc]) : 0.f;
-        gmat[ct][i] = gm;
-        const float dqk = lo ? dP[ct][i] * gm : 0.f;
-        dgam[ct][i] = lo ? dP[ct][i] * Qk[ct][i] : 0.f;
-        Tt.sT1[r * STK + cc] = (bf16)(dqk * sm.srk[cc]);
-        tq[i] = dqk * rq_r[i];
-        Tt.sT3[r * STK + cc] = (bf16)dA[ct][i];
-      }
-      lds_store4_t(Tt.sT2, STK, 16 * ct + lr, 16 * w + lg * 4, tq[0], tq[1], tq[2], tq[3]);
-    }
-    __syncthreads();
-    // M1 = dA A^T
-    f32x4 m1[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      m1[ct] = zero4();
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-        m1[ct] = mfma(lds8(Tt.sT3, STK, 16 * w + lr, k2 * 32 + lg * 8), lds8(sm.sA, STK, 16 * ct + lr, k2 * 32 + lg * 8),
-                      m1[ct]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      lds_store4_t(Tt.sT3, STK, 16 * ct + lr, 16 * w + lg * 4, m1[ct][0], m1[ct][1], m1[ct][2], m1[ct][3]);
-    __syncthreads();
-    // dL = -A^T M1 (strictly lower)
-    float dbl[4] = {0.f, 0.f, 0.f, 0.f};
-    float dkk[4][4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-        acc = mfma(lds8(sm.sAT, STK, 16 * w + lr, k2 * 32 + lg * 8), lds8(Tt.sT3, STK, 16 * ct + lr, k2 * 32 + lg * 8),
-                   acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-        const float dl = r > cc ? -acc[i] : 0.f;
-        dbl[i] += dl * gmat[ct][i] * Kk[ct][i];
-        dkk[ct][i] = dl * beta_r[i] * gmat[ct][i];
-        dgam[ct][i] += dl * beta_r[i] * Kk[ct][i];
-        Tt.sM[r][cc] = dgam[ct][i] * gmat[ct][i];
-      }
-    }
-    __syncthreads(); // done reading sT3 (M1^T)
-    // dKs = dKk + dKk^T (symmetric, zero diagonal), columns scaled by rk
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-        if (r > cc) {
-          Tt.sT3[r * STK + cc] = (bf16)(dkk[ct][i] * sm.srk[cc]);
-          Tt.sT3[cc * STK + r] = (bf16)(dkk[ct][i] * sm.srk[r]);
-        } else if (r == cc) {
-          Tt.sT3[r * STK + r] = (bf16)0.f;
-        }
-      }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dbl[i] = sum16(dbl[i]);
-    __syncthreads();
-
-    // dQh = diag(b) dOS + (dQk rk) K ; dKh = dec R dSn^T - beta b dXS + (dQk rq)^T Q + (dKs rk) K
-    float dbo[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-      f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8 bK = lds8(sm.sKT, STK, 16 * t + lr, k2 * 32 + lg * 8);
-        a1 = mfma(lds8(Tt.sT1, STK, 16 * w + lr, k2 * 32 + lg * 8), bK, a1);
-        a2 = mfma(lds8(Tt.sT2, STK, 16 * w + lr, k2 * 32 + lg * 8), lds8(sm.sQT, STK, 16 * t + lr, k2 * 32 + lg * 8),
-                  a2);
-        a3 = mfma(lds8(Tt.sT3, STK, 16 * w + lr, k2 * 32 + lg * 8), bK, a3);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i, dk = 16 * t + lr;
-        const float qv = (float)sm.sQT[dk * STK + r];
-        dbo[i] += rq_r[i] * qv * dOS[t][i];
-        const float dq = brow[i] * dOS[t][i] + a1[i];
-        const float dkv = dec_r[i] * RdS[t][i] - beta_r[i] * brow[i] * dXS[t][i] + a2[i] + a3[i];
-        if (DET) {
-          dQacc[t][i] += dq;
-          dKacc[t][i] += dkv;
-        } else if (r < len) {
-          atomicAdd(a.dqacc + ((size_t)(t0 + r) * a.H + j) * D + dk, dq);
-          atomicAdd(a.dkacc + ((size_t)(t0 + r) * a.H + j) * D + dk, dkv);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dbo[i] = sum16(dbo[i]);
     if (lr == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i;
-        sm.sZ[r] = zpart[i];
-        sm.sDb[r] = dbo[i] + dbr[i];
-        sm.sDbeta[r] = dbx[i] + dbl[i];
+        const int r = row0 + lg * 4 + i;
+        sm.sRow[half][0][r] = zp[i];
+        sm.sRow[half][1][r] = dbo[i] + dbr[i];
+        sm.sRow[half][2][r] = dbx[i];
       }
     }
+    float gm[2][4], dgam[2][4];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int ct = 2 * half + c2, cc = 16 * ct + lr;
+      float t1[4], t2[4], t3[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lg * 4 + i;
+        const bool lo = r >= cc;
+        gm[c2][i] = lo ? __expf(sm.sG[r] - sm.sG[cc]) : 0.f;
+        const float dqk = lo ? dP[c2][i] * gm[c2][i] : 0.f;
+        dgam[c2][i] = lo ? dP[c2][i] * Qk[c2][i] : 0.f;
+        t1[i] = dqk * sm.srk[cc];
+        t2[i] = dqk * rq_r[i];
+        t3[i] = dA[c2][i];
+      }
+      lds_store4_t(T.sT1t, SA, cc, row0 + lg * 4, t1[0], t1[1], t1[2], t1[3]); // (dQk rk)^T
+      lds_store4_t(T.sT2, SA, cc, row0 + lg * 4, t2[0], t2[1], t2[2], t2[3]);  // (dQk rq)^T
+      lds_store4_t(T.sT3, SA, cc, row0 + lg * 4, t3[0], t3[1], t3[2], t3[3]);  // dA^T
+    }
     __syncthreads();
+    // M1 = dA A^T
+    f32x4 m1[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int ct = 2 * half + c2;
+      m1[c2] = zero4();
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        m1[c2] = mfma(lds_tr8(T.sT3, SA, k2 * 32, row0), lds8(sm.sA, SA, 16 * ct + lr, k2 * 32 + lg * 8), m1[c2]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int ct = 2 * half + c2;
+      lds_store4_t(T.sT3, SA, 16 * ct + lr, row0 + lg * 4, m1[c2][0], m1[c2][1], m1[c2][2], m1[c2][3]); // M1^T
+    }
+    __syncthreads();
+    // dL = -A^T M1 (strictly lower)
+    float dbl[4] = {0.f, 0.f, 0.f, 0.f}, dkk[2][4];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int ct = 2 * half + c2, cc = 16 * ct + lr;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        acc = mfma(lds_tr8(sm.sA, SA, k2 * 32, row0), lds8(T.sT3, SA, 16 * ct + lr, k2 * 32 + lg * 8), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lg * 4 + i;
+        const float dl = r > cc ? -acc[i] : 0.f;
+        dbl[i] += dl * gm[c2][i] * Kk[c2][i];
+        dkk[c2][i] = dl * beta_r[i] * gm[c2][i];
+        dgam[c2][i] += dl * beta_r[i] * Kk[c2][i];
+        T.sM[r][cc] = dgam[c2][i] * gm[c2][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dbl[i] = sum16(dbl[i]);
+    if (lr == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.sRow[half][3][row0 + lg * 4 + i] = dbl[i];
+    }
+    __syncthreads(); // done reading M1^T
+    // dKs = dKk + dKk^T (symmetric, zero diagonal), columns scaled by rk
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lg * 4 + i, cc = 16 * (2 * half + c2) + lr;
+        if (r > cc) {
+          T.sT3[r * SA + cc] = (bf16)(dkk[c2][i] * sm.srk[cc]);
+          T.sT3[cc * SA + r] = (bf16)(dkk[c2][i] * sm.srk[r]);
+        } else if (r == cc) {
+          T.sT3[r * SA + r] = (bf16)0.f;
+        }
+      }
+    __syncthreads();
+    // dQh += (dQk rk) K ; dKh += (dQk rq)^T Q + (dKs rk) K
+    {
+      const bf16x8 a1[2] = {lds_tr8(T.sT1t, SA, 0, row0), lds_tr8(T.sT1t, SA, 32, row0)};
+      const bf16x8 a2[2] = {lds8(T.sT2, SA, arow, lg * 8), lds8(T.sT2, SA, arow, 32 + lg * 8)};
+      const bf16x8 a3[2] = {lds8(T.sT3, SA, arow, lg * 8), lds8(T.sT3, SA, arow, 32 + lg * 8)};
+#pragma unroll
+      for (int t = 0; t < NT2; ++t) {
+        const int dcol = 16 * (half * NT2 + t);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const bf16x8 bK = lds_tr8(sm.sK, SK, k2 * 32, dcol);
+          dQacc[t] = mfma(a1[k2], bK, dQacc[t]);
+          dKacc[t] = mfma(a2[k2], lds_tr8(sm.sQ, SK, k2 * 32, dcol), dKacc[t]);
+          dKacc[t] = mfma(a3[k2], bK, dKacc[t]);
+        }
+      }
+    }
     if (w == 0) {
       const int r = lane;
       float rows = 0.f, cols = 0.f;
       for (int x = 0; x < CH; ++x) {
-        rows += Tt.sM[r][x];
-        cols += Tt.sM[x][r];
+        rows += T.sM[r][x];
+        cols += T.sM[x][r];
       }
       const bool ok = r < len;
-      const float dec = ok ? expf(glast - sm.sG[r]) : 0.f;
-      const float zd = ok ? sm.sZ[r] * dec : 0.f;
+      const float dec = ok ? __expf(glast - sm.sG[r]) : 0.f;
+      const float z = sm.sRow[0][0][r] + sm.sRow[1][0][r];
+      const float db = sm.sRow[0][1][r] + sm.sRow[1][1][r];
+      const float dbeta = sm.sRow[0][2][r] + sm.sRow[1][2][r] + sm.sRow[0][3][r] + sm.sRow[1][3][r];
+      const float zd = ok ? z * dec : 0.f;
       float zsum = zd;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) zsum += __shfl_xor(zsum, off);
-      float dG = ok ? rows - cols + expf(sm.sG[r]) * sm.sDb[r] - zd : 0.f;
-      if (r == len - 1) dG += gam * (sm.sred[0] + sm.sred[1] + sm.sred[2] + sm.sred[3]) + zsum;
-      float x = dG;
+      float dG = ok ? rows - cols + __expf(sm.sG[r]) * db - zd : 0.f;
+      float sd = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sd += sm.sred[q];
+      if (r == len - 1) dG += gam * sd + zsum;
+      float xs = dG;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_down(x, off);
-        if (lane + off < 64) x += y;
+        const float y = __shfl_down(xs, off);
+        if (lane + off < 64) xs += y;
       }
       if (ok) {
-        a.dg[(size_t)(t0 + r) * a.HV + h] = x;
-        a.dbeta[(size_t)(t0 + r) * a.HV + h] = sm.sDbeta[r];
+        a.dg[(size_t)(t0 + r) * a.HV + h] = xs;
+        a.dbeta[(size_t)(t0 + r) * a.HV + h] = dbeta;
       }
+    }
+    if (!DET) {
+#pragma unroll
+      for (int t = 0; t < NT2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0 + lg * 4 + i, dk = 16 * (half * NT2 + t) + lr;
+          if (r < len) {
+            atomicAdd(a.dqacc + ((size_t)(t0 + r) * a.H + j) * D + dk, dQacc[t][i]);
+            atomicAdd(a.dkacc + ((size_t)(t0 + r) * a.H + j) * D + dk, dKacc[t][i]);
+          }
+        }
     }
   }
 
@@ -785,37 +814,46 @@ __global__ __launch_bounds__(NTHREADS) void k_chunk_grad(Args a) {
     TI* dqp = (TI*)a.dq;
     TI* dkp = (TI*)a.dk;
     float qd[4] = {0.f, 0.f, 0.f, 0.f}, kd[4] = {0.f, 0.f, 0.f, 0.f};
-    float rq_r[4], rk_r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rq_r[i] = sm.srq[16 * w + lg * 4 + i];
-      rk_r[i] = sm.srk[16 * w + lg * 4 + i];
-    }
     if (a.l2norm) {
 #pragma unroll
-      for (int t = 0; t < NDT; ++t)
+      for (int t = 0; t < NT2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + lg * 4 + i, dk = 16 * t + lr;
-          qd[i] += rq_r[i] * (float)sm.sQT[dk * STK + r] * dQacc[t][i];
-          kd[i] += rk_r[i] * (float)sm.sKT[dk * STK + r] * dKacc[t][i];
+          const int r = row0 + lg * 4 + i, dk = 16 * (half * NT2 + t) + lr;
+          qd[i] += rq_r[i] * (float)sm.sQ[r * SK + dk] * dQacc[t][i];
+          kd[i] += rk_r[i] * (float)sm.sK[r * SK + dk] * dKacc[t][i];
         }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         qd[i] = sum16(qd[i]);
         kd[i] = sum16(kd[i]);
       }
-    }
+      __syncthreads();
+      if (lr == 0) {
 #pragma unroll
-    for (int t = 0; t < NDT; ++t)
+        for (int i = 0; i < 4; ++i) {
+          sm.sRow[half][0][row0 + lg * 4 + i] = qd[i];
+          sm.sRow[half][1][row0 + lg * 4 + i] = kd[i];
+        }
+      }
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i, dk = 16 * t + lr;
+        const int r = row0 + lg * 4 + i;
+        qd[i] = sm.sRow[0][0][r] + sm.sRow[1][0][r];
+        kd[i] = sm.sRow[0][1][r] + sm.sRow[1][1][r];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lg * 4 + i, dk = 16 * (half * NT2 + t) + lr;
         if (r >= len) continue;
         float dqv = dQacc[t][i], dkv = dKacc[t][i];
         if (a.l2norm) {
-          dqv = rq_r[i] * (dqv - rq_r[i] * (float)IO<TI>::load1(qp + ((size_t)(t0 + r) * a.H + j) * D + dk) * qd[i]);
-          dkv = rk_r[i] * (dkv - rk_r[i] * (float)IO<TI>::load1(kp + ((size_t)(t0 + r) * a.H + j) * D + dk) * kd[i]);
+          dqv = rq_r[i] * (dqv - rq_r[i] * (float)sm.sQ[r * SK + dk] * qd[i]);
+          dkv = rk_r[i] * (dkv - rk_r[i] * (float)sm.sK[r * SK + dk] * kd[i]);
         }
         IO<TI>::store1(dqp + ((size_t)(t0 + r) * a.H + j) * D + dk, dqv);
         IO<TI>::store1(dkp + ((size_t)(t0 + r) * a.H + j) * D + dk, dkv);
@@ -826,8 +864,8 @@ __global__ __launch_bounds__(NTHREADS) void k_chunk_grad(Args a) {
 template <int D, typename TI>
 static int chunk_grad_t(const Args& a, int det, hipStream_t s) {
   if (a.NT == 0) return 0;
-  if (det) hipLaunchKernelGGL((k_chunk_grad<D, TI, true>), dim3(a.NT, a.H), dim3(NTHREADS), 0, s, a);
-  else hipLaunchKernelGGL((k_chunk_grad<D, TI, false>), dim3(a.NT, a.HV), dim3(NTHREADS), 0, s, a);
+  if (det) hipLaunchKernelGGL((k_chunk_grad<D, TI, true>), dim3(a.NT, a.H), dim3(GRAD_THREADS), 0, s, a);
+  else hipLaunchKernelGGL((k_chunk_grad<D, TI, false>), dim3(a.NT, a.HV), dim3(GRAD_THREADS), 0, s, a);
   return (int)hipGetLastError();
 }
 

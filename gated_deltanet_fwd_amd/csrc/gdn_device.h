@@ -39,6 +39,24 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* base, int stride, int row, in
   return *reinterpret_cast<const bf16x8*>(base + row * stride + col);
 }
 
+// Transposed fragment read from an LDS tile stored row-major as tile[k][m] (m contiguous,
+// `stride` elements per row, rows 8-byte aligned): lane l receives tile[k0 + (l/16)*8 + e][m0 + l%16]
+// for e = 0..7, i.e. an MFMA A (or B) fragment of the transposed tile. Uses ds_read_b64_tr_b16,
+// which hands lane i of each 16-lane group element i%4 of the 8-byte blocks addressed by lanes
+// i/4, i/4+4, i/4+8, i/4+12 of that group (layout checked on gfx950 by a lane probe).
+__device__ __forceinline__ bf16x8 lds_tr8(const bf16* tile, int stride, int k0, int m0) {
+  const int l = threadIdx.x & 63;
+  const int g = l >> 4, j = l & 15;
+  const bf16* p0 = tile + (k0 + g * 8 + (j >> 2)) * stride + m0 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 4 * stride));
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
 // Store 4 values of one column, rows r..r+3, into an LDS tile stored transposed
 // (tile[col][row]): one 8-byte write.
 __device__ __forceinline__ void lds_store4_t(bf16* base, int stride, int col, int row, float a, float b, float c,

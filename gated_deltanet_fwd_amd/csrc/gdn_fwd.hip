@@ -91,50 +91,13 @@ __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu,
 }
 
 // ---------------------------------------------------------------------------------------
-// (I + L)^-1 of a 64x64 unit lower-triangular matrix (strict lower part in Lm), FP32 in LDS.
-// Diagonal 16x16 blocks by forward substitution (one lane per column), then block rows in
-// order: A_ij = -A_ii * sum_{m=j}^{i-1} L_im A_mj. Ends with a barrier.
-__device__ void invert64(float (*Lm)[CH + 1], float (*A)[CH + 1], float (*Tm)[16][17], int tid) {
-  const int w = tid >> 6, lane = tid & 63;
-  if (lane < 16) {
-    const int b0 = 16 * w, col = lane;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = (i == col) ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) s -= Lm[b0 + i][b0 + m] * x[m];
-      x[i] = (i < col) ? 0.f : s;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) A[b0 + i][b0 + col] = x[i];
-  }
-  __syncthreads();
-  for (int bi = 1; bi < 4; ++bi) {
-    for (int e = tid; e < bi * 256; e += 256) {
-      const int bj = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      float s = 0.f;
-      for (int m = bj; m < bi; ++m) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) s += Lm[16 * bi + r][16 * m + x] * A[16 * m + x][16 * bj + cc];
-      }
-      Tm[bj][r][cc] = s;
-    }
-    __syncthreads();
-    for (int e = tid; e < bi * 256; e += 256) {
-      const int bj = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      float s = 0.f;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) s += A[16 * bi + r][16 * bi + x] * Tm[bj][x][cc];
-      A[16 * bi + r][16 * bj + cc] = -s;
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// Per (chunk, q/k head): inverse norms rk, rq; normalised q.k (bf16, workspace; transposed for
-// the backward); and, unless BWD, per value head of the group: gcum, gamma and Akk (saved).
+// Per (chunk, q/k head): inverse norms rk, rq; normalised q.k (bf16, workspace; row-major for the
+// forward, transposed for the backward); and, unless BWD, per value head of the group: gcum,
+// gamma and Akk = (I + L)^-1 (saved).
+//
+// K K^T and the q.k products run on MFMA; each wave keeps 16 rows of K K^T in registers. The
+// inverse runs one value head per wave: every lane owns one column c of A and forward-substitutes
+// it, x_i = -sum_{m<i} L_im x_m (x_c = 1), reading rows of L from LDS as broadcasts.
 template <int D, typename TI, bool BWD>
 __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
   if (a.status[0]) return;
@@ -145,91 +108,101 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   constexpr int SK = D + PAD;
-  constexpr int PPR = D / 8;
-  __shared__ __attribute__((aligned(16))) bf16 sK[CH * SK];
-  __shared__ __attribute__((aligned(16))) bf16 sQ[CH * SK];
-  __shared__ float srk[CH], srq[CH], sG[CH], sB[CH];
-  __shared__ float sKK[CH][CH + 1];
-  __shared__ float sL[CH][CH + 1];
-  __shared__ float sA[CH][CH + 1];
-  __shared__ float sT[3][16][17];
+  constexpr int SL = CH + 4; // fp32 row stride of L: 16-byte aligned rows
+  constexpr int KS = D / 32;
+  constexpr int NB = 4;      // value heads per batch, one wave each
+  struct KQ {
+    bf16 k[CH * SK];
+    bf16 q[CH * SK];
+  };
+  union Smem {
+    KQ kq;
+    float L[NB][CH][SL];
+  };
+  __shared__ __attribute__((aligned(16))) Smem u;
+  __shared__ float srk[CH], srq[CH];
+  __shared__ float sG[NB][CH], sB[NB][CH];
   const TI* kp = (const TI*)a.k;
   const TI* qp = (const TI*)a.q;
 
-  for (int idx = tid; idx < CH * PPR; idx += NTHREADS) {
-    const int r = idx / PPR, pc = idx % PPR;
+  // this wave's 16 rows of K and Q (MFMA A fragments), their squared norms
+  const int ar = 16 * w + lr;
+  const bool ok = ar < len;
+  bf16x8 fk[KS], fq[KS];
+  float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
     float kf[8], qf[8];
-    if (r < len) {
-      IO<TI>::load8f(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8, kf);
-      IO<TI>::load8f(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8, qf);
+    if (ok) {
+      IO<TI>::load8f(kp + ((size_t)(t0 + ar) * a.H + j) * D + ks * 32 + lg * 8, kf);
+      IO<TI>::load8f(qp + ((size_t)(t0 + ar) * a.H + j) * D + ks * 32 + lg * 8, qf);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kf[e] = qf[e] = 0.f;
     }
-    float ssk = 0.f, ssq = 0.f;
-    bf16x8 kb, qb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       ssk += kf[e] * kf[e];
       ssq += qf[e] * qf[e];
-      kb[e] = (bf16)kf[e];
-      qb[e] = (bf16)qf[e];
+      fk[ks][e] = (bf16)kf[e];
+      fq[ks][e] = (bf16)qf[e];
     }
-    *reinterpret_cast<bf16x8*>(sK + r * SK + pc * 8) = kb;
-    *reinterpret_cast<bf16x8*>(sQ + r * SK + pc * 8) = qb;
-#pragma unroll
-    for (int off = PPR / 2; off >= 1; off >>= 1) {
-      ssk += __shfl_xor(ssk, off);
-      ssq += __shfl_xor(ssq, off);
-    }
-    if (pc == 0) {
-      const float rkv = a.l2norm ? 1.f / sqrtf(ssk + 1e-6f) : 1.f;
-      const float rqv = a.l2norm ? 1.f / sqrtf(ssq + 1e-6f) : 1.f;
-      srk[r] = r < len ? rkv : 0.f;
-      srq[r] = r < len ? rqv : 0.f;
-      if (r < len) {
-        a.rk[(size_t)(t0 + r) * a.H + j] = rkv;
-        a.rq[(size_t)(t0 + r) * a.H + j] = rqv;
-      }
+    *reinterpret_cast<bf16x8*>(u.kq.k + ar * SK + ks * 32 + lg * 8) = fk[ks];
+    *reinterpret_cast<bf16x8*>(u.kq.q + ar * SK + ks * 32 + lg * 8) = fq[ks];
+  }
+  ssk += __shfl_xor(ssk, 16);
+  ssk += __shfl_xor(ssk, 32);
+  ssq += __shfl_xor(ssq, 16);
+  ssq += __shfl_xor(ssq, 32);
+  if (lg == 0) {
+    const float rkv = a.l2norm ? 1.f / sqrtf(ssk + 1e-6f) : 1.f;
+    const float rqv = a.l2norm ? 1.f / sqrtf(ssq + 1e-6f) : 1.f;
+    srk[ar] = ok ? rkv : 0.f;
+    srq[ar] = ok ? rqv : 0.f;
+    if (ok) {
+      a.rk[(size_t)(t0 + ar) * a.H + j] = rkv;
+      a.rq[(size_t)(t0 + ar) * a.H + j] = rqv;
     }
   }
   __syncthreads();
 
-  // K K^T and Q K^T: wave w owns rows 16w..16w+15
+  // K K^T (rows k, cols k) and, for the q.k tile, Q K^T (backward: rows q) or K Q^T (forward:
+  // rows k), so that the stored layout is written 4 contiguous elements per lane.
   f32x4 kk[4], qk[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) kk[ct] = qk[ct] = zero4();
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    const bf16x8 ak = lds8(sK, SK, 16 * w + lr, ks * 32 + lg * 8);
-    const bf16x8 aq = lds8(sQ, SK, 16 * w + lr, ks * 32 + lg * 8);
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const bf16x8 bk = lds8(sK, SK, 16 * ct + lr, ks * 32 + lg * 8);
-      kk[ct] = mfma(ak, bk, kk[ct]);
-      qk[ct] = mfma(aq, bk, qk[ct]);
+      const bf16x8 bk = lds8(u.kq.k, SK, 16 * ct + lr, ks * 32 + lg * 8);
+      kk[ct] = mfma(fk[ks], bk, kk[ct]);
+      if (BWD) qk[ct] = mfma(fq[ks], bk, qk[ct]);
+      else qk[ct] = mfma(fk[ks], lds8(u.kq.q, SK, 16 * ct + lr, ks * 32 + lg * 8), qk[ct]);
     }
-  }
   bf16* qkout = reinterpret_cast<bf16*>(a.qk) + ((size_t)c * a.H + j) * CH * CH;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
+    const int cc = 16 * ct + lr;
+    float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-      sKK[r][cc] = kk[ct][i] * srk[r] * srk[cc];
-      const bf16 qv = (bf16)(r >= cc ? qk[ct][i] * srq[r] * srk[cc] : 0.f);
-      if (BWD) qkout[cc * CH + r] = qv;
-      else qkout[r * CH + cc] = qv;
+      const int r = 16 * w + lg * 4 + i;
+      kk[ct][i] *= srk[r] * srk[cc];
+      // backward: C[q = r][k = cc], kept for q >= k; forward: C[k = r][q = cc], kept for q >= k
+      v[i] = BWD ? (r >= cc ? qk[ct][i] * srq[r] * srk[cc] : 0.f) : (cc >= r ? qk[ct][i] * srk[r] * srq[cc] : 0.f);
     }
+    // backward stores QKT[k][q], forward QK[q][k]: both are [cc][r..r+3]
+    lds_store4_t(qkout, CH, cc, 16 * w + lg * 4, v[0], v[1], v[2], v[3]);
   }
   if (BWD) return;
-  __syncthreads();
+  __syncthreads(); // the K/Q staging area becomes L
 
   bf16* aout = reinterpret_cast<bf16*>(a.akk);
-  for (int gi = 0; gi < a.G; ++gi) {
-    const int h = j * a.G + gi;
-    if (tid < CH) {
-      const int r = tid;
+  for (int hb = 0; hb < a.G; hb += NB) {
+    const int nb = min(NB, a.G - hb);
+    if (w < nb) {
+      const int h = j * a.G + hb + w, r = lane;
       const float gv = r < len ? a.g[(size_t)(t0 + r) * a.HV + h] : 0.f;
       const float bv = r < len ? a.beta[(size_t)(t0 + r) * a.HV + h] : 0.f;
       float x = gv;
@@ -238,21 +211,55 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
         const float y = __shfl_up(x, off);
         if (lane >= off) x += y;
       }
-      sG[r] = x;
-      sB[r] = bv;
+      sG[w][r] = x;
+      sB[w][r] = bv;
       if (r < len) a.gcum[(size_t)(t0 + r) * a.HV + h] = x;
-      if (r == len - 1) a.gamma[(size_t)c * a.HV + h] = expf(x);
+      if (r == len - 1) a.gamma[(size_t)c * a.HV + h] = __expf(x);
     }
     __syncthreads();
-    for (int idx = tid; idx < CH * CH; idx += NTHREADS) {
-      const int r = idx >> 6, cc = idx & 63;
-      sL[r][cc] = r > cc ? sB[r] * expf(sG[r] - sG[cc]) * sKK[r][cc] : 0.f;
+    for (int b = 0; b < nb; ++b)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
+          u.L[b][r][cc] = r > cc ? sB[b][r] * __expf(sG[b][r] - sG[b][cc]) * kk[ct][i] : 0.f;
+        }
+    __syncthreads();
+    if (w < nb) {
+      const int h = j * a.G + hb + w, col = lane;
+      float x[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+        for (int m = 0; m + 4 <= i; m += 4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&u.L[w][i][m]);
+          s0 = __builtin_fmaf(l4.x, x[m], s0);
+          s1 = __builtin_fmaf(l4.y, x[m + 1], s1);
+          s2 = __builtin_fmaf(l4.z, x[m + 2], s2);
+          s3 = __builtin_fmaf(l4.w, x[m + 3], s3);
+        }
+#pragma unroll
+        for (int m = (i / 4) * 4; m < i; ++m) s0 = __builtin_fmaf(u.L[w][i][m], x[m], s0);
+        x[i] = i < col ? 0.f : (i == col ? 1.f : -((s0 + s1) + (s2 + s3)));
+      }
+      // stage the inverse (bf16) in this wave's own L area, row-major
+      bf16* stage = reinterpret_cast<bf16*>(&u.L[w][0][0]);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) stage[i * (CH + PAD) + col] = (bf16)x[i];
     }
     __syncthreads();
-    invert64(sL, sA, sT, tid);
-    for (int idx = tid; idx < len * CH; idx += NTHREADS) {
-      const int r = idx >> 6, cc = idx & 63;
-      aout[((size_t)(t0 + r) * a.HV + h) * CH + cc] = (bf16)(cc <= r ? sA[r][cc] : 0.f);
+    if (w < nb) {
+      const int h = j * a.G + hb + w;
+      const bf16* stage = reinterpret_cast<const bf16*>(&u.L[w][0][0]);
+#pragma unroll
+      for (int it = 0; it < CH / 8; ++it) {
+        const int r = it * 8 + (lane >> 3), pc = lane & 7;
+        if (r < len)
+          *reinterpret_cast<bf16x8*>(aout + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) =
+              lds8(stage, CH + PAD, r, pc * 8);
+      }
     }
     __syncthreads();
   }
@@ -262,6 +269,25 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
 // State walk, one workgroup per (document, value head, value tile of DVT columns).
 // WRITE_O: write o (and ht). WRITE_TAPE: write the chunk-start state tape (bf16, transposed).
 // FULL: also write v_new = R.
+//
+// The next chunk's inputs are loaded into registers while the current chunk computes, so the
+// serial chain per chunk is LDS + MFMA only. K is staged row-major in LDS; its transpose for the
+// state update comes from transpose-reads.
+template <int D, int DVT>
+struct WalkSmem {
+  static constexpr int SK = D + 16;   // row stride of K (conflict-free transpose-reads)
+  static constexpr int SST = D + PAD; // row stride of S^T
+  static constexpr int STK = CH + PAD;
+  static constexpr int SV = DVT + PAD;
+  bf16 sK[CH * SK];
+  bf16 sST[DVT * SST];
+  bf16 sXT[DVT * STK];
+  bf16 sRT[DVT * STK];
+  bf16 sRdT[DVT * STK];
+  bf16 sV[CH * SV];
+  float sG[CH], sB[CH], srk[CH], srq[CH];
+};
+
 template <int D, int DVT, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL>
 __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
   if (a.status[0]) return;
@@ -276,19 +302,50 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
   constexpr int NCT = DVT / 16; // value-column tiles
   constexpr int NRT = D / 64;   // state row tiles per wave
   constexpr int KS = D / 32;    // k-steps over the key dim
-  constexpr int STK = CH + PAD; // stride of token-indexed transposed tiles
-  constexpr int SST = D + PAD;
-  __shared__ __attribute__((aligned(16))) bf16 sKT[D * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sST[DVT * SST];
-  __shared__ __attribute__((aligned(16))) bf16 sXT[DVT * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sRT[DVT * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sRdT[DVT * STK];
-  __shared__ float sG[CH], sB[CH], srk[CH], srq[CH];
+  using SM = WalkSmem<D, DVT>;
+  constexpr int SK = SM::SK, SST = SM::SST, STK = SM::STK, SV = SM::SV;
+  constexpr int VPR = DVT / 8; // 16-byte pieces per row of the value tile
+  __shared__ __attribute__((aligned(16))) SM sm;
   const TI* kp = (const TI*)a.k;
   const TI* qp = (const TI*)a.q;
   const TI* vp = (const TI*)a.v;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* qkp = reinterpret_cast<const bf16*>(a.qk);
+  const int ar = 16 * w + lr; // this lane's A-fragment row (token in the chunk)
+
+  // ---- prefetch registers: the chunk about to be processed
+  bf16x8 nk[KS], nq[KS], na[2], np[2], nv;
+  float ng = 0.f, nb = 0.f, nrk = 0.f, nrq = 0.f, ngam = 0.f;
+  int nlen = 0, nt0 = 0;
+  auto prefetch = [&](int c) {
+    nlen = a.c_len[c];
+    nt0 = a.c_t0[c];
+    const bool ok = ar < nlen;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      nk[ks] = ok ? IO<TI>::load8(kp + ((size_t)(nt0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
+      if (WRITE_O) nq[ks] = ok ? IO<TI>::load8(qp + ((size_t)(nt0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      na[k2] = ok ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(nt0 + ar) * a.HV + h) * CH + k2 * 32 + lg * 8)
+                  : zero8();
+      if (WRITE_O)
+        np[k2] = *reinterpret_cast<const bf16x8*>(qkp + ((size_t)c * a.H + j) * CH * CH + ar * CH + k2 * 32 + lg * 8);
+    }
+    if (tid < CH * VPR) {
+      const int r = tid / VPR, pc = tid % VPR;
+      nv = r < nlen ? IO<TI>::load8(vp + ((size_t)(nt0 + r) * a.HV + h) * D + col0 + pc * 8) : zero8();
+    }
+    if (tid < CH) {
+      const bool rok = tid < nlen;
+      ng = rok ? a.gcum[(size_t)(nt0 + tid) * a.HV + h] : 0.f;
+      nb = rok ? a.beta[(size_t)(nt0 + tid) * a.HV + h] : 0.f;
+      nrk = rok ? a.rk[(size_t)(nt0 + tid) * a.H + j] : 0.f;
+      nrq = rok ? a.rq[(size_t)(nt0 + tid) * a.H + j] : 0.f;
+    }
+    ngam = a.gamma[(size_t)c * a.HV + h];
+  };
 
   f32x4 S[NRT][NCT];
 #pragma unroll
@@ -304,66 +361,51 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
-      lds_store4_t(sST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, S[rt][ct][0], S[rt][ct][1], S[rt][ct][2],
-                   S[rt][ct][3]);
-  __syncthreads();
+      lds_store4_t(sm.sST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, S[rt][ct][0], S[rt][ct][1],
+                   S[rt][ct][2], S[rt][ct][3]);
+  if (c_begin < c_end) prefetch(c_begin);
 
   for (int c = c_begin; c < c_end; ++c) {
-    const int len = a.c_len[c], t0 = a.c_t0[c];
-    if (tid < CH) {
-      const int r = tid;
-      const bool ok = r < len;
-      sG[r] = ok ? a.gcum[(size_t)(t0 + r) * a.HV + h] : 0.f;
-      sB[r] = ok ? a.beta[(size_t)(t0 + r) * a.HV + h] : 0.f;
-      srk[r] = ok ? a.rk[(size_t)(t0 + r) * a.H + j] : 0.f;
-      srq[r] = ok ? a.rq[(size_t)(t0 + r) * a.H + j] : 0.f;
-    }
-    for (int idx = tid; idx < CH * (D / 8); idx += NTHREADS) {
-      const int r = idx & 63, pc = idx >> 6;
-      const bf16x8 kv = r < len ? IO<TI>::load8(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8) : zero8();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sKT[(pc * 8 + e) * STK + r] = kv[e];
-    }
-    const int ar = 16 * w + lr;
-    const bool arok = ar < len;
+    // ---- take the prefetched chunk, stage it, and start loading the next one
+    const int len = nlen, t0 = nt0;
+    const float gam = ngam;
     bf16x8 fk[KS], fq[KS], fa[2], fp[2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      fk[ks] = arok ? IO<TI>::load8(kp + ((size_t)(t0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
-      if (WRITE_O) fq[ks] = arok ? IO<TI>::load8(qp + ((size_t)(t0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
+      fk[ks] = nk[ks];
+      if (WRITE_O) fq[ks] = nq[ks];
+      *reinterpret_cast<bf16x8*>(sm.sK + ar * SK + ks * 32 + lg * 8) = nk[ks];
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      fa[k2] = arok ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + ar) * a.HV + h) * CH + k2 * 32 + lg * 8)
-                    : zero8();
-      if (WRITE_O)
-        fp[k2] = *reinterpret_cast<const bf16x8*>(qkp + ((size_t)c * a.H + j) * CH * CH + ar * CH + k2 * 32 + lg * 8);
+      fa[k2] = na[k2];
+      if (WRITE_O) fp[k2] = np[k2];
     }
-    float vv[NCT][4];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i;
-        vv[ct][i] = r < len ? IO<TI>::load1(vp + ((size_t)(t0 + r) * a.HV + h) * D + col0 + 16 * ct + lr) : 0.f;
-      }
-    const float gam = a.gamma[(size_t)c * a.HV + h];
+    if (tid < CH * VPR) *reinterpret_cast<bf16x8*>(sm.sV + (tid / VPR) * SV + (tid % VPR) * 8) = nv;
+    if (tid < CH) {
+      sm.sG[tid] = ng;
+      sm.sB[tid] = nb;
+      sm.srk[tid] = nrk;
+      sm.srq[tid] = nrq;
+    }
+    if (c + 1 < c_end) prefetch(c + 1);
     __syncthreads();
 
     if (WRITE_TAPE) {
       bf16* tp = reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D + (size_t)col0 * D;
       for (int idx = tid; idx < DVT * (D / 8); idx += NTHREADS) {
         const int cc = idx / (D / 8), pc = idx % (D / 8);
-        *reinterpret_cast<bf16x8*>(tp + (size_t)cc * D + pc * 8) = lds8(sST, SST, cc, pc * 8);
+        *reinterpret_cast<bf16x8*>(tp + (size_t)cc * D + pc * 8) = lds8(sm.sST, SST, cc, pc * 8);
       }
     }
     if (WRITE_O) {
+      const float gr = sm.sG[ar];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int jj = k2 * 32 + lg * 8 + e;
-          fp[k2][e] = (jj <= ar) ? (bf16)(expf(sG[ar] - sG[jj]) * (float)fp[k2][e]) : (bf16)0.f;
+          fp[k2][e] = (jj <= ar) ? (bf16)(__expf(gr - sm.sG[jj]) * (float)fp[k2][e]) : (bf16)0.f;
         }
     }
     f32x4 ksv[NCT], qsv[NCT];
@@ -373,41 +415,53 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const bf16x8 bS = lds8(sST, SST, 16 * ct + lr, kk * 32 + lg * 8);
+        const bf16x8 bS = lds8(sm.sST, SST, 16 * ct + lr, kk * 32 + lg * 8);
         ksv[ct] = mfma(fk[kk], bS, ksv[ct]);
         if (WRITE_O) qsv[ct] = mfma(fq[kk], bS, qsv[ct]);
       }
-    float brow[4];
+    float brow[4], krow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) brow[i] = expf(sG[16 * w + lg * 4 + i]);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + lg * 4 + i;
+      brow[i] = __expf(sm.sG[r]);
+      krow[i] = brow[i] * sm.srk[r];
+    }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + lg * 4 + i;
-        x[i] = sB[r] * (vv[ct][i] - brow[i] * srk[r] * ksv[ct][i]);
+        const float vv = (float)sm.sV[r * SV + 16 * ct + lr];
+        x[i] = sm.sB[r] * (vv - krow[i] * ksv[ct][i]);
       }
-      lds_store4_t(sXT, STK, 16 * ct + lr, 16 * w + lg * 4, x[0], x[1], x[2], x[3]);
+      lds_store4_t(sm.sXT, STK, 16 * ct + lr, 16 * w + lg * 4, x[0], x[1], x[2], x[3]);
     }
     __syncthreads();
 
-    const float glast = sG[len - 1];
+    const float glast = sm.sG[len - 1];
+    float dec[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + lg * 4 + i;
+      dec[i] = __expf(glast - sm.sG[r]) * sm.srk[r];
+    }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 R = zero4();
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) R = mfma(fa[k2], lds8(sXT, STK, 16 * ct + lr, k2 * 32 + lg * 8), R);
-      float rd[4];
+      for (int k2 = 0; k2 < 2; ++k2) R = mfma(fa[k2], lds8(sm.sXT, STK, 16 * ct + lr, k2 * 32 + lg * 8), R);
+      if (FULL) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i;
-        rd[i] = expf(glast - sG[r]) * srk[r] * R[i];
-        if (FULL && r < len)
-          reinterpret_cast<bf16*>(a.vnew)[((size_t)(t0 + r) * a.HV + h) * D + col0 + 16 * ct + lr] = (bf16)R[i];
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + lg * 4 + i;
+          if (r < len)
+            reinterpret_cast<bf16*>(a.vnew)[((size_t)(t0 + r) * a.HV + h) * D + col0 + 16 * ct + lr] = (bf16)R[i];
+        }
       }
-      lds_store4_t(sRT, STK, 16 * ct + lr, 16 * w + lg * 4, R[0], R[1], R[2], R[3]);
-      lds_store4_t(sRdT, STK, 16 * ct + lr, 16 * w + lg * 4, rd[0], rd[1], rd[2], rd[3]);
+      lds_store4_t(sm.sRT, STK, 16 * ct + lr, 16 * w + lg * 4, R[0], R[1], R[2], R[3]);
+      lds_store4_t(sm.sRdT, STK, 16 * ct + lr, 16 * w + lg * 4, dec[0] * R[0], dec[1] * R[1], dec[2] * R[2],
+                   dec[3] * R[3]);
     }
     __syncthreads();
 
@@ -417,13 +471,13 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(fp[k2], lds8(sRT, STK, 16 * ct + lr, k2 * 32 + lg * 8), acc);
+        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(fp[k2], lds8(sm.sRT, STK, 16 * ct + lr, k2 * 32 + lg * 8), acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * w + lg * 4 + i;
           if (r < len)
             IO<TI>::store1(op + ((size_t)(t0 + r) * a.HV + h) * D + col0 + 16 * ct + lr,
-                           brow[i] * srq[r] * qsv[ct][i] + acc[i]);
+                           brow[i] * sm.srq[r] * qsv[ct][i] + acc[i]);
         }
       }
     }
@@ -434,8 +488,8 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
-          acc = mfma(lds8(sKT, STK, 16 * (w * NRT + rt) + lr, k2 * 32 + lg * 8),
-                     lds8(sRdT, STK, 16 * ct + lr, k2 * 32 + lg * 8), acc);
+          acc = mfma(lds_tr8(sm.sK, SK, k2 * 32, 16 * (w * NRT + rt)),
+                     lds8(sm.sRdT, STK, 16 * ct + lr, k2 * 32 + lg * 8), acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[rt][ct][i] = __builtin_fmaf(gam, S[rt][ct][i], acc[i]);
       }
@@ -444,7 +498,7 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        lds_store4_t(sST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, S[rt][ct][0], S[rt][ct][1],
+        lds_store4_t(sm.sST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, S[rt][ct][0], S[rt][ct][1],
                      S[rt][ct][2], S[rt][ct][3]);
   }
   if (WRITE_O && a.want_ht) {
