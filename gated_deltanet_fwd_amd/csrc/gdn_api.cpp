@@ -123,7 +123,7 @@ WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
   L.status = take(4);
   L.rk = take((size_t)s.T * s.H * 4);
   L.rq = take((size_t)s.T * s.H * 4);
-  L.qk = take((size_t)s.NT * s.H * kChunk * kChunk * 2);
+  L.qk = take((size_t)s.NT * s.HV * kChunk * kChunk * 2);
   if (op == GDN_OP_BWD) {
     if (!full) L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
     L.dstape = take((size_t)s.NT * s.HV * s.D * s.D * 2);

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(NTHREADS) void k_wy_full(Args a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kf[e] = vf[e] = 0.f;
     }
-    const float sk = sB[r] * expf(sG[r]) * srk[r], sv = sB[r];
+    const float sk = sB[r] * __expf(sG[r]) * srk[r], sv = sB[r];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sKsT[(pc * 8 + e) * STK + r] = (bf16)(kf[e] * sk);
@@ -119,12 +119,12 @@ __global__ __launch_bounds__(NTHREADS) void k_wy_full(Args a) {
       }
     }
   }
-  const bf16* qkp = reinterpret_cast<const bf16*>(a.qk) + ((size_t)c * a.H + j) * CH * CH;
+  const bf16* pp = reinterpret_cast<const bf16*>(a.qk) + ((size_t)c * a.HV + h) * CH * CH;
   bf16* aq = reinterpret_cast<bf16*>(a.aqk);
-  for (int idx = tid; idx < len * CH; idx += NTHREADS) {
-    const int r = idx >> 6, cc = idx & 63;
-    const float p = cc <= r ? expf(sG[r] - sG[cc]) * (float)qkp[r * CH + cc] : 0.f;
-    aq[((size_t)(t0 + r) * a.HV + h) * CH + cc] = (bf16)p;
+  for (int idx = tid; idx < len * (CH / 8); idx += NTHREADS) {
+    const int r = idx >> 3, pc = idx & 7;
+    *reinterpret_cast<bf16x8*>(aq + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) =
+        *reinterpret_cast<const bf16x8*>(pp + r * CH + pc * 8);
   }
 }
 
@@ -192,35 +192,39 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
 
   // ---- prefetch registers
   bf16x8 nk[KS], nq[KS], na[2], np[2], ndo;
-  float ng = 0.f, nb = 0.f, nrk = 0.f, ngam = 0.f, nsc = 0.f;
+  float ng = 0.f, nb = 0.f, nrk = 0.f, ngam = 0.f, nsc = 0.f, nrq = 0.f;
   int nlen = 0, nt0 = 0;
+  // chunk c of the document starts at token cu[n] + 64 (c - c_begin): no table lookup on the
+  // serial path
+  const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
   auto prefetch = [&](int c) {
-    nlen = a.c_len[c];
-    nt0 = a.c_t0[c];
-    const bool ok = ar < nlen;
+    nt0 = doc_t0 + (c - c_begin) * CH;
+    nlen = min(CH, doc_t1 - nt0);
+    // unconditional loads from rows clamped into the chunk; rows past its end are zeroed when
+    // the data is consumed
+    const int rr = min(ar, nlen - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      nk[ks] = ok ? IO<TI>::load8(kp + ((size_t)(nt0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
-      nq[ks] = ok ? IO<TI>::load8(qp + ((size_t)(nt0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
+      nk[ks] = IO<TI>::load8(kp + ((size_t)(nt0 + rr) * a.H + j) * D + ks * 32 + lg * 8);
+      nq[ks] = IO<TI>::load8(qp + ((size_t)(nt0 + rr) * a.H + j) * D + ks * 32 + lg * 8);
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      na[k2] = ok ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(nt0 + ar) * a.HV + h) * CH + k2 * 32 + lg * 8)
-                  : zero8();
-      np[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.H + j) * CH * CH + ar * CH + k2 * 32 + lg * 8);
+      na[k2] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(nt0 + rr) * a.HV + h) * CH + k2 * 32 + lg * 8);
+      np[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + ar * CH + k2 * 32 + lg * 8);
     }
     if (tid < CH * VPR) {
-      const int r = tid / VPR, pc = tid % VPR;
-      const bool rok = r < nlen;
-      ndo = rok ? IO<TI>::load8(dop + ((size_t)(nt0 + r) * a.HV + h) * D + col0 + pc * 8) : zero8();
-      // scale of row r in Qh^T diag(b) dO: exp(gcum) * rq
-      nsc = rok ? __expf(a.gcum[(size_t)(nt0 + r) * a.HV + h]) * a.rq[(size_t)(nt0 + r) * a.H + j] : 0.f;
+      const int r = min(tid / VPR, nlen - 1), pc = tid % VPR;
+      ndo = IO<TI>::load8(dop + ((size_t)(nt0 + r) * a.HV + h) * D + col0 + pc * 8);
+      // scale of row r in Qh^T diag(b) dO: exp(gcum) * rq (applied when staged)
+      nsc = a.gcum[(size_t)(nt0 + r) * a.HV + h];
+      nrq = a.rq[(size_t)(nt0 + r) * a.H + j];
     }
     if (tid < CH) {
-      const bool rok = tid < nlen;
-      ng = rok ? a.gcum[(size_t)(nt0 + tid) * a.HV + h] : 0.f;
-      nb = rok ? a.beta[(size_t)(nt0 + tid) * a.HV + h] : 0.f;
-      nrk = rok ? a.rk[(size_t)(nt0 + tid) * a.H + j] : 0.f;
+      const int r = min(tid, nlen - 1);
+      ng = a.gcum[(size_t)(nt0 + r) * a.HV + h];
+      nb = a.beta[(size_t)(nt0 + r) * a.HV + h];
+      nrk = a.rk[(size_t)(nt0 + r) * a.H + j];
     }
     ngam = a.gamma[(size_t)c * a.HV + h];
   };
@@ -246,6 +250,8 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
   for (int c = c_end - 1; c >= c_begin; --c) {
     const int len = nlen;
     const float gam = ngam;
+    // K, Q and A rows past the chunk's end hold copies of its last row: finite, and their
+    // contributions vanish (rk, beta and the dO scale are zero there, P^T is masked)
     bf16x8 fk[KS], fpt[2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -260,16 +266,20 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
     }
     if (tid < CH * VPR) {
       const int r = tid / VPR, pc = tid % VPR;
-      *reinterpret_cast<bf16x8*>(sm.sdO + r * SDO + pc * 8) = ndo;
+      const bool rok = r < len;
+      const bf16x8 dov = rok ? ndo : zero8();
+      *reinterpret_cast<bf16x8*>(sm.sdO + r * SDO + pc * 8) = dov;
+      const float scl = rok ? __expf(nsc) * nrq : 0.f;
       bf16x8 sc;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sc[e] = (bf16)(nsc * (float)ndo[e]);
+      for (int e = 0; e < 8; ++e) sc[e] = (bf16)(scl * (float)dov[e]);
       *reinterpret_cast<bf16x8*>(sm.sdOp + r * SDO + pc * 8) = sc;
     }
     if (tid < CH) {
-      sm.sG[tid] = ng;
-      sm.sB[tid] = nb;
-      sm.srk[tid] = nrk;
+      const bool rok = tid < len;
+      sm.sG[tid] = rok ? ng : 0.f;
+      sm.sB[tid] = rok ? nb : 0.f;
+      sm.srk[tid] = rok ? nrk : 0.f;
     }
     if (c - 1 >= c_begin) prefetch(c - 1);
     __syncthreads();
@@ -280,16 +290,6 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
         const int cc = idx / (D / 8), pc = idx % (D / 8);
         *reinterpret_cast<bf16x8*>(tp + (size_t)cc * D + pc * 8) = lds8(sm.sdST, SST, cc, pc * 8);
       }
-    }
-    {
-      const float gr = sm.sG[ar];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ii = k2 * 32 + lg * 8 + e;
-          fpt[k2][e] = (ii >= ar) ? (bf16)(__expf(sm.sG[ii] - gr) * (float)fpt[k2][e]) : (bf16)0.f;
-        }
     }
     const float glast = sm.sG[len - 1];
     float dec[4], ybr[4];
@@ -503,9 +503,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       nS = *reinterpret_cast<const bf16x8*>(htape + off);
       ndS = *reinterpret_cast<const bf16x8*>(dstape + off);
     }
-    const int u = tid & 255, r = u >> 2, pv = u & 3;
+    const int u = tid & 255, r = min(u >> 2, len - 1), pv = u & 3;
     const TI* src = tid < 256 ? dop : vp;
-    nx = r < len ? IO<TI>::load8(src + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + pv * 8) : zero8();
+    nx = IO<TI>::load8(src + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + pv * 8); // rows past len zeroed when staged
   };
 
   for (int hh = 0; hh < h_count; ++hh) {
@@ -526,20 +526,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     bf16x8 fpt[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
-      fpt[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.H + j) * CH * CH + arow * CH + k2 * 32 + lg * 8);
+      fpt[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + arow * CH + k2 * 32 + lg * 8);
     prefetch(h, 0);
     __syncthreads();
     const float glast = sm.sG[len - 1];
-    {
-      const float ga = sm.sG[arow];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ii = k2 * 32 + lg * 8 + e;
-          fpt[k2][e] = (ii >= arow) ? (bf16)(__expf(sm.sG[ii] - ga) * (float)fpt[k2][e]) : (bf16)0.f;
-        }
-    }
     // per-row factors: this lane's C rows (r) and A-fragment row (arow)
     float brow[4], beta_r[4], dec_r[4];
 #pragma unroll
@@ -571,8 +561,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
           for (int e = 0; e < 8; ++e) sdot += (float)nS[e] * (float)ndS[e];
         }
         const int u = tid & 255, r = u >> 2, pv = u & 3;
-        if (tid < 256) *reinterpret_cast<bf16x8*>(B.sdO + r * SDO + pv * 8) = nx;
-        else *reinterpret_cast<bf16x8*>(B.sV + r * SV + pv * 8) = nx;
+        const bf16x8 xv = r < len ? nx : zero8();
+        if (tid < 256) *reinterpret_cast<bf16x8*>(B.sdO + r * SDO + pv * 8) = xv;
+        else *reinterpret_cast<bf16x8*>(B.sV + r * SV + pv * 8) = xv;
       }
       if (cv + 1 < NDC) prefetch(h, cv + 1);
       __syncthreads();

@@ -180,43 +180,63 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
       if (BWD) qk[ct] = mfma(fq[ks], bk, qk[ct]);
       else qk[ct] = mfma(fk[ks], lds8(u.kq.q, SK, 16 * ct + lr, ks * 32 + lg * 8), qk[ct]);
     }
-  bf16* qkout = reinterpret_cast<bf16*>(a.qk) + ((size_t)c * a.H + j) * CH * CH;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int cc = 16 * ct + lr;
-    float v[4];
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + lg * 4 + i;
+      const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
       kk[ct][i] *= srk[r] * srk[cc];
-      // backward: C[q = r][k = cc], kept for q >= k; forward: C[k = r][q = cc], kept for q >= k
-      v[i] = BWD ? (r >= cc ? qk[ct][i] * srq[r] * srk[cc] : 0.f) : (cc >= r ? qk[ct][i] * srk[r] * srq[cc] : 0.f);
+      // backward: C[q = r][k = cc]; forward: C[k = r][q = cc]
+      qk[ct][i] *= BWD ? srq[r] * srk[cc] : srk[r] * srq[cc];
     }
-    // backward stores QKT[k][q], forward QK[q][k]: both are [cc][r..r+3]
-    lds_store4_t(qkout, CH, cc, 16 * w + lg * 4, v[0], v[1], v[2], v[3]);
-  }
-  if (BWD) return;
-  __syncthreads(); // the K/Q staging area becomes L
 
   bf16* aout = reinterpret_cast<bf16*>(a.akk);
   for (int hb = 0; hb < a.G; hb += NB) {
     const int nb = min(NB, a.G - hb);
     if (w < nb) {
       const int h = j * a.G + hb + w, r = lane;
-      const float gv = r < len ? a.g[(size_t)(t0 + r) * a.HV + h] : 0.f;
-      const float bv = r < len ? a.beta[(size_t)(t0 + r) * a.HV + h] : 0.f;
-      float x = gv;
+      float x;
+      if (BWD) {
+        x = r < len ? a.gcum[(size_t)(t0 + r) * a.HV + h] : 0.f;
+      } else {
+        const float gv = r < len ? a.g[(size_t)(t0 + r) * a.HV + h] : 0.f;
+        const float bv = r < len ? a.beta[(size_t)(t0 + r) * a.HV + h] : 0.f;
+        x = gv;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off);
+          if (lane >= off) x += y;
+        }
+        sB[w][r] = bv;
+        if (r < len) a.gcum[(size_t)(t0 + r) * a.HV + h] = x;
+        if (r == len - 1) a.gamma[(size_t)c * a.HV + h] = __expf(x);
       }
       sG[w][r] = x;
-      sB[w][r] = bv;
-      if (r < len) a.gcum[(size_t)(t0 + r) * a.HV + h] = x;
-      if (r == len - 1) a.gamma[(size_t)c * a.HV + h] = __expf(x);
     }
     __syncthreads();
+    // P_qk = exp(G_q - G_k) qh.kh for q >= k, per value head: the forward stores P[q][k], the
+    // backward P^T[k][q]; both are [cc][r..r+3] of this wave's tile
+    for (int b = 0; b < nb; ++b) {
+      const int h = j * a.G + hb + b;
+      bf16* pout = reinterpret_cast<bf16*>(a.qk) + ((size_t)c * a.HV + h) * CH * CH;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int cc = 16 * ct + lr;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + lg * 4 + i;
+          const int qi = BWD ? r : cc, ki = BWD ? cc : r;
+          const float e = __expf(fminf(sG[b][qi] - sG[b][ki], 0.f));
+          v[i] = qi >= ki ? e * qk[ct][i] : 0.f;
+        }
+        lds_store4_t(pout, CH, cc, 16 * w + lg * 4, v[0], v[1], v[2], v[3]);
+      }
+    }
+    if (BWD) {
+      __syncthreads();
+      continue;
+    }
     for (int b = 0; b < nb; ++b)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
@@ -288,6 +308,14 @@ struct WalkSmem {
   float sG[CH], sB[CH], srk[CH], srq[CH];
 };
 
+// Inputs of one chunk, loaded into registers one chunk ahead of use.
+template <int KS>
+struct WalkPrefetch {
+  bf16x8 k[KS], q[KS], a[2], p[2], v;
+  float g, b, rk, rq, gam;
+  int len, t0;
+};
+
 template <int D, int DVT, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL>
 __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
   if (a.status[0]) return;
@@ -312,39 +340,42 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* qkp = reinterpret_cast<const bf16*>(a.qk);
   const int ar = 16 * w + lr; // this lane's A-fragment row (token in the chunk)
+  // chunk c of the document starts at token cu[n] + 64 (c - c_begin): no table lookup on the
+  // serial path
+  const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
+  using PF = WalkPrefetch<KS>;
 
-  // ---- prefetch registers: the chunk about to be processed
-  bf16x8 nk[KS], nq[KS], na[2], np[2], nv;
-  float ng = 0.f, nb = 0.f, nrk = 0.f, nrq = 0.f, ngam = 0.f;
-  int nlen = 0, nt0 = 0;
-  auto prefetch = [&](int c) {
-    nlen = a.c_len[c];
-    nt0 = a.c_t0[c];
-    const bool ok = ar < nlen;
+  // Unconditional loads from rows clamped into the chunk; rows past its end are zeroed when the
+  // data is consumed, so nothing waits on a load before its use one chunk later.
+  auto prefetch = [&](PF& P, int c) {
+    P.t0 = doc_t0 + (c - c_begin) * CH;
+    P.len = min(CH, doc_t1 - P.t0);
+    const int rr = min(ar, P.len - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      nk[ks] = ok ? IO<TI>::load8(kp + ((size_t)(nt0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
-      if (WRITE_O) nq[ks] = ok ? IO<TI>::load8(qp + ((size_t)(nt0 + ar) * a.H + j) * D + ks * 32 + lg * 8) : zero8();
+      P.k[ks] = IO<TI>::load8(kp + ((size_t)(P.t0 + rr) * a.H + j) * D + ks * 32 + lg * 8);
+      if (WRITE_O) P.q[ks] = IO<TI>::load8(qp + ((size_t)(P.t0 + rr) * a.H + j) * D + ks * 32 + lg * 8);
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      na[k2] = ok ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(nt0 + ar) * a.HV + h) * CH + k2 * 32 + lg * 8)
-                  : zero8();
+      P.a[k2] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(P.t0 + rr) * a.HV + h) * CH + k2 * 32 + lg * 8);
       if (WRITE_O)
-        np[k2] = *reinterpret_cast<const bf16x8*>(qkp + ((size_t)c * a.H + j) * CH * CH + ar * CH + k2 * 32 + lg * 8);
+        P.p[k2] = *reinterpret_cast<const bf16x8*>(qkp + ((size_t)c * a.HV + h) * CH * CH + ar * CH + k2 * 32 + lg * 8);
     }
-    if (tid < CH * VPR) {
-      const int r = tid / VPR, pc = tid % VPR;
-      nv = r < nlen ? IO<TI>::load8(vp + ((size_t)(nt0 + r) * a.HV + h) * D + col0 + pc * 8) : zero8();
+    // every thread loads (threads past the tile re-read a valid row), so no load sits in a
+    // divergent branch and the wait counts before each use stay exact
+    {
+      const int r = min((tid / VPR) % CH, P.len - 1), pc = tid % VPR;
+      P.v = IO<TI>::load8(vp + ((size_t)(P.t0 + r) * a.HV + h) * D + col0 + pc * 8);
     }
-    if (tid < CH) {
-      const bool rok = tid < nlen;
-      ng = rok ? a.gcum[(size_t)(nt0 + tid) * a.HV + h] : 0.f;
-      nb = rok ? a.beta[(size_t)(nt0 + tid) * a.HV + h] : 0.f;
-      nrk = rok ? a.rk[(size_t)(nt0 + tid) * a.H + j] : 0.f;
-      nrq = rok ? a.rq[(size_t)(nt0 + tid) * a.H + j] : 0.f;
+    {
+      const int r = min(tid % CH, P.len - 1);
+      P.g = a.gcum[(size_t)(P.t0 + r) * a.HV + h];
+      P.b = a.beta[(size_t)(P.t0 + r) * a.HV + h];
+      P.rk = a.rk[(size_t)(P.t0 + r) * a.H + j];
+      P.rq = a.rq[(size_t)(P.t0 + r) * a.H + j];
     }
-    ngam = a.gamma[(size_t)c * a.HV + h];
+    P.gam = a.gamma[(size_t)c * a.HV + h];
   };
 
   f32x4 S[NRT][NCT];
@@ -363,32 +394,25 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
     for (int ct = 0; ct < NCT; ++ct)
       lds_store4_t(sm.sST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, S[rt][ct][0], S[rt][ct][1],
                    S[rt][ct][2], S[rt][ct][3]);
-  if (c_begin < c_end) prefetch(c_begin);
 
-  for (int c = c_begin; c < c_end; ++c) {
-    // ---- take the prefetched chunk, stage it, and start loading the next one
-    const int len = nlen, t0 = nt0;
-    const float gam = ngam;
-    bf16x8 fk[KS], fq[KS], fa[2], fp[2];
+  // one chunk: stage P into LDS, start loading chunk `cn` into Q, then the chunk's products and
+  // the state update
+  auto step = [&](const PF& P, int c, PF& Q, int cn) {
+    const int len = P.len, t0 = P.t0;
+    const float gam = P.gam;
+    // K, Q, A and V rows past the chunk's end hold copies of its last row: they stay finite and
+    // their contributions vanish because beta and rk are zero there and P is masked
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      fk[ks] = nk[ks];
-      if (WRITE_O) fq[ks] = nq[ks];
-      *reinterpret_cast<bf16x8*>(sm.sK + ar * SK + ks * 32 + lg * 8) = nk[ks];
-    }
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      fa[k2] = na[k2];
-      if (WRITE_O) fp[k2] = np[k2];
-    }
-    if (tid < CH * VPR) *reinterpret_cast<bf16x8*>(sm.sV + (tid / VPR) * SV + (tid % VPR) * 8) = nv;
+    for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<bf16x8*>(sm.sK + ar * SK + ks * 32 + lg * 8) = P.k[ks];
+    if (tid < CH * VPR) *reinterpret_cast<bf16x8*>(sm.sV + (tid / VPR) * SV + (tid % VPR) * 8) = P.v;
     if (tid < CH) {
-      sm.sG[tid] = ng;
-      sm.sB[tid] = nb;
-      sm.srk[tid] = nrk;
-      sm.srq[tid] = nrq;
+      const bool rok = tid < len;
+      sm.sG[tid] = rok ? P.g : 0.f;
+      sm.sB[tid] = rok ? P.b : 0.f;
+      sm.srk[tid] = rok ? P.rk : 0.f;
+      sm.srq[tid] = rok ? P.rq : 0.f;
     }
-    if (c + 1 < c_end) prefetch(c + 1);
+    if (cn < c_end) prefetch(Q, cn);
     __syncthreads();
 
     if (WRITE_TAPE) {
@@ -398,16 +422,6 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
         *reinterpret_cast<bf16x8*>(tp + (size_t)cc * D + pc * 8) = lds8(sm.sST, SST, cc, pc * 8);
       }
     }
-    if (WRITE_O) {
-      const float gr = sm.sG[ar];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = k2 * 32 + lg * 8 + e;
-          fp[k2][e] = (jj <= ar) ? (bf16)(__expf(gr - sm.sG[jj]) * (float)fp[k2][e]) : (bf16)0.f;
-        }
-    }
     f32x4 ksv[NCT], qsv[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) ksv[ct] = qsv[ct] = zero4();
@@ -416,52 +430,51 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const bf16x8 bS = lds8(sm.sST, SST, 16 * ct + lr, kk * 32 + lg * 8);
-        ksv[ct] = mfma(fk[kk], bS, ksv[ct]);
-        if (WRITE_O) qsv[ct] = mfma(fq[kk], bS, qsv[ct]);
+        ksv[ct] = mfma(P.k[kk], bS, ksv[ct]);
+        if (WRITE_O) qsv[ct] = mfma(P.q[kk], bS, qsv[ct]);
       }
+    const int r0 = 16 * w + lg * 4;
+    const float4 g4 = *reinterpret_cast<const float4*>(&sm.sG[r0]);
+    const float4 b4 = *reinterpret_cast<const float4*>(&sm.sB[r0]);
+    const float4 k4 = *reinterpret_cast<const float4*>(&sm.srk[r0]);
+    const float4 q4 = *reinterpret_cast<const float4*>(&sm.srq[r0]);
+    const float grow[4] = {g4.x, g4.y, g4.z, g4.w}, brw[4] = {b4.x, b4.y, b4.z, b4.w};
+    const float rkw[4] = {k4.x, k4.y, k4.z, k4.w}, rqw[4] = {q4.x, q4.y, q4.z, q4.w};
     float brow[4], krow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + lg * 4 + i;
-      brow[i] = __expf(sm.sG[r]);
-      krow[i] = brow[i] * sm.srk[r];
+      brow[i] = __expf(grow[i]);
+      krow[i] = brow[i] * rkw[i];
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + lg * 4 + i;
-        const float vv = (float)sm.sV[r * SV + 16 * ct + lr];
-        x[i] = sm.sB[r] * (vv - krow[i] * ksv[ct][i]);
+        const float vv = (float)sm.sV[(r0 + i) * SV + 16 * ct + lr];
+        x[i] = brw[i] * (vv - krow[i] * ksv[ct][i]);
       }
-      lds_store4_t(sm.sXT, STK, 16 * ct + lr, 16 * w + lg * 4, x[0], x[1], x[2], x[3]);
+      lds_store4_t(sm.sXT, STK, 16 * ct + lr, r0, x[0], x[1], x[2], x[3]);
     }
     __syncthreads();
 
     const float glast = sm.sG[len - 1];
     float dec[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + lg * 4 + i;
-      dec[i] = __expf(glast - sm.sG[r]) * sm.srk[r];
-    }
+    for (int i = 0; i < 4; ++i) dec[i] = __expf(glast - grow[i]) * rkw[i];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 R = zero4();
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) R = mfma(fa[k2], lds8(sm.sXT, STK, 16 * ct + lr, k2 * 32 + lg * 8), R);
+      for (int k2 = 0; k2 < 2; ++k2) R = mfma(P.a[k2], lds8(sm.sXT, STK, 16 * ct + lr, k2 * 32 + lg * 8), R);
       if (FULL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + lg * 4 + i;
-          if (r < len)
-            reinterpret_cast<bf16*>(a.vnew)[((size_t)(t0 + r) * a.HV + h) * D + col0 + 16 * ct + lr] = (bf16)R[i];
-        }
+        for (int i = 0; i < 4; ++i)
+          if (r0 + i < len)
+            reinterpret_cast<bf16*>(a.vnew)[((size_t)(t0 + r0 + i) * a.HV + h) * D + col0 + 16 * ct + lr] = (bf16)R[i];
       }
-      lds_store4_t(sm.sRT, STK, 16 * ct + lr, 16 * w + lg * 4, R[0], R[1], R[2], R[3]);
-      lds_store4_t(sm.sRdT, STK, 16 * ct + lr, 16 * w + lg * 4, dec[0] * R[0], dec[1] * R[1], dec[2] * R[2],
-                   dec[3] * R[3]);
+      lds_store4_t(sm.sRT, STK, 16 * ct + lr, r0, R[0], R[1], R[2], R[3]);
+      lds_store4_t(sm.sRdT, STK, 16 * ct + lr, r0, dec[0] * R[0], dec[1] * R[1], dec[2] * R[2], dec[3] * R[3]);
     }
     __syncthreads();
 
@@ -471,14 +484,13 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(fp[k2], lds8(sm.sRT, STK, 16 * ct + lr, k2 * 32 + lg * 8), acc);
+        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(P.p[k2], lds8(sm.sRT, STK, 16 * ct + lr, k2 * 32 + lg * 8), acc);
+        float ov[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + lg * 4 + i;
-          if (r < len)
-            IO<TI>::store1(op + ((size_t)(t0 + r) * a.HV + h) * D + col0 + 16 * ct + lr,
-                           brow[i] * sm.srq[r] * qsv[ct][i] + acc[i]);
-        }
+        for (int i = 0; i < 4; ++i) ov[i] = brow[i] * rqw[i] * qsv[ct][i] + acc[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r0 + i < len) IO<TI>::store1(op + ((size_t)(t0 + r0 + i) * a.HV + h) * D + col0 + 16 * ct + lr, ov[i]);
       }
     }
 #pragma unroll
@@ -500,6 +512,15 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
       for (int ct = 0; ct < NCT; ++ct)
         lds_store4_t(sm.sST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, S[rt][ct][0], S[rt][ct][1],
                      S[rt][ct][2], S[rt][ct][3]);
+  };
+
+  // two register sets, alternating: the loads for chunk c+1 fly while chunk c computes
+  PF pa, pb;
+  if (c_begin < c_end) prefetch(pa, c_begin);
+  for (int c = c_begin; c < c_end; c += 2) {
+    step(pa, c, pb, c + 1);
+    if (c + 1 >= c_end) break;
+    step(pb, c + 1, pa, c + 2);
   }
   if (WRITE_O && a.want_ht) {
 #pragma unroll

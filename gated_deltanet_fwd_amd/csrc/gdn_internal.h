@@ -48,16 +48,23 @@ struct Args {
   int* status;     // [1] nonzero if the device tables disagree with the host's chunk count
   float* rk;       // [T, H] inverse L2 norms of k rows (1 when the norm is off)
   float* rq;       // [T, H] inverse L2 norms of q rows
-  uint16_t* qk;    // bf16 [NT, H, 64, 64] normalised q.k per chunk (row-major fwd, transposed bwd)
+  uint16_t* qk;    // bf16 [NT, HV, 64, 64] P = exp(G_q - G_k) qh.kh masked to q >= k, per value head
+                   // (row-major P for the forward, P^T for the backward)
   uint16_t* dstape;// bf16 [NT, HV, d(value), d(key)]: gradient of each chunk's end state, transposed
   float* dqacc;    // f32 [T, H, d] (atomic reduction only)
   float* dkacc;    // f32 [T, H, d] (atomic reduction only)
 };
 
-// Value-column tile width of the forward state walk (columns of S per workgroup).
-constexpr int WALK_DVT = 32;
-// Value-column tile width of the reverse walk.
-constexpr int BWALK_DVT = 32;
+// Value-column tile width of the forward and reverse state walks (columns of S per workgroup).
+// The split does not change any column's arithmetic, only how the chains share the chip.
+#ifndef GDN_WALK_DVT
+#define GDN_WALK_DVT 32
+#endif
+#ifndef GDN_BWALK_DVT
+#define GDN_BWALK_DVT 32
+#endif
+constexpr int WALK_DVT = GDN_WALK_DVT;
+constexpr int BWALK_DVT = GDN_BWALK_DVT;
 
 int chain_blocks(const Args& a, int ntile);
 
