@@ -21,6 +21,12 @@ namespace gdn {
 
 static inline hipStream_t S_(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+__device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)(s * (float)v[e]);
+  return v;
+}
+
 // ---------------------------------------------------------------------------------------
 // utilities
 
@@ -143,213 +149,246 @@ int launch_wy_full(const Args& a, void* stream) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Reverse walk, one workgroup per (document, value head, value tile), chunks in reverse.
-// Writes the end-state gradient of every chunk (bf16, transposed) and dh0. The next chunk's
-// inputs are prefetched into registers; K, Q, A and dO are staged row-major and read transposed
-// with transpose-reads where a contraction runs over tokens.
-template <int D, int DVT>
+// Reverse walk, one workgroup per (document, value head), chunks in reverse. Writes the
+// end-state gradient of every chunk (bf16, transposed) and dh0. Same organisation as the forward
+// walk: wave w keeps its columns of dS and every per-chunk intermediate in registers, chaining
+// MFMA results into B operands with c_to_b; LDS holds the double-buffered chunk inputs (K, Q
+// pre-scaled by exp(gcum) rq, dO, A, P^T and the per-token scalars), one barrier per chunk.
+template <int D>
 struct BWalkSmem {
   static constexpr int SK = D + 16;
   static constexpr int SA = CH + 16;
-  static constexpr int SST = D + PAD;
-  static constexpr int STK = CH + PAD;
-  static constexpr int SDO = DVT + PAD;
-  bf16 sK[CH * SK];
-  bf16 sQ[CH * SK];
-  bf16 sA[CH * SA];
-  bf16 sdST[DVT * SST];
-  bf16 sdO[CH * SDO];
-  bf16 sdOp[CH * SDO];
-  bf16 sdRT[DVT * STK];
-  bf16 sYT[DVT * STK];
-  float sG[CH], sB[CH], srk[CH];
+  bf16 sK[2][CH * SK];
+  bf16 sQ[2][CH * SK];
+  bf16 sdO[2][CH * SK];
+  bf16 sA[2][CH * SA];
+  bf16 sPT[2][CH * SA];
+  float sc[2][3][CH]; // gcum, beta, rk (zero past the chunk's end)
 };
 
-template <int D, int DVT, typename TI>
-__global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
+template <int D, typename TI>
+__global__ __launch_bounds__(NTHREADS, 1) void k_walk_bwd(Args a) {
   if (a.status[0]) return;
-  constexpr int NTILE = D / DVT;
-  const ChainMap cm = decode_chain(blockIdx.x, a.N, a.H, a.G, NTILE);
+  const ChainMap cm = decode_chain(blockIdx.x, a.N, a.H, a.G, 1);
   if (!cm.valid) return;
   const int n = a.seq_order[cm.rank];
-  const int j = cm.j, h = j * a.G + cm.gi, col0 = cm.tile * DVT;
+  const int j = cm.j, h = j * a.G + cm.gi;
   const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  constexpr int NCT = DVT / 16;
-  constexpr int NRT = D / 64;
-  constexpr int KS = D / 32;
-  using SM = BWalkSmem<D, DVT>;
-  constexpr int SK = SM::SK, SA = SM::SA, SST = SM::SST, STK = SM::STK, SDO = SM::SDO;
-  constexpr int VPR = DVT / 8;
+  constexpr int NRT = D / 16, NCW = D / 64, KD = D / 32, PPT = D / 32, RP = D / 8;
+  using SM = BWalkSmem<D>;
+  constexpr int SK = SM::SK, SA = SM::SA;
   __shared__ __attribute__((aligned(16))) SM sm;
   const TI* kp = (const TI*)a.k;
   const TI* qp = (const TI*)a.q;
   const TI* dop = (const TI*)a.dO;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
-  const bf16* qkt = reinterpret_cast<const bf16*>(a.qk);
-  const int ar = 16 * w + lr;
-
-  // ---- prefetch registers
-  bf16x8 nk[KS], nq[KS], na[2], np[2], ndo;
-  float ng = 0.f, nb = 0.f, nrk = 0.f, ngam = 0.f, nsc = 0.f, nrq = 0.f;
-  int nlen = 0, nt0 = 0;
-  // chunk c of the document starts at token cu[n] + 64 (c - c_begin): no table lookup on the
-  // serial path
+  const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
+  const int v0 = 16 * NCW * w;
   const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
-  auto prefetch = [&](int c) {
-    nt0 = doc_t0 + (c - c_begin) * CH;
-    nlen = min(CH, doc_t1 - nt0);
-    // unconditional loads from rows clamped into the chunk; rows past its end are zeroed when
-    // the data is consumed
-    const int rr = min(ar, nlen - 1);
+
+  // staging (rows past the chunk's end re-read its last row; beta, rk and the q scale are zero
+  // there and P^T is masked, so they contribute nothing)
+  bf16x8 rK[PPT], rQ[PPT], rD[PPT], rA[2], rP[2];
+  float rqs[PPT], rS;
+  auto load_chunk = [&](int c) {
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int last = min(CH, doc_t1 - t0) - 1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      nk[ks] = IO<TI>::load8(kp + ((size_t)(nt0 + rr) * a.H + j) * D + ks * 32 + lg * 8);
-      nq[ks] = IO<TI>::load8(qp + ((size_t)(nt0 + rr) * a.H + j) * D + ks * 32 + lg * 8);
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + NTHREADS * it, row = p / RP, pc = p % RP, rr = t0 + min(row, last);
+      rK[it] = IO<TI>::load8(kp + ((size_t)rr * a.H + j) * D + pc * 8);
+      rQ[it] = IO<TI>::load8(qp + ((size_t)rr * a.H + j) * D + pc * 8);
+      rD[it] = IO<TI>::load8(dop + ((size_t)rr * a.HV + h) * D + pc * 8);
+      // the scale exp(gcum) rq of the row is applied to Q when staged (zero past the end)
+      rqs[it] = row <= last ? a.gcum[(size_t)rr * a.HV + h] : -INFINITY;
+      rqs[it] = __expf(rqs[it]) * a.rq[(size_t)rr * a.H + j];
     }
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      na[k2] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(nt0 + rr) * a.HV + h) * CH + k2 * 32 + lg * 8);
-      np[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + ar * CH + k2 * 32 + lg * 8);
+    for (int it = 0; it < 2; ++it) {
+      const int p = tid + NTHREADS * it, row = p >> 3, pc = p & 7;
+      rA[it] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + min(row, last)) * a.HV + h) * CH + pc * 8);
+      rP[it] = *reinterpret_cast<const bf16x8*>(pm + ((size_t)c * a.HV + h) * CH * CH + row * CH + pc * 8);
     }
-    if (tid < CH * VPR) {
-      const int r = min(tid / VPR, nlen - 1), pc = tid % VPR;
-      ndo = IO<TI>::load8(dop + ((size_t)(nt0 + r) * a.HV + h) * D + col0 + pc * 8);
-      // scale of row r in Qh^T diag(b) dO: exp(gcum) * rq (applied when staged)
-      nsc = a.gcum[(size_t)(nt0 + r) * a.HV + h];
-      nrq = a.rq[(size_t)(nt0 + r) * a.H + j];
+    const int which = min(tid >> 6, 2), row = t0 + min(lane, last);
+    const float* src = which == 0   ? a.gcum + (size_t)row * a.HV + h
+                       : which == 1 ? a.beta + (size_t)row * a.HV + h
+                                    : a.rk + (size_t)row * a.H + j;
+    rS = *src;
+  };
+  auto store_chunk = [&](int b, int c) {
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int len = min(CH, doc_t1 - t0);
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + NTHREADS * it, row = p / RP, pc = p % RP;
+      *reinterpret_cast<bf16x8*>(&sm.sK[b][row * SK + pc * 8]) = rK[it];
+      *reinterpret_cast<bf16x8*>(&sm.sQ[b][row * SK + pc * 8]) = scale8(rQ[it], rqs[it]);
+      *reinterpret_cast<bf16x8*>(&sm.sdO[b][row * SK + pc * 8]) = rD[it];
     }
-    if (tid < CH) {
-      const int r = min(tid, nlen - 1);
-      ng = a.gcum[(size_t)(nt0 + r) * a.HV + h];
-      nb = a.beta[(size_t)(nt0 + r) * a.HV + h];
-      nrk = a.rk[(size_t)(nt0 + r) * a.H + j];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int p = tid + NTHREADS * it, row = p >> 3, pc = p & 7;
+      *reinterpret_cast<bf16x8*>(&sm.sA[b][row * SA + pc * 8]) = rA[it];
+      *reinterpret_cast<bf16x8*>(&sm.sPT[b][row * SA + pc * 8]) = rP[it];
     }
-    ngam = a.gamma[(size_t)c * a.HV + h];
+    if (tid < 3 * CH) sm.sc[b][tid >> 6][lane] = lane < len ? rS : 0.f;
   };
 
-  f32x4 dS[NRT][NCT];
+  f32x4 dS[NRT][NCW];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int d = 16 * (w * NRT + rt) + lg * 4 + i, cc = col0 + 16 * ct + lr;
+        const int d = 16 * rt + 4 * lg + i, cc = v0 + 16 * ct + lr;
         dS[rt][ct][i] = a.dht ? a.dht[(((size_t)n * a.HV + h) * D + d) * D + cc] : 0.f;
       }
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      lds_store4_t(sm.sdST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, dS[rt][ct][0], dS[rt][ct][1],
-                   dS[rt][ct][2], dS[rt][ct][3]);
-  if (c_begin < c_end) prefetch(c_end - 1);
 
-  for (int c = c_end - 1; c >= c_begin; --c) {
-    const int len = nlen;
-    const float gam = ngam;
-    // K, Q and A rows past the chunk's end hold copies of its last row: finite, and their
-    // contributions vanish (rk, beta and the dO scale are zero there, P^T is masked)
-    bf16x8 fk[KS], fpt[2];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      fk[ks] = nk[ks];
-      *reinterpret_cast<bf16x8*>(sm.sK + ar * SK + ks * 32 + lg * 8) = nk[ks];
-      *reinterpret_cast<bf16x8*>(sm.sQ + ar * SK + ks * 32 + lg * 8) = nq[ks];
-    }
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      fpt[k2] = np[k2];
-      *reinterpret_cast<bf16x8*>(sm.sA + ar * SA + k2 * 32 + lg * 8) = na[k2];
-    }
-    if (tid < CH * VPR) {
-      const int r = tid / VPR, pc = tid % VPR;
-      const bool rok = r < len;
-      const bf16x8 dov = rok ? ndo : zero8();
-      *reinterpret_cast<bf16x8*>(sm.sdO + r * SDO + pc * 8) = dov;
-      const float scl = rok ? __expf(nsc) * nrq : 0.f;
-      bf16x8 sc;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sc[e] = (bf16)(scl * (float)dov[e]);
-      *reinterpret_cast<bf16x8*>(sm.sdOp + r * SDO + pc * 8) = sc;
-    }
-    if (tid < CH) {
-      const bool rok = tid < len;
-      sm.sG[tid] = rok ? ng : 0.f;
-      sm.sB[tid] = rok ? nb : 0.f;
-      sm.srk[tid] = rok ? nrk : 0.f;
-    }
-    if (c - 1 >= c_begin) prefetch(c - 1);
-    __syncthreads();
+  auto step = [&](int b, int c) {
+    const bf16* Kt = sm.sK[b];
+    const bf16* Qt = sm.sQ[b];
+    const bf16* Dt = sm.sdO[b];
+    const bf16* At = sm.sA[b];
+    const bf16* PTt = sm.sPT[b];
+    const float* Gs = sm.sc[b][0];
+    const float* Bs = sm.sc[b][1];
+    const float* Ks = sm.sc[b][2];
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int len = min(CH, doc_t1 - t0);
+    const float glast = Gs[len - 1];
+    const float gam = __expf(glast);
 
+    bf16x8 sb[KD][NCW];
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) sb[kd][ct] = c_to_b(dS[2 * kd][ct], dS[2 * kd + 1][ct]);
     {
-      bf16* tp = reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D + (size_t)col0 * D;
-      for (int idx = tid; idx < DVT * (D / 8); idx += NTHREADS) {
-        const int cc = idx / (D / 8), pc = idx % (D / 8);
-        *reinterpret_cast<bf16x8*>(tp + (size_t)cc * D + pc * 8) = lds8(sm.sdST, SST, cc, pc * 8);
-      }
-    }
-    const float glast = sm.sG[len - 1];
-    float dec[4], ybr[4];
+      bf16* tp = reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + lg * 4 + i;
-      dec[i] = __expf(glast - sm.sG[r]) * sm.srk[r];
-      ybr[i] = sm.sB[r] * __expf(sm.sG[r]) * sm.srk[r];
-    }
+      for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 kd = zero4(), pd = zero4();
+        for (int ct = 0; ct < NCW; ++ct) {
+          bf16x4 v;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kd = mfma(fk[ks], lds8(sm.sdST, SST, 16 * ct + lr, ks * 32 + lg * 8), kd);
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) pd = mfma(fpt[k2], lds_tr8(sm.sdO, SDO, k2 * 32, 16 * ct), pd);
-      lds_store4_t(sm.sdRT, STK, 16 * ct + lr, 16 * w + lg * 4, pd[0] + dec[0] * kd[0], pd[1] + dec[1] * kd[1],
-                   pd[2] + dec[2] * kd[2], pd[3] + dec[3] * kd[3]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 y = zero4();
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-        y = mfma(lds_tr8(sm.sA, SA, k2 * 32, 16 * w), lds8(sm.sdRT, STK, 16 * ct + lr, k2 * 32 + lg * 8), y);
-      lds_store4_t(sm.sYT, STK, 16 * ct + lr, 16 * w + lg * 4, ybr[0] * y[0], ybr[1] * y[1], ybr[2] * y[2],
-                   ybr[3] * y[3]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 a1 = zero4(), a2 = zero4();
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          a1 = mfma(lds_tr8(sm.sQ, SK, k2 * 32, 16 * (w * NRT + rt)), lds_tr8(sm.sdOp, SDO, k2 * 32, 16 * ct), a1);
-          a2 = mfma(lds_tr8(sm.sK, SK, k2 * 32, 16 * (w * NRT + rt)), lds8(sm.sYT, STK, 16 * ct + lr, k2 * 32 + lg * 8),
-                    a2);
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)dS[rt][ct][i];
+          *reinterpret_cast<bf16x4*>(tp + (size_t)(v0 + 16 * ct + lr) * D + 16 * rt + 4 * lg) = v;
         }
+    }
+    // dO as B operands (k = tokens), shared by P^T dO and (Q')^T dO
+    bf16x8 db[2][NCW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dS[rt][ct][i] = __builtin_fmaf(gam, dS[rt][ct][i], a1[i] - a2[i]);
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) db[kt][ct] = lds_tr8(Dt, SK, 32 * kt, v0 + 16 * ct);
+    // dR = P^T dO + diag(exp(G_last - G) rk) K dS
+    f32x4 dR[4][NCW];
+    float ybr[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 kd_[NCW], pd[NCW];
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) kd_[ct] = pd[ct] = zero4();
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) {
+        const bf16x8 ak = lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) kd_[ct] = mfma(ak, sb[kd][ct], kd_[ct]);
       }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 ap = lds8(PTt, SA, 16 * mt + lr, 32 * kt + 8 * lg);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) pd[ct] = mfma(ap, db[kt][ct], pd[ct]);
+      }
+      const int r0 = 16 * mt + 4 * lg;
+      const float4 g4 = *reinterpret_cast<const float4*>(Gs + r0);
+      const float4 b4 = *reinterpret_cast<const float4*>(Bs + r0);
+      const float4 k4 = *reinterpret_cast<const float4*>(Ks + r0);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w}, bb[4] = {b4.x, b4.y, b4.z, b4.w};
+      const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float dec = __expf(glast - gg[i]) * kk[i];
+        ybr[mt][i] = bb[i] * __expf(gg[i]) * kk[i];
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) dR[mt][ct][i] = pd[ct][i] + dec * kd_[ct][i];
+      }
+    }
+    bf16x8 drb[2][NCW];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) drb[kt][ct] = c_to_b(dR[2 * kt][ct], dR[2 * kt + 1][ct]);
+    // Y' = diag(beta b rk) A^T dR
+    f32x4 Y[4][NCW];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) Y[mt][ct] = zero4();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 aat = lds_tr8(At, SA, 32 * kt, 16 * mt);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) Y[mt][ct] = mfma(aat, drb[kt][ct], Y[mt][ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[mt][ct][i] *= ybr[mt][i];
+    }
+    bf16x8 yb[2][NCW];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) yb[kt][ct] = c_to_b(Y[2 * kt][ct], Y[2 * kt + 1][ct]);
+    // dS <- gamma dS + (Q')^T dO - K^T Y'
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x4 a1[NCW], a2[NCW];
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) a1[ct] = a2[ct] = zero4();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 aq = lds_tr8(Qt, SK, 32 * kt, 16 * rt);
+        const bf16x8 ak = lds_tr8(Kt, SK, 32 * kt, 16 * rt);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) {
+          a1[ct] = mfma(aq, db[kt][ct], a1[ct]);
+          a2[ct] = mfma(ak, yb[kt][ct], a2[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS[rt][ct][i] = __builtin_fmaf(gam, dS[rt][ct][i], a1[ct][i] - a2[ct][i]);
+    }
+  };
+
+  if (c_begin < c_end) {
+    load_chunk(c_end - 1);
+    store_chunk(0, c_end - 1);
+  }
+  __syncthreads();
+  for (int c = c_end - 1; c >= c_begin; --c) {
+    const int b = (c_end - 1 - c) & 1;
+    const bool more = c - 1 >= c_begin;
+    if (more) load_chunk(c - 1);
+    step(b, c);
+    if (more) store_chunk(b ^ 1, c - 1);
     __syncthreads();
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        lds_store4_t(sm.sdST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, dS[rt][ct][0], dS[rt][ct][1],
-                     dS[rt][ct][2], dS[rt][ct][3]);
   }
   if (a.dh0) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int d = 16 * (w * NRT + rt) + lg * 4 + i, cc = col0 + 16 * ct + lr;
+          const int d = 16 * rt + 4 * lg + i, cc = v0 + 16 * ct + lr;
           a.dh0[(((size_t)n * a.HV + h) * D + d) * D + cc] = dS[rt][ct][i];
         }
   }
@@ -357,8 +396,8 @@ __global__ __launch_bounds__(NTHREADS) void k_walk_bwd(Args a) {
 
 template <int D, typename TI>
 static int walk_bwd_t(const Args& a, hipStream_t s) {
-  const dim3 grid(chain_blocks(a, D / BWALK_DVT));
-  hipLaunchKernelGGL((k_walk_bwd<D, BWALK_DVT, TI>), grid, dim3(NTHREADS), 0, s, a);
+  const dim3 grid(chain_blocks(a, 1));
+  hipLaunchKernelGGL((k_walk_bwd<D, TI>), grid, dim3(NTHREADS), 0, s, a);
   return (int)hipGetLastError();
 }
 
@@ -413,11 +452,6 @@ struct GradSmem {
   } u;
 };
 
-__device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (bf16)(s * (float)v[e]);
-  return v;
-}
 
 template <int D, typename TI, bool DET>
 __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {

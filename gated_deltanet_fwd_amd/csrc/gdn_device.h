@@ -57,6 +57,48 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* tile, int stride, int k0, 
   return r;
 }
 
+// C-layout read of a 16x16 block of a row-major LDS tile: lane l receives
+// tile[r0 + (l/16)*4 + i][c0 + l%16] for i = 0..3 (the layout of an MFMA result tile), with one
+// transpose-read per lane.
+__device__ __forceinline__ bf16x4 lds_tr4c(const bf16* tile, int stride, int r0, int c0) {
+  const int l = threadIdx.x & 63;
+  const int g = l >> 4, j = l & 15;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)(tile + (r0 + 4 * g + (j >> 2)) * stride + c0 + 4 * (j & 3)));
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// MFMA B operand (32 rows of k, 16 columns) from the two 16x16 result tiles that hold rows
+// [0, 16) and [16, 32) of that k range, without LDS. A result tile gives lane l rows
+// (l/16)*4 .. +3; the B operand wants rows (l/16)*8 .. +7. With the four 16-lane groups of t0 and
+// t1 written G0..G3, permlane32_swap(t0, t1) yields (t0.G0 t0.G1 t1.G0 t1.G1 | t0.G2 t0.G3 t1.G2
+// t1.G3) and permlane16_swap of those yields (t0.G0 t0.G2 t1.G0 t1.G2 | t0.G1 t0.G3 t1.G1 t1.G3):
+// the low and high 4-row halves of every group's 8 rows (swap semantics checked on gfx950 by a
+// lane probe).
+__device__ __forceinline__ bf16x8 c_to_b(const f32x4& t0, const f32x4& t1) {
+  const unsigned a0 = pack_bf16x2(t0[0], t0[1]), a1 = pack_bf16x2(t0[2], t0[3]);
+  const unsigned b0 = pack_bf16x2(t1[0], t1[1]), b1 = pack_bf16x2(t1[2], t1[3]);
+  const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+  const auto u0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+  const auto u1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 r;
+  r[0] = u0[0];
+  r[1] = u1[0];
+  r[2] = u0[1];
+  r[3] = u1[1];
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // Store 4 values of one column, rows r..r+3, into an LDS tile stored transposed
 // (tile[col][row]): one 8-byte write.
 __device__ __forceinline__ void lds_store4_t(bf16* base, int stride, int col, int row, float a, float b, float c,

@@ -286,250 +286,303 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// State walk, one workgroup per (document, value head, value tile of DVT columns).
+// State walk, one workgroup per (document, value head); chunks in order.
 // WRITE_O: write o (and ht). WRITE_TAPE: write the chunk-start state tape (bf16, transposed).
 // FULL: also write v_new = R.
 //
-// The next chunk's inputs are loaded into registers while the current chunk computes, so the
-// serial chain per chunk is LDS + MFMA only. K is staged row-major in LDS; its transpose for the
-// state update comes from transpose-reads.
-template <int D, int DVT>
+// Wave w owns value columns [16*NCW*w, 16*NCW*(w+1)) of the state and keeps them, and every
+// per-chunk intermediate (K S, X, R, the output), in registers: results of one MFMA become B
+// operands of the next through c_to_b, and the state itself is the B operand of K S and Q S. The
+// waves never exchange data; LDS holds only the chunk's shared inputs (K, Q, V, A, P and the
+// per-token scalars), double-buffered, so the next chunk is staged while this one computes and
+// there is one barrier per chunk.
+template <int D, bool WRITE_O>
 struct WalkSmem {
-  static constexpr int SK = D + 16;   // row stride of K (conflict-free transpose-reads)
-  static constexpr int SST = D + PAD; // row stride of S^T
-  static constexpr int STK = CH + PAD;
-  static constexpr int SV = DVT + PAD;
-  bf16 sK[CH * SK];
-  bf16 sST[DVT * SST];
-  bf16 sXT[DVT * STK];
-  bf16 sRT[DVT * STK];
-  bf16 sRdT[DVT * STK];
-  bf16 sV[CH * SV];
-  float sG[CH], sB[CH], srk[CH], srq[CH];
+  static constexpr int SK = D + 16; // token rows of K, Q, V (conflict-free transpose-reads)
+  static constexpr int SA = CH + 16;
+  static constexpr int NQ = WRITE_O ? 2 : 1;
+  static constexpr int LQ = WRITE_O ? CH * SK : 8;
+  static constexpr int LP = WRITE_O ? CH * SA : 8;
+  bf16 sK[2][CH * SK];
+  bf16 sV[2][CH * SK];
+  bf16 sA[2][CH * SA];
+  bf16 sQ[NQ][LQ];
+  bf16 sP[NQ][LP];
+  float sc[2][4][CH]; // gcum, beta, rk, rq (zero past the chunk's end)
 };
 
-// Inputs of one chunk, loaded into registers one chunk ahead of use.
-template <int KS>
-struct WalkPrefetch {
-  bf16x8 k[KS], q[KS], a[2], p[2], v;
-  float g, b, rk, rq, gam;
-  int len, t0;
-};
-
-template <int D, int DVT, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL>
-__global__ __launch_bounds__(NTHREADS) void k_walk_fwd(Args a) {
+template <int D, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL>
+__global__ __launch_bounds__(NTHREADS, 1) void k_walk_fwd(Args a) {
   if (a.status[0]) return;
-  constexpr int NTILE = D / DVT;
-  const ChainMap cm = decode_chain(blockIdx.x, a.N, a.H, a.G, NTILE);
+  const ChainMap cm = decode_chain(blockIdx.x, a.N, a.H, a.G, 1);
   if (!cm.valid) return;
   const int n = a.seq_order[cm.rank];
-  const int j = cm.j, h = j * a.G + cm.gi, col0 = cm.tile * DVT;
+  const int j = cm.j, h = j * a.G + cm.gi;
   const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  constexpr int NCT = DVT / 16; // value-column tiles
-  constexpr int NRT = D / 64;   // state row tiles per wave
-  constexpr int KS = D / 32;    // k-steps over the key dim
-  using SM = WalkSmem<D, DVT>;
-  constexpr int SK = SM::SK, SST = SM::SST, STK = SM::STK, SV = SM::SV;
-  constexpr int VPR = DVT / 8; // 16-byte pieces per row of the value tile
+  constexpr int NRT = D / 16; // state row tiles (key dim)
+  constexpr int NCW = D / 64; // 16-column tiles per wave
+  constexpr int KD = D / 32;  // k-steps over the key dim
+  constexpr int PPT = D / 32; // 16-byte pieces per thread of a 64 x D token tile
+  constexpr int RP = D / 8;   // pieces per row
+  using SM = WalkSmem<D, WRITE_O>;
+  constexpr int SK = SM::SK, SA = SM::SA;
   __shared__ __attribute__((aligned(16))) SM sm;
   const TI* kp = (const TI*)a.k;
   const TI* qp = (const TI*)a.q;
   const TI* vp = (const TI*)a.v;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
-  const bf16* qkp = reinterpret_cast<const bf16*>(a.qk);
-  const int ar = 16 * w + lr; // this lane's A-fragment row (token in the chunk)
-  // chunk c of the document starts at token cu[n] + 64 (c - c_begin): no table lookup on the
-  // serial path
+  const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
+  const int v0 = 16 * NCW * w;
+  // chunk c of the document starts at token cu[n] + 64 (c - c_begin)
   const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
-  using PF = WalkPrefetch<KS>;
 
-  // Unconditional loads from rows clamped into the chunk; rows past its end are zeroed when the
-  // data is consumed, so nothing waits on a load before its use one chunk later.
-  auto prefetch = [&](PF& P, int c) {
-    P.t0 = doc_t0 + (c - c_begin) * CH;
-    P.len = min(CH, doc_t1 - P.t0);
-    const int rr = min(ar, P.len - 1);
+  // ---- staging: global -> registers (issued before a chunk's compute) -> LDS (after it).
+  // Rows past the chunk's end re-read its last row: finite values whose contributions vanish
+  // because beta and rk are zero there and P is masked.
+  bf16x8 rK[PPT], rV[PPT], rQ[PPT], rA[2], rP[2];
+  float rS;
+  auto load_chunk = [&](int c) {
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int last = min(CH, doc_t1 - t0) - 1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      P.k[ks] = IO<TI>::load8(kp + ((size_t)(P.t0 + rr) * a.H + j) * D + ks * 32 + lg * 8);
-      if (WRITE_O) P.q[ks] = IO<TI>::load8(qp + ((size_t)(P.t0 + rr) * a.H + j) * D + ks * 32 + lg * 8);
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + NTHREADS * it, row = min(p / RP, last), pc = p % RP;
+      rK[it] = IO<TI>::load8(kp + ((size_t)(t0 + row) * a.H + j) * D + pc * 8);
+      rV[it] = IO<TI>::load8(vp + ((size_t)(t0 + row) * a.HV + h) * D + pc * 8);
+      if (WRITE_O) rQ[it] = IO<TI>::load8(qp + ((size_t)(t0 + row) * a.H + j) * D + pc * 8);
     }
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      P.a[k2] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(P.t0 + rr) * a.HV + h) * CH + k2 * 32 + lg * 8);
-      if (WRITE_O)
-        P.p[k2] = *reinterpret_cast<const bf16x8*>(qkp + ((size_t)c * a.HV + h) * CH * CH + ar * CH + k2 * 32 + lg * 8);
+    for (int it = 0; it < 2; ++it) {
+      const int p = tid + NTHREADS * it, row = p >> 3, pc = p & 7;
+      rA[it] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + min(row, last)) * a.HV + h) * CH + pc * 8);
+      if (WRITE_O) rP[it] = *reinterpret_cast<const bf16x8*>(pm + ((size_t)c * a.HV + h) * CH * CH + row * CH + pc * 8);
     }
-    // every thread loads (threads past the tile re-read a valid row), so no load sits in a
-    // divergent branch and the wait counts before each use stay exact
-    {
-      const int r = min((tid / VPR) % CH, P.len - 1), pc = tid % VPR;
-      P.v = IO<TI>::load8(vp + ((size_t)(P.t0 + r) * a.HV + h) * D + col0 + pc * 8);
+    const int which = tid >> 6, row = t0 + min(lane, last);
+    const float* src = which == 0   ? a.gcum + (size_t)row * a.HV + h
+                       : which == 1 ? a.beta + (size_t)row * a.HV + h
+                       : which == 2 ? a.rk + (size_t)row * a.H + j
+                                    : a.rq + (size_t)row * a.H + j;
+    rS = *src;
+  };
+  auto store_chunk = [&](int b, int c) {
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int len = min(CH, doc_t1 - t0);
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + NTHREADS * it, row = p / RP, pc = p % RP;
+      *reinterpret_cast<bf16x8*>(&sm.sK[b][row * SK + pc * 8]) = rK[it];
+      *reinterpret_cast<bf16x8*>(&sm.sV[b][row * SK + pc * 8]) = rV[it];
+      if (WRITE_O) *reinterpret_cast<bf16x8*>(&sm.sQ[b][row * SK + pc * 8]) = rQ[it];
     }
-    {
-      const int r = min(tid % CH, P.len - 1);
-      P.g = a.gcum[(size_t)(P.t0 + r) * a.HV + h];
-      P.b = a.beta[(size_t)(P.t0 + r) * a.HV + h];
-      P.rk = a.rk[(size_t)(P.t0 + r) * a.H + j];
-      P.rq = a.rq[(size_t)(P.t0 + r) * a.H + j];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int p = tid + NTHREADS * it, row = p >> 3, pc = p & 7;
+      *reinterpret_cast<bf16x8*>(&sm.sA[b][row * SA + pc * 8]) = rA[it];
+      if (WRITE_O) *reinterpret_cast<bf16x8*>(&sm.sP[b][row * SA + pc * 8]) = rP[it];
     }
-    P.gam = a.gamma[(size_t)c * a.HV + h];
+    sm.sc[b][tid >> 6][lane] = lane < len ? rS : 0.f;
   };
 
-  f32x4 S[NRT][NCT];
+  // ---- state: rows 16 rt + 4 lg + i (key), columns v0 + 16 ct + lr (value)
+  f32x4 S[NRT][NCW];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int d = 16 * (w * NRT + rt) + lg * 4 + i, cc = col0 + 16 * ct + lr;
+        const int d = 16 * rt + 4 * lg + i, cc = v0 + 16 * ct + lr;
         S[rt][ct][i] = a.has_h0 ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + cc] : 0.f;
       }
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      lds_store4_t(sm.sST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, S[rt][ct][0], S[rt][ct][1],
-                   S[rt][ct][2], S[rt][ct][3]);
 
-  // one chunk: stage P into LDS, start loading chunk `cn` into Q, then the chunk's products and
-  // the state update
-  auto step = [&](const PF& P, int c, PF& Q, int cn) {
-    const int len = P.len, t0 = P.t0;
-    const float gam = P.gam;
-    // K, Q, A and V rows past the chunk's end hold copies of its last row: they stay finite and
-    // their contributions vanish because beta and rk are zero there and P is masked
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<bf16x8*>(sm.sK + ar * SK + ks * 32 + lg * 8) = P.k[ks];
-    if (tid < CH * VPR) *reinterpret_cast<bf16x8*>(sm.sV + (tid / VPR) * SV + (tid % VPR) * 8) = P.v;
-    if (tid < CH) {
-      const bool rok = tid < len;
-      sm.sG[tid] = rok ? P.g : 0.f;
-      sm.sB[tid] = rok ? P.b : 0.f;
-      sm.srk[tid] = rok ? P.rk : 0.f;
-      sm.srq[tid] = rok ? P.rq : 0.f;
-    }
-    if (cn < c_end) prefetch(Q, cn);
-    __syncthreads();
+  auto step = [&](int b, int c) {
+    const bf16* Kt = sm.sK[b];
+    const bf16* Vt = sm.sV[b];
+    const bf16* At = sm.sA[b];
+    const bf16* Qt = sm.sQ[WRITE_O ? b : 0];
+    const bf16* Pt = sm.sP[WRITE_O ? b : 0];
+    const float* Gs = sm.sc[b][0];
+    const float* Bs = sm.sc[b][1];
+    const float* Ks = sm.sc[b][2];
+    const float* Qs = sm.sc[b][3];
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int len = min(CH, doc_t1 - t0);
+    const float glast = Gs[len - 1];
+    const float gam = __expf(glast);
 
+    // the state as bf16 B operands (k = key dim)
+    bf16x8 sb[KD][NCW];
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) sb[kd][ct] = c_to_b(S[2 * kd][ct], S[2 * kd + 1][ct]);
     if (WRITE_TAPE) {
-      bf16* tp = reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D + (size_t)col0 * D;
-      for (int idx = tid; idx < DVT * (D / 8); idx += NTHREADS) {
-        const int cc = idx / (D / 8), pc = idx % (D / 8);
-        *reinterpret_cast<bf16x8*>(tp + (size_t)cc * D + pc * 8) = lds8(sm.sST, SST, cc, pc * 8);
-      }
+      bf16* tp = reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) {
+          bf16x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)S[rt][ct][i];
+          *reinterpret_cast<bf16x4*>(tp + (size_t)(v0 + 16 * ct + lr) * D + 16 * rt + 4 * lg) = v;
+        }
     }
-    f32x4 ksv[NCT], qsv[NCT];
+    // K S and Q S: 64 tokens x this wave's columns
+    f32x4 ks[4][NCW], qs[4][NCW];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) ksv[ct] = qsv[ct] = zero4();
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
+      for (int ct = 0; ct < NCW; ++ct) ks[mt][ct] = qs[mt][ct] = zero4();
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const bf16x8 bS = lds8(sm.sST, SST, 16 * ct + lr, kk * 32 + lg * 8);
-        ksv[ct] = mfma(P.k[kk], bS, ksv[ct]);
-        if (WRITE_O) qsv[ct] = mfma(P.q[kk], bS, qsv[ct]);
+    for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 ak = lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
+        bf16x8 aq;
+        if (WRITE_O) aq = lds8(Qt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) {
+          ks[mt][ct] = mfma(ak, sb[kd][ct], ks[mt][ct]);
+          if (WRITE_O) qs[mt][ct] = mfma(aq, sb[kd][ct], qs[mt][ct]);
+        }
       }
-    const int r0 = 16 * w + lg * 4;
-    const float4 g4 = *reinterpret_cast<const float4*>(&sm.sG[r0]);
-    const float4 b4 = *reinterpret_cast<const float4*>(&sm.sB[r0]);
-    const float4 k4 = *reinterpret_cast<const float4*>(&sm.srk[r0]);
-    const float4 q4 = *reinterpret_cast<const float4*>(&sm.srq[r0]);
-    const float grow[4] = {g4.x, g4.y, g4.z, g4.w}, brw[4] = {b4.x, b4.y, b4.z, b4.w};
-    const float rkw[4] = {k4.x, k4.y, k4.z, k4.w}, rqw[4] = {q4.x, q4.y, q4.z, q4.w};
-    float brow[4], krow[4];
+    // X = diag(beta) (V - diag(b rk) K S); per-row factors of this lane's rows
+    f32x4 X[4][NCW];
+    float brow[4][4], rqrow[4][4], decr[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      brow[i] = __expf(grow[i]);
-      krow[i] = brow[i] * rkw[i];
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      float x[4];
+    for (int mt = 0; mt < 4; ++mt) {
+      const int r0 = 16 * mt + 4 * lg;
+      const float4 g4 = *reinterpret_cast<const float4*>(Gs + r0);
+      const float4 b4 = *reinterpret_cast<const float4*>(Bs + r0);
+      const float4 k4 = *reinterpret_cast<const float4*>(Ks + r0);
+      const float4 q4 = *reinterpret_cast<const float4*>(Qs + r0);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w}, bb[4] = {b4.x, b4.y, b4.z, b4.w};
+      const float kk[4] = {k4.x, k4.y, k4.z, k4.w}, qq[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float vv = (float)sm.sV[(r0 + i) * SV + 16 * ct + lr];
-        x[i] = brw[i] * (vv - krow[i] * ksv[ct][i]);
+        brow[mt][i] = __expf(gg[i]);
+        rqrow[mt][i] = qq[i];
+        decr[mt][i] = __expf(glast - gg[i]) * kk[i];
       }
-      lds_store4_t(sm.sXT, STK, 16 * ct + lr, r0, x[0], x[1], x[2], x[3]);
-    }
-    __syncthreads();
-
-    const float glast = sm.sG[len - 1];
-    float dec[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dec[i] = __expf(glast - grow[i]) * rkw[i];
+      for (int ct = 0; ct < NCW; ++ct) {
+        const bf16x4 vv = lds_tr4c(Vt, SK, 16 * mt, v0 + 16 * ct);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 R = zero4();
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) R = mfma(P.a[k2], lds8(sm.sXT, STK, 16 * ct + lr, k2 * 32 + lg * 8), R);
-      if (FULL) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r0 + i < len)
-            reinterpret_cast<bf16*>(a.vnew)[((size_t)(t0 + r0 + i) * a.HV + h) * D + col0 + 16 * ct + lr] = (bf16)R[i];
+        for (int i = 0; i < 4; ++i) X[mt][ct][i] = bb[i] * ((float)vv[i] - brow[mt][i] * kk[i] * ks[mt][ct][i]);
       }
-      lds_store4_t(sm.sRT, STK, 16 * ct + lr, r0, R[0], R[1], R[2], R[3]);
-      lds_store4_t(sm.sRdT, STK, 16 * ct + lr, r0, dec[0] * R[0], dec[1] * R[1], dec[2] * R[2], dec[3] * R[3]);
     }
-    __syncthreads();
-
+    bf16x8 xb[2][NCW];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) xb[kt][ct] = c_to_b(X[2 * kt][ct], X[2 * kt + 1][ct]);
+    // R = A X
+    f32x4 R[4][NCW];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) R[mt][ct] = zero4();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 aa = lds8(At, SA, 16 * mt + lr, 32 * kt + 8 * lg);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) R[mt][ct] = mfma(aa, xb[kt][ct], R[mt][ct]);
+      }
+    }
+    if (FULL) {
+      bf16* vn = reinterpret_cast<bf16*>(a.vnew);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mt + 4 * lg + i;
+            if (r < len) vn[((size_t)(t0 + r) * a.HV + h) * D + v0 + 16 * ct + lr] = (bf16)R[mt][ct][i];
+          }
+    }
+    // B operands of R (for P R) and of diag(exp(G_last - G) rk) R (for the state update)
+    bf16x8 rb[2][NCW], rdb[2][NCW];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        if (WRITE_O) rb[kt][ct] = c_to_b(R[2 * kt][ct], R[2 * kt + 1][ct]);
+        f32x4 d0, d1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          d0[i] = decr[2 * kt][i] * R[2 * kt][ct][i];
+          d1[i] = decr[2 * kt + 1][i] * R[2 * kt + 1][ct][i];
+        }
+        rdb[kt][ct] = c_to_b(d0, d1);
+      }
+    // O = diag(b rq) Q S + P R
     if (WRITE_O) {
       TI* op = (TI*)a.o;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 acc = zero4();
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 acc[NCW];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(P.p[k2], lds8(sm.sRT, STK, 16 * ct + lr, k2 * 32 + lg * 8), acc);
-        float ov[4];
+        for (int ct = 0; ct < NCW; ++ct) acc[ct] = zero4();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = brow[i] * rqw[i] * qsv[ct][i] + acc[i];
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 ap = lds8(Pt, SA, 16 * mt + lr, 32 * kt + 8 * lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r0 + i < len) IO<TI>::store1(op + ((size_t)(t0 + r0 + i) * a.HV + h) * D + col0 + 16 * ct + lr, ov[i]);
+          for (int ct = 0; ct < NCW; ++ct) acc[ct] = mfma(ap, rb[kt][ct], acc[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mt + 4 * lg + i;
+            const float ov = brow[mt][i] * rqrow[mt][i] * qs[mt][ct][i] + acc[ct][i];
+            if (r < len) IO<TI>::store1(op + ((size_t)(t0 + r) * a.HV + h) * D + v0 + 16 * ct + lr, ov);
+          }
       }
     }
+    // S <- gamma S + K^T diag(exp(G_last - G) rk) R
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x4 acc[NCW];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 acc = zero4();
+      for (int ct = 0; ct < NCW; ++ct) acc[ct] = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          acc = mfma(lds_tr8(sm.sK, SK, k2 * 32, 16 * (w * NRT + rt)),
-                     lds8(sm.sRdT, STK, 16 * ct + lr, k2 * 32 + lg * 8), acc);
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 akt = lds_tr8(Kt, SK, 32 * kt, 16 * rt);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[rt][ct][i] = __builtin_fmaf(gam, S[rt][ct][i], acc[i]);
+        for (int ct = 0; ct < NCW; ++ct) acc[ct] = mfma(akt, rdb[kt][ct], acc[ct]);
       }
-    __syncthreads();
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+      for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        lds_store4_t(sm.sST, SST, 16 * ct + lr, 16 * (w * NRT + rt) + lg * 4, S[rt][ct][0], S[rt][ct][1],
-                     S[rt][ct][2], S[rt][ct][3]);
+        for (int i = 0; i < 4; ++i) S[rt][ct][i] = __builtin_fmaf(gam, S[rt][ct][i], acc[ct][i]);
+    }
   };
 
-  // two register sets, alternating: the loads for chunk c+1 fly while chunk c computes
-  PF pa, pb;
-  if (c_begin < c_end) prefetch(pa, c_begin);
-  for (int c = c_begin; c < c_end; c += 2) {
-    step(pa, c, pb, c + 1);
-    if (c + 1 >= c_end) break;
-    step(pb, c + 1, pa, c + 2);
+  if (c_begin < c_end) {
+    load_chunk(c_begin);
+    store_chunk(0, c_begin);
+  }
+  __syncthreads();
+  for (int c = c_begin; c < c_end; ++c) {
+    const int b = (c - c_begin) & 1;
+    const bool more = c + 1 < c_end;
+    if (more) load_chunk(c + 1);
+    step(b, c);
+    if (more) store_chunk(b ^ 1, c + 1);
+    __syncthreads();
   }
   if (WRITE_O && a.want_ht) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int d = 16 * (w * NRT + rt) + lg * 4 + i, cc = col0 + 16 * ct + lr;
+          const int d = 16 * rt + 4 * lg + i, cc = v0 + 16 * ct + lr;
           a.ht[(((size_t)n * a.HV + h) * D + d) * D + cc] = S[rt][ct][i];
         }
   }
@@ -565,23 +618,21 @@ int launch_intra(const Args& a, int bwd_prep, void* stream) {
 // (one per XCD), times the G value heads and the value tiles of each group.
 int chain_blocks(const Args& a, int ntile) { return ((a.N * a.H + 7) / 8) * 8 * a.G * ntile; }
 
-template <int D, int DVT, typename TI>
+template <int D, typename TI>
 static int walk_t(const Args& a, int write_o, int write_tape, hipStream_t s) {
-  const dim3 grid(chain_blocks(a, D / DVT)), blk(NTHREADS);
-  if (write_o && !write_tape) hipLaunchKernelGGL((k_walk_fwd<D, DVT, TI, true, false, false>), grid, blk, 0, s, a);
-  else if (write_o) hipLaunchKernelGGL((k_walk_fwd<D, DVT, TI, true, true, true>), grid, blk, 0, s, a);
-  else if (a.full) hipLaunchKernelGGL((k_walk_fwd<D, DVT, TI, false, true, true>), grid, blk, 0, s, a);
-  else hipLaunchKernelGGL((k_walk_fwd<D, DVT, TI, false, true, false>), grid, blk, 0, s, a);
+  const dim3 grid(chain_blocks(a, 1)), blk(NTHREADS);
+  if (write_o && !write_tape) hipLaunchKernelGGL((k_walk_fwd<D, TI, true, false, false>), grid, blk, 0, s, a);
+  else if (write_o) hipLaunchKernelGGL((k_walk_fwd<D, TI, true, true, true>), grid, blk, 0, s, a);
+  else if (a.full) hipLaunchKernelGGL((k_walk_fwd<D, TI, false, true, true>), grid, blk, 0, s, a);
+  else hipLaunchKernelGGL((k_walk_fwd<D, TI, false, true, false>), grid, blk, 0, s, a);
   return (int)hipGetLastError();
 }
 
 int launch_walk_fwd(const Args& a, int write_o, int write_tape, void* stream) {
   const hipStream_t s = S_(stream);
   if (a.D == 128)
-    return a.dtype == 0 ? walk_t<128, WALK_DVT, bf16>(a, write_o, write_tape, s)
-                        : walk_t<128, WALK_DVT, float>(a, write_o, write_tape, s);
-  return a.dtype == 0 ? walk_t<64, WALK_DVT, bf16>(a, write_o, write_tape, s)
-                      : walk_t<64, WALK_DVT, float>(a, write_o, write_tape, s);
+    return a.dtype == 0 ? walk_t<128, bf16>(a, write_o, write_tape, s) : walk_t<128, float>(a, write_o, write_tape, s);
+  return a.dtype == 0 ? walk_t<64, bf16>(a, write_o, write_tape, s) : walk_t<64, float>(a, write_o, write_tape, s);
 }
 
 } // namespace gdn
