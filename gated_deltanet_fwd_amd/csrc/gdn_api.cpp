@@ -105,7 +105,7 @@ SavedLayout saved_layout(const Sizes& s, int full) {
 }
 
 struct WorkLayout {
-  size_t seq_c0, c_t0, c_len, seq_order, status, rk, rq, qk, htape, dstape, dqacc, dkacc, total;
+  size_t seq_c0, c_t0, c_len, seq_order, status, discard, rk, rq, qk, htape, dstape, dqacc, dkacc, total;
 };
 
 WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
@@ -121,6 +121,7 @@ WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
   L.c_len = take((size_t)s.NT * 4);
   L.seq_order = take((size_t)s.N * 4);
   L.status = take(4);
+  L.discard = take(gdn::kDiscardBytes);
   L.rk = take((size_t)s.T * s.H * 4);
   L.rq = take((size_t)s.T * s.H * 4);
   L.qk = take((size_t)s.NT * s.HV * kChunk * kChunk * 2);
@@ -237,6 +238,7 @@ void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
   a.c_len = (int*)(b + W.c_len);
   a.seq_order = (int*)(b + W.seq_order);
   a.status = (int*)(b + W.status);
+  a.discard = b + W.discard;
   a.rk = (float*)(b + W.rk);
   a.rq = (float*)(b + W.rq);
   a.qk = (uint16_t*)(b + W.qk);

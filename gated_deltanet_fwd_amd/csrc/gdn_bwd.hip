@@ -151,9 +151,15 @@ int launch_wy_full(const Args& a, void* stream) {
 // ---------------------------------------------------------------------------------------
 // Reverse walk, one workgroup per (document, value head), chunks in reverse. Writes the
 // end-state gradient of every chunk (bf16, transposed) and dh0. Same organisation as the forward
-// walk: wave w keeps its columns of dS and every per-chunk intermediate in registers, chaining
-// MFMA results into B operands with c_to_b; LDS holds the double-buffered chunk inputs (K, Q
-// pre-scaled by exp(gcum) rq, dO, A, P^T and the per-token scalars), one barrier per chunk.
+// walk: D / 16 waves, wave w keeps columns [16 w, 16 w + 16) of dS and every per-chunk
+// intermediate in registers, chaining MFMA results into operands by packing alone (k-permuted
+// fragments, with P^T staged column-permuted to match); LDS holds the double-buffered chunk inputs (K, Q pre-scaled by exp(G) rq, dO, A,
+// P^T and per-token factors), one barrier per chunk.
+template <int D>
+constexpr int bwalk_threads() {
+  return 64 * (D / 16);
+}
+
 template <int D>
 struct BWalkSmem {
   static constexpr int SK = D + 16;
@@ -162,21 +168,25 @@ struct BWalkSmem {
   bf16 sQ[2][CH * SK];
   bf16 sdO[2][CH * SK];
   bf16 sA[2][CH * SA];
-  bf16 sPT[2][CH * SA];
-  float sc[2][3][CH]; // gcum, beta, rk (zero past the chunk's end)
+  bf16 sPT[2][CH * SA]; // columns k-permuted
+  // per token: exp(G_last - G) rk, -beta exp(G) rk (zero past the chunk's end); gamma = exp(G_last)
+  float sc[2][2][CH];
+  float sgam[2];
 };
 
 template <int D, typename TI>
-__global__ __launch_bounds__(NTHREADS, 1) void k_walk_bwd(Args a) {
+__global__ __launch_bounds__(bwalk_threads<D>(), 1) void k_walk_bwd(Args a) {
   if (a.status[0]) return;
   const ChainMap cm = decode_chain(blockIdx.x, a.N, a.H, a.G, 1);
   if (!cm.valid) return;
   const int n = a.seq_order[cm.rank];
   const int j = cm.j, h = j * a.G + cm.gi;
   const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
+  constexpr int NT = bwalk_threads<D>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  constexpr int NRT = D / 16, NCW = D / 64, KD = D / 32, PPT = D / 32, RP = D / 8;
+  constexpr int NRT = D / 16, KD = D / 32, RP = D / 8;
+  constexpr int PPT = CH * RP / NT, APT = CH * 8 / NT;
   using SM = BWalkSmem<D>;
   constexpr int SK = SM::SK, SA = SM::SA;
   __shared__ __attribute__((aligned(16))) SM sm;
@@ -185,67 +195,80 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_walk_bwd(Args a) {
   const TI* dop = (const TI*)a.dO;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
-  const int v0 = 16 * NCW * w;
+  const int v0 = 16 * w;
   const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
 
-  // staging (rows past the chunk's end re-read its last row; beta, rk and the q scale are zero
-  // there and P^T is masked, so they contribute nothing)
-  bf16x8 rK[PPT], rQ[PPT], rD[PPT], rA[2], rP[2];
-  float rqs[PPT], rS;
+  // staging (rows past the chunk's end re-read its last row; the row factors and the q scale are
+  // zero there and P^T is masked, so they contribute nothing)
+  bf16x8 rK[PPT], rQ[PPT], rD[PPT], rA[APT], rP[APT];
+  float rgq[PPT], rrq[PPT];
+  float sg = 0.f, sglast = 0.f, sbeta = 0.f, srk = 0.f;
   auto load_chunk = [&](int c) {
     const int t0 = doc_t0 + (c - c_begin) * CH;
     const int last = min(CH, doc_t1 - t0) - 1;
+    const TI* kc = kp + ((size_t)t0 * a.H + j) * D;
+    const TI* qc = qp + ((size_t)t0 * a.H + j) * D;
+    const TI* dc = dop + ((size_t)t0 * a.HV + h) * D;
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
-      const int p = tid + NTHREADS * it, row = p / RP, pc = p % RP, rr = t0 + min(row, last);
-      rK[it] = IO<TI>::load8(kp + ((size_t)rr * a.H + j) * D + pc * 8);
-      rQ[it] = IO<TI>::load8(qp + ((size_t)rr * a.H + j) * D + pc * 8);
-      rD[it] = IO<TI>::load8(dop + ((size_t)rr * a.HV + h) * D + pc * 8);
-      // the scale exp(gcum) rq of the row is applied to Q when staged (zero past the end)
-      rqs[it] = row <= last ? a.gcum[(size_t)rr * a.HV + h] : -INFINITY;
-      rqs[it] = __expf(rqs[it]) * a.rq[(size_t)rr * a.H + j];
+      const int p = tid + NT * it, row = p / RP, pc = p % RP, rr = min(row, last);
+      rK[it] = IO<TI>::load8(kc + rr * a.H * D + pc * 8);
+      rQ[it] = IO<TI>::load8(qc + rr * a.H * D + pc * 8);
+      rD[it] = IO<TI>::load8(dc + rr * a.HV * D + pc * 8);
+      // Q rows are staged scaled by exp(G) rq (zero past the end; formed in store_chunk, so no
+      // load result is used before the chunk's compute)
+      rgq[it] = a.gcum[(size_t)(t0 + rr) * a.HV + h];
+      rrq[it] = a.rq[(size_t)(t0 + rr) * a.H + j];
     }
+    const bf16* ac = akk + ((size_t)t0 * a.HV + h) * CH;
+    const bf16* pc_ = pm + ((size_t)c * a.HV + h) * CH * CH;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int p = tid + NTHREADS * it, row = p >> 3, pc = p & 7;
-      rA[it] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + min(row, last)) * a.HV + h) * CH + pc * 8);
-      rP[it] = *reinterpret_cast<const bf16x8*>(pm + ((size_t)c * a.HV + h) * CH * CH + row * CH + pc * 8);
+    for (int it = 0; it < APT; ++it) {
+      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+      rA[it] = *reinterpret_cast<const bf16x8*>(ac + min(row, last) * a.HV * CH + pc * 8);
+      rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
     }
-    const int which = min(tid >> 6, 2), row = t0 + min(lane, last);
-    const float* src = which == 0   ? a.gcum + (size_t)row * a.HV + h
-                       : which == 1 ? a.beta + (size_t)row * a.HV + h
-                                    : a.rk + (size_t)row * a.H + j;
-    rS = *src;
+    {
+      // per-token scalars of row `lane` (every wave loads them; wave 0 stages them)
+      const size_t rv = (size_t)(t0 + min(lane, last)), rl = (size_t)(t0 + last);
+      sg = a.gcum[rv * a.HV + h];
+      sglast = a.gcum[rl * a.HV + h];
+      sbeta = a.beta[rv * a.HV + h];
+      srk = a.rk[rv * a.H + j];
+    }
   };
   auto store_chunk = [&](int b, int c) {
     const int t0 = doc_t0 + (c - c_begin) * CH;
     const int len = min(CH, doc_t1 - t0);
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
-      const int p = tid + NTHREADS * it, row = p / RP, pc = p % RP;
+      const int p = tid + NT * it, row = p / RP, pc = p % RP;
       *reinterpret_cast<bf16x8*>(&sm.sK[b][row * SK + pc * 8]) = rK[it];
-      *reinterpret_cast<bf16x8*>(&sm.sQ[b][row * SK + pc * 8]) = scale8(rQ[it], rqs[it]);
+      *reinterpret_cast<bf16x8*>(&sm.sQ[b][row * SK + pc * 8]) = scale8(rQ[it], row < len ? __expf(rgq[it]) * rrq[it] : 0.f);
       *reinterpret_cast<bf16x8*>(&sm.sdO[b][row * SK + pc * 8]) = rD[it];
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int p = tid + NTHREADS * it, row = p >> 3, pc = p & 7;
+    for (int it = 0; it < APT; ++it) {
+      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
       *reinterpret_cast<bf16x8*>(&sm.sA[b][row * SA + pc * 8]) = rA[it];
-      *reinterpret_cast<bf16x8*>(&sm.sPT[b][row * SA + pc * 8]) = rP[it];
+      lds_store_kp8(sm.sPT[b], SA, row, pc, rP[it]);
     }
-    if (tid < 3 * CH) sm.sc[b][tid >> 6][lane] = lane < len ? rS : 0.f;
+    if (w == 0) {
+      const bool ok = lane < len;
+      sm.sc[b][0][lane] = ok ? __expf(sglast - sg) * srk : 0.f;
+      sm.sc[b][1][lane] = ok ? -sbeta * __expf(sg) * srk : 0.f;
+      if (lane == 0) sm.sgam[b] = __expf(sglast);
+    }
   };
 
-  f32x4 dS[NRT][NCW];
+  f32x4 dS[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 16 * rt + 4 * lg + i, cc = v0 + 16 * ct + lr;
-        dS[rt][ct][i] = a.dht ? a.dht[(((size_t)n * a.HV + h) * D + d) * D + cc] : 0.f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * rt + 4 * lg + i;
+      dS[rt][i] = a.dht ? a.dht[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] : 0.f;
+    }
 
   auto step = [&](int b, int c) {
     const bf16* Kt = sm.sK[b];
@@ -253,118 +276,73 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_walk_bwd(Args a) {
     const bf16* Dt = sm.sdO[b];
     const bf16* At = sm.sA[b];
     const bf16* PTt = sm.sPT[b];
-    const float* Gs = sm.sc[b][0];
-    const float* Bs = sm.sc[b][1];
-    const float* Ks = sm.sc[b][2];
-    const int t0 = doc_t0 + (c - c_begin) * CH;
-    const int len = min(CH, doc_t1 - t0);
-    const float glast = Gs[len - 1];
-    const float gam = __expf(glast);
+    const float* DKs = sm.sc[b][0];
+    const float* YKs = sm.sc[b][1];
+    const float gam = sm.sgam[b];
 
-    bf16x8 sb[KD][NCW];
+    bf16x8 sb[KD];
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) sb[kd][ct] = c_to_b(dS[2 * kd][ct], dS[2 * kd + 1][ct]);
+    for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(dS[2 * kd], dS[2 * kd + 1]);
     {
-      bf16* tp = reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D;
+      // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
+      bf16* tp = reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D + (size_t)(v0 + lr) * D + 8 * lg;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) {
-          bf16x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)dS[rt][ct][i];
-          *reinterpret_cast<bf16x4*>(tp + (size_t)(v0 + 16 * ct + lr) * D + 16 * rt + 4 * lg) = v;
-        }
+      for (int kd = 0; kd < KD; ++kd) *reinterpret_cast<bf16x8*>(tp + 32 * kd) = sb[kd];
     }
-    // dO as B operands (k = tokens), shared by P^T dO and (Q')^T dO
-    bf16x8 db[2][NCW];
+    // dO as operands (k = tokens), shared by P^T dO and (Q')^T dO
+    bf16x8 db[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) db[kt][ct] = lds_tr8(Dt, SK, 32 * kt, v0 + 16 * ct);
+    for (int kt = 0; kt < 2; ++kt) db[kt] = lds_tr_kp(Dt, SK, 32 * kt, v0);
     // dR = P^T dO + diag(exp(G_last - G) rk) K dS
-    f32x4 dR[4][NCW];
-    float ybr[4][4];
+    bf16x8 drb[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 kd_[NCW], pd[NCW];
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 dR[2];
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) kd_[ct] = pd[ct] = zero4();
+      for (int hm = 0; hm < 2; ++hm) {
+        const int mt = 2 * kt + hm;
+        f32x4 kd_ = zero4(), pd = zero4();
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) {
-        const bf16x8 ak = lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
+        for (int kd = 0; kd < KD; ++kd) kd_ = mfma(lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg), sb[kd], kd_);
 #pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) kd_[ct] = mfma(ak, sb[kd][ct], kd_[ct]);
+        for (int k2 = 0; k2 < 2; ++k2) pd = mfma(lds8(PTt, SA, 16 * mt + lr, 32 * k2 + 8 * lg), db[k2], pd);
+        const float4 dk4 = *reinterpret_cast<const float4*>(DKs + 16 * mt + 4 * lg);
+        dR[hm][0] = __builtin_fmaf(dk4.x, kd_[0], pd[0]);
+        dR[hm][1] = __builtin_fmaf(dk4.y, kd_[1], pd[1]);
+        dR[hm][2] = __builtin_fmaf(dk4.z, kd_[2], pd[2]);
+        dR[hm][3] = __builtin_fmaf(dk4.w, kd_[3], pd[3]);
       }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 ap = lds8(PTt, SA, 16 * mt + lr, 32 * kt + 8 * lg);
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) pd[ct] = mfma(ap, db[kt][ct], pd[ct]);
-      }
-      const int r0 = 16 * mt + 4 * lg;
-      const float4 g4 = *reinterpret_cast<const float4*>(Gs + r0);
-      const float4 b4 = *reinterpret_cast<const float4*>(Bs + r0);
-      const float4 k4 = *reinterpret_cast<const float4*>(Ks + r0);
-      const float gg[4] = {g4.x, g4.y, g4.z, g4.w}, bb[4] = {b4.x, b4.y, b4.z, b4.w};
-      const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float dec = __expf(glast - gg[i]) * kk[i];
-        ybr[mt][i] = bb[i] * __expf(gg[i]) * kk[i];
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) dR[mt][ct][i] = pd[ct][i] + dec * kd_[ct][i];
-      }
+      drb[kt] = pack_kp(dR[0], dR[1]);
     }
-    bf16x8 drb[2][NCW];
+    // -Y' = -diag(beta b rk) A^T dR
+    bf16x8 yb[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 Y[2];
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) drb[kt][ct] = c_to_b(dR[2 * kt][ct], dR[2 * kt + 1][ct]);
-    // Y' = diag(beta b rk) A^T dR
-    f32x4 Y[4][NCW];
+      for (int hm = 0; hm < 2; ++hm) {
+        const int mt = 2 * kt + hm;
+        f32x4 acc = zero4();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) Y[mt][ct] = zero4();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 aat = lds_tr8(At, SA, 32 * kt, 16 * mt);
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) Y[mt][ct] = mfma(aat, drb[kt][ct], Y[mt][ct]);
+        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(lds_tr_kp(At, SA, 32 * k2, 16 * mt), drb[k2], acc);
+        const float4 y4 = *reinterpret_cast<const float4*>(YKs + 16 * mt + 4 * lg);
+        Y[hm][0] = y4.x * acc[0];
+        Y[hm][1] = y4.y * acc[1];
+        Y[hm][2] = y4.z * acc[2];
+        Y[hm][3] = y4.w * acc[3];
       }
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Y[mt][ct][i] *= ybr[mt][i];
+      yb[kt] = pack_kp(Y[0], Y[1]);
     }
-    bf16x8 yb[2][NCW];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) yb[kt][ct] = c_to_b(Y[2 * kt][ct], Y[2 * kt + 1][ct]);
     // dS <- gamma dS + (Q')^T dO - K^T Y'
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      f32x4 a1[NCW], a2[NCW];
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) a1[ct] = a2[ct] = zero4();
+      f32x4 acc = dS[rt] * gam;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 aq = lds_tr8(Qt, SK, 32 * kt, 16 * rt);
-        const bf16x8 ak = lds_tr8(Kt, SK, 32 * kt, 16 * rt);
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) {
-          a1[ct] = mfma(aq, db[kt][ct], a1[ct]);
-          a2[ct] = mfma(ak, yb[kt][ct], a2[ct]);
-        }
+        acc = mfma(lds_tr_kp(Qt, SK, 32 * kt, 16 * rt), db[kt], acc);
+        acc = mfma(lds_tr_kp(Kt, SK, 32 * kt, 16 * rt), yb[kt], acc);
       }
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dS[rt][ct][i] = __builtin_fmaf(gam, dS[rt][ct][i], a1[ct][i] - a2[ct][i]);
+      dS[rt] = acc;
     }
   };
 
@@ -375,29 +353,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_walk_bwd(Args a) {
   __syncthreads();
   for (int c = c_end - 1; c >= c_begin; --c) {
     const int b = (c_end - 1 - c) & 1;
-    const bool more = c - 1 >= c_begin;
-    if (more) load_chunk(c - 1);
+    // the next chunk in reverse (the first one again at the end, staged into the idle buffer)
+    const int cn = max(c - 1, c_begin);
+    load_chunk(cn);
+    __builtin_amdgcn_sched_barrier(0); // keep every prefetch load ahead of the chunk's compute
     step(b, c);
-    if (more) store_chunk(b ^ 1, c - 1);
+    store_chunk(b ^ 1, cn);
     __syncthreads();
   }
   if (a.dh0) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 16 * rt + 4 * lg + i, cc = v0 + 16 * ct + lr;
-          a.dh0[(((size_t)n * a.HV + h) * D + d) * D + cc] = dS[rt][ct][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * rt + 4 * lg + i;
+        a.dh0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] = dS[rt][i];
+      }
   }
 }
 
 template <int D, typename TI>
 static int walk_bwd_t(const Args& a, hipStream_t s) {
   const dim3 grid(chain_blocks(a, 1));
-  hipLaunchKernelGGL((k_walk_bwd<D, TI>), grid, dim3(NTHREADS), 0, s, a);
+  hipLaunchKernelGGL((k_walk_bwd<D, TI>), grid, dim3(bwalk_threads<D>()), 0, s, a);
   return (int)hipGetLastError();
 }
 

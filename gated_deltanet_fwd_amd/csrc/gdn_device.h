@@ -99,6 +99,63 @@ __device__ __forceinline__ bf16x8 c_to_b(const f32x4& t0, const f32x4& t1) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// ---------------------------------------------------------------------------------------
+// k-permuted fragments. An MFMA sums over its 32 k values in any order, as long as the A and B
+// operands agree on it. The fragments below give lane group g (= lane / 16) the k values
+// 4g .. 4g+3 and 16+4g .. 16+4g+3 of a 32-wide k block, in that order. With that order the two
+// 16x16 result tiles holding k rows [0, 16) and [16, 32) become a B (or A) operand by packing
+// alone: a result tile gives lane group g rows 4g .. 4g+3.
+
+// B (or A) operand from two result tiles, t0 = k rows [0, 16), t1 = k rows [16, 32).
+__device__ __forceinline__ bf16x8 pack_kp(const f32x4& t0, const f32x4& t1) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 r;
+  r[0] = pack_bf16x2(t0[0], t0[1]);
+  r[1] = pack_bf16x2(t0[2], t0[3]);
+  r[2] = pack_bf16x2(t1[0], t1[1]);
+  r[3] = pack_bf16x2(t1[2], t1[3]);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Staging store of 8 consecutive columns [8 q, 8 q + 8) of a row (q = piece index within the row)
+// into a tile kept column-permuted within each 32-column block, so that lds8 at column 32 b + 8 g
+// returns the k-permuted fragment of block b. Column c of a block sits at position
+// 8 ((c % 16) / 4) + 4 (c / 16) + c % 4; a piece splits into two 8-byte writes.
+__device__ __forceinline__ void lds_store_kp8(bf16* tile, int stride, int row, int q, const bf16x8& v) {
+  const int qq = q & 3;
+  bf16* p = tile + row * stride + 32 * (q >> 2) + 16 * (qq & 1) + 4 * (qq >> 1);
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<bf16x4*>(p + 8) = bf16x4{v[4], v[5], v[6], v[7]};
+}
+
+// Operand whose rows are m (lane % 16) and whose k runs along a row-major LDS tile's row:
+// tile[row][k0 + k] in k-permuted order (two 8-byte reads).
+__device__ __forceinline__ bf16x8 lds_kp(const bf16* tile, int stride, int row, int k0) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const bf16* p = tile + row * stride + k0 + 4 * g;
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// Operand whose k runs down a row-major LDS tile's columns: lane receives tile[k0 + k][m0 + lane % 16]
+// in k-permuted order (two transpose-reads; see lds_tr8 for the instruction's lane mapping).
+__device__ __forceinline__ bf16x8 lds_tr_kp(const bf16* tile, int stride, int k0, int m0) {
+  const int l = threadIdx.x & 63;
+  const int g = l >> 4, j = l & 15;
+  const bf16* p0 = tile + (k0 + 4 * g + (j >> 2)) * stride + m0 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 16 * stride));
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
 // Store 4 values of one column, rows r..r+3, into an LDS tile stored transposed
 // (tile[col][row]): one 8-byte write.
 __device__ __forceinline__ void lds_store4_t(bf16* base, int stride, int col, int row, float a, float b, float c,
@@ -127,6 +184,10 @@ struct IO<bf16> {
   static __device__ __forceinline__ bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
   static __device__ __forceinline__ float load1(const bf16* p) { return (float)*p; }
   static __device__ __forceinline__ void store1(bf16* p, float x) { *p = (bf16)x; }
+  // 4 consecutive values (8-byte aligned)
+  static __device__ __forceinline__ void store4(bf16* p, const float x[4]) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+  }
 };
 
 template <>
@@ -147,6 +208,10 @@ struct IO<float> {
   }
   static __device__ __forceinline__ float load1(const float* p) { return *p; }
   static __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
+  // 4 consecutive values (16-byte aligned)
+  static __device__ __forceinline__ void store4(float* p, const float x[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
 };
 
 // Sum over the 16 lanes that share l / 16 (the lanes of one MFMA output row group).

@@ -290,16 +290,23 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
 // WRITE_O: write o (and ht). WRITE_TAPE: write the chunk-start state tape (bf16, transposed).
 // FULL: also write v_new = R.
 //
-// Wave w owns value columns [16*NCW*w, 16*NCW*(w+1)) of the state and keeps them, and every
-// per-chunk intermediate (K S, X, R, the output), in registers: results of one MFMA become B
-// operands of the next through c_to_b, and the state itself is the B operand of K S and Q S. The
-// waves never exchange data; LDS holds only the chunk's shared inputs (K, Q, V, A, P and the
-// per-token scalars), double-buffered, so the next chunk is staged while this one computes and
-// there is one barrier per chunk.
+// D / 16 waves; wave w owns value columns [16 w, 16 w + 16) of the state and keeps them, and
+// every per-chunk intermediate (K S, X, R, the output), in registers. Results of one MFMA become
+// operands of the next by packing alone (k-permuted fragments; A and P are staged with their
+// columns permuted to match, so every row fragment is one 16-byte read), and the state, in
+// natural key order, is the B operand of K S and the A operand of (Q S)^T. The output is formed transposed, so a lane holds four
+// consecutive values of one token's row. The waves never exchange data; LDS holds only the
+// chunk's shared inputs (K, Q, V, A, P and per-token factors), double-buffered, so the next chunk
+// is staged while this one computes, with one barrier per chunk.
+template <int D>
+constexpr int walk_threads() {
+  return 64 * (D / 16);
+}
+
 template <int D, bool WRITE_O>
 struct WalkSmem {
-  static constexpr int SK = D + 16; // token rows of K, Q, V (conflict-free transpose-reads)
-  static constexpr int SA = CH + 16;
+  static constexpr int SK = D + 16; // token rows of K, Q, V
+  static constexpr int SA = CH + 16; // token rows of A and P, columns k-permuted
   static constexpr int NQ = WRITE_O ? 2 : 1;
   static constexpr int LQ = WRITE_O ? CH * SK : 8;
   static constexpr int LP = WRITE_O ? CH * SA : 8;
@@ -308,24 +315,28 @@ struct WalkSmem {
   bf16 sA[2][CH * SA];
   bf16 sQ[NQ][LQ];
   bf16 sP[NQ][LP];
-  float sc[2][4][CH]; // gcum, beta, rk, rq (zero past the chunk's end)
+  // per token: exp(G) rk, beta, exp(G_last - G) rk, exp(G) rq (zero past the chunk's end);
+  // gamma = exp(G_last)
+  float sc[2][4][CH];
+  float sgam[2];
 };
 
 template <int D, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL>
-__global__ __launch_bounds__(NTHREADS, 1) void k_walk_fwd(Args a) {
+__global__ __launch_bounds__(walk_threads<D>(), 1) void k_walk_fwd(Args a) {
   if (a.status[0]) return;
   const ChainMap cm = decode_chain(blockIdx.x, a.N, a.H, a.G, 1);
   if (!cm.valid) return;
   const int n = a.seq_order[cm.rank];
   const int j = cm.j, h = j * a.G + cm.gi;
   const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
+  constexpr int NT = walk_threads<D>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  constexpr int NRT = D / 16; // state row tiles (key dim)
-  constexpr int NCW = D / 64; // 16-column tiles per wave
-  constexpr int KD = D / 32;  // k-steps over the key dim
-  constexpr int PPT = D / 32; // 16-byte pieces per thread of a 64 x D token tile
-  constexpr int RP = D / 8;   // pieces per row
+  constexpr int NRT = D / 16;       // state row tiles (key dim)
+  constexpr int KD = D / 32;        // k-steps over the key dim
+  constexpr int RP = D / 8;         // 16-byte pieces per token row of K, Q, V
+  constexpr int PPT = CH * RP / NT; // pieces per thread of a 64 x D token tile (2)
+  constexpr int APT = CH * 8 / NT;  // pieces per thread of a 64 x 64 tile
   using SM = WalkSmem<D, WRITE_O>;
   constexpr int SK = SM::SK, SA = SM::SA;
   __shared__ __attribute__((aligned(16))) SM sm;
@@ -334,68 +345,82 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_walk_fwd(Args a) {
   const TI* vp = (const TI*)a.v;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
-  const int v0 = 16 * NCW * w;
+  const int v0 = 16 * w;
   // chunk c of the document starts at token cu[n] + 64 (c - c_begin)
   const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
 
   // ---- staging: global -> registers (issued before a chunk's compute) -> LDS (after it).
   // Rows past the chunk's end re-read its last row: finite values whose contributions vanish
-  // because beta and rk are zero there and P is masked.
-  bf16x8 rK[PPT], rV[PPT], rQ[PPT], rA[2], rP[2];
-  float rS;
+  // because beta and the row factors are zero there and P is masked.
+  bf16x8 rK[PPT], rV[PPT], rQ[PPT], rA[APT], rP[APT];
+  float sg = 0.f, sglast = 0.f, sbeta = 0.f, srk = 0.f, srq = 0.f;
   auto load_chunk = [&](int c) {
     const int t0 = doc_t0 + (c - c_begin) * CH;
     const int last = min(CH, doc_t1 - t0) - 1;
+    const TI* kc = kp + ((size_t)t0 * a.H + j) * D;
+    const TI* qc = qp + ((size_t)t0 * a.H + j) * D;
+    const TI* vc = vp + ((size_t)t0 * a.HV + h) * D;
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
-      const int p = tid + NTHREADS * it, row = min(p / RP, last), pc = p % RP;
-      rK[it] = IO<TI>::load8(kp + ((size_t)(t0 + row) * a.H + j) * D + pc * 8);
-      rV[it] = IO<TI>::load8(vp + ((size_t)(t0 + row) * a.HV + h) * D + pc * 8);
-      if (WRITE_O) rQ[it] = IO<TI>::load8(qp + ((size_t)(t0 + row) * a.H + j) * D + pc * 8);
+      const int p = tid + NT * it, row = min(p / RP, last), pc = p % RP;
+      rK[it] = IO<TI>::load8(kc + row * a.H * D + pc * 8);
+      rV[it] = IO<TI>::load8(vc + row * a.HV * D + pc * 8);
+      if (WRITE_O) rQ[it] = IO<TI>::load8(qc + row * a.H * D + pc * 8);
     }
+    const bf16* ac = akk + ((size_t)t0 * a.HV + h) * CH;
+    const bf16* pc_ = pm + ((size_t)c * a.HV + h) * CH * CH;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int p = tid + NTHREADS * it, row = p >> 3, pc = p & 7;
-      rA[it] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + min(row, last)) * a.HV + h) * CH + pc * 8);
-      if (WRITE_O) rP[it] = *reinterpret_cast<const bf16x8*>(pm + ((size_t)c * a.HV + h) * CH * CH + row * CH + pc * 8);
+    for (int it = 0; it < APT; ++it) {
+      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+      rA[it] = *reinterpret_cast<const bf16x8*>(ac + min(row, last) * a.HV * CH + pc * 8);
+      if (WRITE_O) rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
     }
-    const int which = tid >> 6, row = t0 + min(lane, last);
-    const float* src = which == 0   ? a.gcum + (size_t)row * a.HV + h
-                       : which == 1 ? a.beta + (size_t)row * a.HV + h
-                       : which == 2 ? a.rk + (size_t)row * a.H + j
-                                    : a.rq + (size_t)row * a.H + j;
-    rS = *src;
+    {
+      // per-token scalars of row `lane` (every wave loads them; wave 0 stages them)
+      const size_t rv = (size_t)(t0 + min(lane, last)), rl = (size_t)(t0 + last);
+      sg = a.gcum[rv * a.HV + h];
+      sglast = a.gcum[rl * a.HV + h];
+      sbeta = a.beta[rv * a.HV + h];
+      srk = a.rk[rv * a.H + j];
+      if (WRITE_O) srq = a.rq[rv * a.H + j];
+    }
   };
   auto store_chunk = [&](int b, int c) {
     const int t0 = doc_t0 + (c - c_begin) * CH;
     const int len = min(CH, doc_t1 - t0);
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
-      const int p = tid + NTHREADS * it, row = p / RP, pc = p % RP;
+      const int p = tid + NT * it, row = p / RP, pc = p % RP;
       *reinterpret_cast<bf16x8*>(&sm.sK[b][row * SK + pc * 8]) = rK[it];
       *reinterpret_cast<bf16x8*>(&sm.sV[b][row * SK + pc * 8]) = rV[it];
       if (WRITE_O) *reinterpret_cast<bf16x8*>(&sm.sQ[b][row * SK + pc * 8]) = rQ[it];
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int p = tid + NTHREADS * it, row = p >> 3, pc = p & 7;
-      *reinterpret_cast<bf16x8*>(&sm.sA[b][row * SA + pc * 8]) = rA[it];
-      if (WRITE_O) *reinterpret_cast<bf16x8*>(&sm.sP[b][row * SA + pc * 8]) = rP[it];
+    for (int it = 0; it < APT; ++it) {
+      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+      lds_store_kp8(sm.sA[b], SA, row, pc, rA[it]);
+      if (WRITE_O) lds_store_kp8(sm.sP[b], SA, row, pc, rP[it]);
     }
-    sm.sc[b][tid >> 6][lane] = lane < len ? rS : 0.f;
+    if (w == 0) {
+      const bool ok = lane < len;
+      const float eb = __expf(sg);
+      sm.sc[b][0][lane] = ok ? eb * srk : 0.f;
+      sm.sc[b][1][lane] = ok ? sbeta : 0.f;
+      sm.sc[b][2][lane] = ok ? __expf(sglast - sg) * srk : 0.f;
+      if (WRITE_O) sm.sc[b][3][lane] = ok ? eb * srq : 0.f;
+      if (lane == 0) sm.sgam[b] = __expf(sglast);
+    }
   };
 
-  // ---- state: rows 16 rt + 4 lg + i (key), columns v0 + 16 ct + lr (value)
-  f32x4 S[NRT][NCW];
+  // ---- state: rows 16 rt + 4 lg + i (key), column v0 + lr (value)
+  f32x4 S[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 16 * rt + 4 * lg + i, cc = v0 + 16 * ct + lr;
-        S[rt][ct][i] = a.has_h0 ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + cc] : 0.f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * rt + 4 * lg + i;
+      S[rt][i] = a.has_h0 ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] : 0.f;
+    }
 
   auto step = [&](int b, int c) {
     const bf16* Kt = sm.sK[b];
@@ -403,162 +428,113 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_walk_fwd(Args a) {
     const bf16* At = sm.sA[b];
     const bf16* Qt = sm.sQ[WRITE_O ? b : 0];
     const bf16* Pt = sm.sP[WRITE_O ? b : 0];
-    const float* Gs = sm.sc[b][0];
+    const float* BKs = sm.sc[b][0];
     const float* Bs = sm.sc[b][1];
-    const float* Ks = sm.sc[b][2];
-    const float* Qs = sm.sc[b][3];
+    const float* DKs = sm.sc[b][2];
+    const float* BQs = sm.sc[b][3];
     const int t0 = doc_t0 + (c - c_begin) * CH;
     const int len = min(CH, doc_t1 - t0);
-    const float glast = Gs[len - 1];
-    const float gam = __expf(glast);
+    const float gam = sm.sgam[b];
 
-    // the state as bf16 B operands (k = key dim)
-    bf16x8 sb[KD][NCW];
+    // the state as operands in natural key order (k = key dim)
+    bf16x8 sb[KD];
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) sb[kd][ct] = c_to_b(S[2 * kd][ct], S[2 * kd + 1][ct]);
+    for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(S[2 * kd], S[2 * kd + 1]);
     if (WRITE_TAPE) {
-      bf16* tp = reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D;
+      // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
+      bf16* tp = reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D + (size_t)(v0 + lr) * D + 8 * lg;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) {
-          bf16x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)S[rt][ct][i];
-          *reinterpret_cast<bf16x4*>(tp + (size_t)(v0 + 16 * ct + lr) * D + 16 * rt + 4 * lg) = v;
-        }
+      for (int kd = 0; kd < KD; ++kd) *reinterpret_cast<bf16x8*>(tp + 32 * kd) = sb[kd];
     }
-    // K S and Q S: 64 tokens x this wave's columns
-    f32x4 ks[4][NCW], qs[4][NCW];
+    // K S (64 tokens x 16 columns) and (Q S)^T (16 columns x 64 tokens)
+    f32x4 ks[4], qsT[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) ks[mt][ct] = qs[mt][ct] = zero4();
+    for (int mt = 0; mt < 4; ++mt) ks[mt] = qsT[mt] = zero4();
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 ak = lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
-        bf16x8 aq;
-        if (WRITE_O) aq = lds8(Qt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) {
-          ks[mt][ct] = mfma(ak, sb[kd][ct], ks[mt][ct]);
-          if (WRITE_O) qs[mt][ct] = mfma(aq, sb[kd][ct], qs[mt][ct]);
-        }
+        ks[mt] = mfma(lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg), sb[kd], ks[mt]);
+        if (WRITE_O) qsT[mt] = mfma(sb[kd], lds8(Qt, SK, 16 * mt + lr, 32 * kd + 8 * lg), qsT[mt]);
       }
-    // X = diag(beta) (V - diag(b rk) K S); per-row factors of this lane's rows
-    f32x4 X[4][NCW];
-    float brow[4][4], rqrow[4][4], decr[4][4];
+    // X = diag(beta) (V - diag(b rk) K S)
+    bf16x8 xb[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int r0 = 16 * mt + 4 * lg;
-      const float4 g4 = *reinterpret_cast<const float4*>(Gs + r0);
-      const float4 b4 = *reinterpret_cast<const float4*>(Bs + r0);
-      const float4 k4 = *reinterpret_cast<const float4*>(Ks + r0);
-      const float4 q4 = *reinterpret_cast<const float4*>(Qs + r0);
-      const float gg[4] = {g4.x, g4.y, g4.z, g4.w}, bb[4] = {b4.x, b4.y, b4.z, b4.w};
-      const float kk[4] = {k4.x, k4.y, k4.z, k4.w}, qq[4] = {q4.x, q4.y, q4.z, q4.w};
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 X[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        brow[mt][i] = __expf(gg[i]);
-        rqrow[mt][i] = qq[i];
-        decr[mt][i] = __expf(glast - gg[i]) * kk[i];
+      for (int hm = 0; hm < 2; ++hm) {
+        const int mt = 2 * kt + hm, r0 = 16 * mt + 4 * lg;
+        const float4 bk4 = *reinterpret_cast<const float4*>(BKs + r0);
+        const float4 be4 = *reinterpret_cast<const float4*>(Bs + r0);
+        const float bk[4] = {bk4.x, bk4.y, bk4.z, bk4.w}, be[4] = {be4.x, be4.y, be4.z, be4.w};
+        const bf16x4 vv = lds_tr4c(Vt, SK, 16 * mt, v0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[hm][i] = be[i] * __builtin_fmaf(-bk[i], ks[mt][i], (float)vv[i]);
       }
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) {
-        const bf16x4 vv = lds_tr4c(Vt, SK, 16 * mt, v0 + 16 * ct);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) X[mt][ct][i] = bb[i] * ((float)vv[i] - brow[mt][i] * kk[i] * ks[mt][ct][i]);
-      }
+      xb[kt] = pack_kp(X[0], X[1]);
     }
-    bf16x8 xb[2][NCW];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) xb[kt][ct] = c_to_b(X[2 * kt][ct], X[2 * kt + 1][ct]);
     // R = A X
-    f32x4 R[4][NCW];
+    f32x4 R[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+      R[mt] = zero4();
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) R[mt][ct] = zero4();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 aa = lds8(At, SA, 16 * mt + lr, 32 * kt + 8 * lg);
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) R[mt][ct] = mfma(aa, xb[kt][ct], R[mt][ct]);
-      }
+      for (int kt = 0; kt < 2; ++kt) R[mt] = mfma(lds8(At, SA, 16 * mt + lr, 32 * kt + 8 * lg), xb[kt], R[mt]);
     }
     if (FULL) {
-      bf16* vn = reinterpret_cast<bf16*>(a.vnew);
+      // rows past the chunk's end go to the discard area (no branch around the stores)
+      bf16* vn = reinterpret_cast<bf16*>(a.vnew) + ((size_t)t0 * a.HV + h) * D + v0 + lr;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mt + 4 * lg + i;
-            if (r < len) vn[((size_t)(t0 + r) * a.HV + h) * D + v0 + 16 * ct + lr] = (bf16)R[mt][ct][i];
-          }
-    }
-    // B operands of R (for P R) and of diag(exp(G_last - G) rk) R (for the state update)
-    bf16x8 rb[2][NCW], rdb[2][NCW];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) {
-        if (WRITE_O) rb[kt][ct] = c_to_b(R[2 * kt][ct], R[2 * kt + 1][ct]);
-        f32x4 d0, d1;
-#pragma unroll
         for (int i = 0; i < 4; ++i) {
-          d0[i] = decr[2 * kt][i] * R[2 * kt][ct][i];
-          d1[i] = decr[2 * kt + 1][i] * R[2 * kt + 1][ct][i];
+          const int r = 16 * mt + 4 * lg + i;
+          bf16* dst = r < len ? vn + (size_t)r * a.HV * D : reinterpret_cast<bf16*>(a.discard) + lane;
+          *dst = (bf16)R[mt][i];
         }
-        rdb[kt][ct] = c_to_b(d0, d1);
+    }
+    // operands of R (for (P R)^T) and of diag(exp(G_last - G) rk) R (for the state update)
+    bf16x8 rb[2], rdb[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if (WRITE_O) rb[kt] = pack_kp(R[2 * kt], R[2 * kt + 1]);
+      f32x4 d[2];
+#pragma unroll
+      for (int hm = 0; hm < 2; ++hm) {
+        const float4 dk4 = *reinterpret_cast<const float4*>(DKs + 16 * (2 * kt + hm) + 4 * lg);
+        d[hm][0] = dk4.x * R[2 * kt + hm][0];
+        d[hm][1] = dk4.y * R[2 * kt + hm][1];
+        d[hm][2] = dk4.z * R[2 * kt + hm][2];
+        d[hm][3] = dk4.w * R[2 * kt + hm][3];
       }
-    // O = diag(b rq) Q S + P R
+      rdb[kt] = pack_kp(d[0], d[1]);
+    }
+    // O^T = diag-column(b rq) (Q S)^T + (P R)^T; lane holds O[t][v0 + 4 lg .. +3], t = 16 mt + lr
     if (WRITE_O) {
-      TI* op = (TI*)a.o;
+      TI* op = (TI*)a.o + ((size_t)t0 * a.HV + h) * D + v0 + 4 * lg;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc[NCW];
+        f32x4 acc = zero4();
 #pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) acc[ct] = zero4();
+        for (int kt = 0; kt < 2; ++kt) acc = mfma(rb[kt], lds8(Pt, SA, 16 * mt + lr, 32 * kt + 8 * lg), acc);
+        const int t = 16 * mt + lr;
+        const float sq = BQs[t];
+        float ov[4];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 ap = lds8(Pt, SA, 16 * mt + lr, 32 * kt + 8 * lg);
-#pragma unroll
-          for (int ct = 0; ct < NCW; ++ct) acc[ct] = mfma(ap, rb[kt][ct], acc[ct]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mt + 4 * lg + i;
-            const float ov = brow[mt][i] * rqrow[mt][i] * qs[mt][ct][i] + acc[ct][i];
-            if (r < len) IO<TI>::store1(op + ((size_t)(t0 + r) * a.HV + h) * D + v0 + 16 * ct + lr, ov);
-          }
+        for (int i = 0; i < 4; ++i) ov[i] = __builtin_fmaf(sq, qsT[mt][i], acc[i]);
+        // tokens past the chunk's end go to the discard area: every lane stores, so no branch
+        // hides the number of outstanding stores from the wait counts
+        IO<TI>::store4(t < len ? op + (size_t)t * a.HV * D : reinterpret_cast<TI*>(a.discard) + 4 * lane, ov);
       }
     }
     // S <- gamma S + K^T diag(exp(G_last - G) rk) R
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      f32x4 acc[NCW];
+      f32x4 acc = S[rt] * gam;
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) acc[ct] = zero4();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 akt = lds_tr8(Kt, SK, 32 * kt, 16 * rt);
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) acc[ct] = mfma(akt, rdb[kt][ct], acc[ct]);
-      }
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[rt][ct][i] = __builtin_fmaf(gam, S[rt][ct][i], acc[ct][i]);
+      for (int kt = 0; kt < 2; ++kt) acc = mfma(lds_tr_kp(Kt, SK, 32 * kt, 16 * rt), rdb[kt], acc);
+      S[rt] = acc;
     }
   };
 
@@ -569,22 +545,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_walk_fwd(Args a) {
   __syncthreads();
   for (int c = c_begin; c < c_end; ++c) {
     const int b = (c - c_begin) & 1;
-    const bool more = c + 1 < c_end;
-    if (more) load_chunk(c + 1);
+    // the next chunk (the last one again at the end: staged into the idle buffer, never read);
+    // unconditional, so the loads stay in flight across the whole step
+    const int cn = min(c + 1, c_end - 1);
+    load_chunk(cn);
+    __builtin_amdgcn_sched_barrier(0); // keep every prefetch load ahead of the chunk's compute
     step(b, c);
-    if (more) store_chunk(b ^ 1, c + 1);
+    store_chunk(b ^ 1, cn);
     __syncthreads();
   }
   if (WRITE_O && a.want_ht) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 16 * rt + 4 * lg + i, cc = v0 + 16 * ct + lr;
-          a.ht[(((size_t)n * a.HV + h) * D + d) * D + cc] = S[rt][ct][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * rt + 4 * lg + i;
+        a.ht[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] = S[rt][i];
+      }
   }
 }
 
@@ -620,7 +597,7 @@ int chain_blocks(const Args& a, int ntile) { return ((a.N * a.H + 7) / 8) * 8 * 
 
 template <int D, typename TI>
 static int walk_t(const Args& a, int write_o, int write_tape, hipStream_t s) {
-  const dim3 grid(chain_blocks(a, 1)), blk(NTHREADS);
+  const dim3 grid(chain_blocks(a, 1)), blk(walk_threads<D>());
   if (write_o && !write_tape) hipLaunchKernelGGL((k_walk_fwd<D, TI, true, false, false>), grid, blk, 0, s, a);
   else if (write_o) hipLaunchKernelGGL((k_walk_fwd<D, TI, true, true, true>), grid, blk, 0, s, a);
   else if (a.full) hipLaunchKernelGGL((k_walk_fwd<D, TI, false, true, true>), grid, blk, 0, s, a);

@@ -46,6 +46,7 @@ struct Args {
   int* c_len;      // [NT] valid tokens of each chunk (1..64)
   int* seq_order;  // [N] documents, longest first
   int* status;     // [1] nonzero if the device tables disagree with the host's chunk count
+  void* discard;   // [kDiscardBytes] target of stores from lanes past a chunk's end (never read)
   float* rk;       // [T, H] inverse L2 norms of k rows (1 when the norm is off)
   float* rq;       // [T, H] inverse L2 norms of q rows
   uint16_t* qk;    // bf16 [NT, HV, 64, 64] P = exp(G_q - G_k) qh.kh masked to q >= k, per value head
@@ -55,16 +56,8 @@ struct Args {
   float* dkacc;    // f32 [T, H, d] (atomic reduction only)
 };
 
-// Value-column tile width of the forward and reverse state walks (columns of S per workgroup).
-// The split does not change any column's arithmetic, only how the chains share the chip.
-#ifndef GDN_WALK_DVT
-#define GDN_WALK_DVT 32
-#endif
-#ifndef GDN_BWALK_DVT
-#define GDN_BWALK_DVT 32
-#endif
-constexpr int WALK_DVT = GDN_WALK_DVT;
-constexpr int BWALK_DVT = GDN_BWALK_DVT;
+// Bytes of the workspace area that takes the stores of lanes past a chunk's end.
+constexpr size_t kDiscardBytes = 4096;
 
 int chain_blocks(const Args& a, int ntile);
 
