@@ -34,37 +34,41 @@ CHUNK = 64
 METRIC = "tokens/s fwd+bwd (and fwd, ckpt) at (H,HV)=(16,48), d=128, 262144 tok"
 
 
-def kernel_models(T, NT, N, H, HV, D, io, has_h0=False):
+def kernel_models(T, NT, N, H, HV, D, io, has_h0=False, det=False):
     """Algorithmic (compulsory) bytes and MFMA flops of one launch of each kernel.
 
-    Bytes: every operand of the kernel read once and every result written once. Flops: the
-    contractions of the chunked method the kernel performs, 2 flops per multiply-add.
+    Bytes: every operand of the kernel read once and every result written once (a q/k tile read by
+    the G value heads of its group counts once). Flops: the contractions of the chunked method the
+    kernel performs, 2 flops per multiply-add.
     """
     C = CHUNK
     f4 = 4
-    qk_ws = NT * H * C * C * 2
-    akk = T * HV * C * 2
-    scal_v = T * HV * f4
-    scal_q = T * H * f4
-    tape = NT * HV * D * D * 2
+    pv = NT * HV * C * C * 2       # decayed masked q.k per value head (P or P^T), bf16
+    akk = T * HV * C * 2           # A rows, bf16
+    scal_v = T * HV * f4           # one f32 per token and value head
+    scal_q = T * H * f4            # one f32 per token and q/k head
+    gam = NT * HV * f4
+    tape = NT * HV * D * D * 2     # one bf16 state per chunk and value head
     qkin = T * H * D * io
     vin = T * HV * D * io
     states = N * HV * D * D * f4
+    acc = T * H * D * f4           # f32 dq or dk accumulator (atomic reduction)
     m = {}
-    m["gdn_intra"] = (2 * qkin + 2 * scal_v + 2 * scal_q + qk_ws + akk + scal_v + NT * HV * f4,
+    m["gdn_intra"] = (2 * qkin + 2 * scal_v + 2 * scal_q + pv + akk + scal_v + gam,
                       NT * H * 2 * (2 * C * C * D) + NT * HV * (2 * C ** 3 // 3))
-    m["gdn_intra_bwd"] = (2 * qkin + 2 * scal_q + qk_ws, NT * H * 2 * (2 * C * C * D))
-    m["gdn_walk_fwd"] = (2 * qkin + vin + akk + qk_ws + 2 * scal_v + 2 * scal_q + NT * HV * f4 + vin
-                         + (states if has_h0 else 0), T * HV * (6 * D * D + 4 * C * D))
-    m["gdn_walk_tape"] = (qkin + vin + akk + 2 * scal_v + scal_q + NT * HV * f4 + tape,
-                          T * HV * (4 * D * D + 2 * C * D))
-    m["gdn_walk_bwd"] = (2 * qkin + vin + akk + qk_ws + 2 * scal_v + 2 * scal_q + NT * HV * f4 + tape,
+    m["gdn_intra_bwd"] = (2 * qkin + scal_v + 2 * scal_q + pv, NT * H * 2 * (2 * C * C * D))
+    m["gdn_walk_fwd"] = (2 * qkin + vin + akk + pv + 2 * scal_v + 2 * scal_q + vin + (2 * states if has_h0 else 0),
                          T * HV * (6 * D * D + 4 * C * D))
-    m["gdn_chunk_grad"] = (2 * tape + 2 * qkin + 2 * vin + akk + 2 * scal_v + 2 * scal_q + NT * HV * f4
-                           + 2 * qkin + vin + 2 * scal_v,
+    m["gdn_walk_tape"] = (qkin + vin + akk + 2 * scal_v + scal_q + tape + (states if has_h0 else 0),
+                          T * HV * (4 * D * D + 2 * C * D))
+    m["gdn_walk_bwd"] = (2 * qkin + vin + akk + pv + 2 * scal_v + 2 * scal_q + tape + (2 * states if has_h0 else 0),
+                         T * HV * (6 * D * D + 4 * C * D))
+    out_qk = 2 * qkin if det else 2 * acc
+    m["gdn_chunk_grad"] = (2 * tape + 2 * qkin + 2 * vin + akk + pv + 2 * scal_v + 2 * scal_q + gam
+                           + vin + 2 * scal_v + out_qk,
                            T * HV * 2 * (5 * D * D + 8 * C * D + 2 * C * C) + NT * H * 2 * (2 * C * C * D))
-    m["gdn_finalize_qk"] = (2 * T * H * D * f4 + 2 * qkin + 2 * scal_q + 2 * qkin, 0)
-    m["gdn_fill_zero"] = (T * H * D * f4, 0)
+    m["gdn_finalize_qk"] = (2 * acc + 2 * qkin + 2 * scal_q + 2 * qkin, 0)
+    m["gdn_fill_zero"] = (acc, 0)
     return m
 
 
@@ -107,26 +111,131 @@ def load_traffic(kernel, workload):
 
 
 def cpu_baseline(w, inputs_dev):
-    """Time the FP64 oracle (fwd + bwd) on the shortest document of the workload, all heads."""
+    """Time the FP64 oracle (fwd + bwd, all heads) on the two shortest documents of the workload."""
     import numpy as np
     import oracle
 
     cu = inputs_dev["cu_seqlens"].cpu().numpy()
     lens = np.diff(cu)
-    n = int(np.argmin(lens))
-    s, e = int(cu[n]), int(cu[n + 1])
-    f = lambda t: None if t is None else t[s:e].float().cpu().numpy()
+    docs = sorted(np.argsort(lens, kind="stable")[:2].tolist())
+    tok = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in docs])
+    ti = __import__("torch").from_numpy(tok).to(inputs_dev["q"].device)
+    f = lambda t: None if t is None else t.index_select(0, ti).float().cpu().numpy()
     q, k, v, g, b, dO = (f(inputs_dev[x]) for x in ("q", "k", "v", "g", "beta", "dO"))
-    cu1 = np.array([0, e - s], np.int32)
+    cu1 = np.zeros(len(docs) + 1, np.int32)
+    cu1[1:] = np.cumsum(lens[docs])
     threads = oracle.default_threads()
-    used = min(threads, w.H)  # the oracle splits work over (document, q/k head) items
+    used = min(threads, len(docs) * w.H)  # the oracle splits work over (document, q/k head) items
     t0 = time.time()
     oracle.fwd(cu1, q, k, v, g, b, None, l2norm=w.l2norm, threads=threads)
     oracle.bwd(cu1, q, k, v, g, b, dO, None, None, l2norm=w.l2norm, threads=threads)
     dt = time.time() - t0
-    return {"value": (e - s) / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": "fwd+bwd of document %d (%d tokens, all %d q/k and %d v heads, d=%d) of the same pack, "
-                      "FP64 token recurrence, %.1f s" % (n, e - s, w.H, w.HV, w.d, dt)}
+    ntok = int(len(tok))
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "fwd+bwd of documents %s (%d tokens, all %d q/k and %d v heads, d=%d) of the same pack, "
+                      "FP64 token recurrence, %.1f s" % ("/".join(str(int(lens[n])) for n in docs), ntok, w.H,
+                                                          w.HV, w.d, dt)}
+
+
+COPY_BYTES = 1 << 30  # bytes read (and written) by the calibration copy
+
+# Library kernels in launch order within one fwd + bwd step (light, D = 128). rocprofv3 prints some
+# template instances mangled and some garbled, so two instances of one template are told apart by
+# the order in which their kernel ids first appear: the forward call runs before the backward.
+KERNEL_ORDER = {"k_tables": ["gdn_tables"], "k_intra": ["gdn_intra", "gdn_intra_bwd"],
+                "k_walk_fwd": ["gdn_walk_fwd", "gdn_walk_tape"], "k_write_tag": ["gdn_write_tag"],
+                "k_walk_bwd": ["gdn_walk_bwd"], "k_fill_zero": ["gdn_fill_zero"],
+                "k_chunk_grad": ["gdn_chunk_grad"], "k_finalize_qk": ["gdn_finalize_qk"]}
+KERNEL_SOURCE = {"gdn_tables": "gdn_fwd.hip", "gdn_intra": "gdn_fwd.hip", "gdn_intra_bwd": "gdn_fwd.hip",
+                 "gdn_walk_fwd": "gdn_fwd.hip", "gdn_walk_tape": "gdn_fwd.hip", "gdn_write_tag": "gdn_bwd.hip",
+                 "gdn_walk_bwd": "gdn_bwd.hip", "gdn_fill_zero": "gdn_bwd.hip", "gdn_chunk_grad": "gdn_bwd.hip",
+                 "gdn_finalize_qk": "gdn_bwd.hip"}
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _kernel_names(rows):
+    """Kernel_Id -> library kernel name (or None), by template and first appearance."""
+    first = {}
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        first.setdefault(r["Kernel_Id"], (int(r["Dispatch_Id"]), r["Kernel_Name"]))
+    seen = {}
+    out = {}
+    for kid, (_, name) in sorted(first.items(), key=lambda x: x[1][0]):
+        tmpl = next((t for t in KERNEL_ORDER if t in name), None)
+        if tmpl is None:
+            out[kid] = None
+            continue
+        i = seen.get(tmpl, 0)
+        seen[tmpl] = i + 1
+        out[kid] = KERNEL_ORDER[tmpl][min(i, len(KERNEL_ORDER[tmpl]) - 1)]
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir, out_dir, workload):
+    """Per-launch HBM bytes of each library kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by bytes / reading of the same counter on the calibration copy (COPY_BYTES read and
+    written by one copy kernel, the run's last torch elementwise kernel). Writes
+    pmc_<kernel>_<workload>.json per kernel into out_dir and prints a table."""
+    import statistics
+    res, scales = {}, {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        if not rows:
+            raise SystemExit("no %s rows in %s" % (counter, d))
+        names = _kernel_names(rows)
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if names[r["Kernel_Id"]] is None and ("copy" in r["Kernel_Name"].lower()
+                                                        or "elementwise" in r["Kernel_Name"].lower())]
+        scales[counter] = COPY_BYTES / copies[-1]
+        for r in rows:
+            n = names[r["Kernel_Id"]]
+            if n:
+                res.setdefault(n, {}).setdefault(counter, []).append(float(r["Counter_Value"]) * scales[counter])
+    os.makedirs(out_dir, exist_ok=True)
+    lines = ["| kernel | launches | FETCH bytes/launch | WRITE bytes/launch | HBM GB/launch |",
+             "|---|---|---|---|---|"]
+    for name, c in sorted(res.items()):
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        fb, wb = statistics.median(c["FETCH_SIZE"]), statistics.median(c["WRITE_SIZE"])
+        src = KERNEL_SOURCE[name]
+        rec = {"kernel": name, "workload": workload, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+               "bytes_per_launch": fb + wb, "launches": len(c["FETCH_SIZE"]), "source": src,
+               "source_sha": source_sha(os.path.join(ROOT, "gated_deltanet_fwd_amd", "csrc", src)),
+               "copy_scale_bytes_per_unit": scales}
+        with open(os.path.join(out_dir, "pmc_%s_%s.json" % (name, workload)), "w") as f:
+            json.dump(rec, f, indent=1)
+        lines.append("| `%s` | %d | %.4e | %.4e | %.3f |" % (name, len(c["FETCH_SIZE"]), fb, wb, (fb + wb) / 1e9))
+    print("\n".join(lines))
+    print("\ncalibration: bytes per counter unit %s (copy of %d bytes read and written)" % (scales, COPY_BYTES))
+
+
+def summarize_trace(trace_dir, command):
+    """Per-kernel count, total and average duration from a rocprofv3 --kernel-trace CSV."""
+    import statistics
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    names = _kernel_names(rows)
+    agg = {}
+    for r in rows:
+        n = names[r["Kernel_Id"]] or r["Kernel_Name"][:60]
+        agg.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6)
+    total = sum(sum(v) for v in agg.values())
+    lines = ["Command (from the repository root on one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | total ms | avg ms | median ms | % of GPU time |", "|---|---|---|---|---|---|"]
+    for n, v in sorted(agg.items(), key=lambda x: -sum(x[1])):
+        lines.append("| `%s` | %d | %.3f | %.3f | %.3f | %.1f |" % (n, len(v), sum(v), sum(v) / len(v),
+                                                                  statistics.median(v), 100 * sum(v) / total))
+    print("\n".join(lines))
 
 
 def main():
@@ -138,7 +247,21 @@ def main():
     ap.add_argument("--deterministic", action="store_true", help="deterministic dq/dk reduction")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fwd-only and ckpt timings")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain device copy of %d MiB (counter calibration)" %
+                    (COPY_BYTES >> 20))
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with "
+                         "--copy-calibration into per-kernel HBM traffic records; no GPU is used")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
+                    help="per-kernel durations from a rocprofv3 --kernel-trace run of this script; no GPU")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, workload=args.workload)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (it would shard the "
@@ -221,7 +344,7 @@ def main():
     value = w.T * args.steps / t_fb
     io = 2 if w.dtype == "bf16" else 4
     NT = int(sum((L + CHUNK - 1) // CHUNK for L in w.lengths))
-    models = kernel_models(w.T, NT, w.N, w.H, w.HV, w.d, io, has_h0=w.has_h0)
+    models = kernel_models(w.T, NT, w.N, w.H, w.HV, w.d, io, has_h0=w.has_h0, det=det)
     # dominant kernel = largest share of the timed step
     dom = max((k for k in kernels if k in models), key=lambda k: kernels[k]["total_ms"])
     by, fl = models[dom]
@@ -267,6 +390,13 @@ def main():
         out[k] = dict(v, roofline_frac=sr[k]["roofline_s"] / (v["ms"] / 1e3))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(out), flush=True)
 
 

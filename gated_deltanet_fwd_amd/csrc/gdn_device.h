@@ -223,6 +223,24 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
+// Sum over the 16 lanes of each row (lanes with equal l / 16), in every lane: DPP row rotations,
+// no LDS traffic.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
+// Sum over the four 16-lane rows (lanes with equal l % 16), in every lane. (The lane-swap
+// instructions are not used here: with one value as both operands the compiler folds them away.)
+__device__ __forceinline__ float col_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
 // Chain index -> (document rank, q/k head, v head within the group, value tile), with
 // workgroups that read the same q/k tiles placed on the same XCD. Workgroups are dealt to
 // the 8 XCDs round-robin by workgroup id, so a group of GS chains (one q/k head of one
