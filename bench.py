@@ -63,6 +63,7 @@ def kernel_models(T, NT, N, H, HV, D, io, has_h0=False, det=False):
                           T * HV * (4 * D * D + 2 * C * D))
     m["gdn_walk_bwd"] = (2 * qkin + vin + akk + pv + 2 * scal_v + 2 * scal_q + tape + (2 * states if has_h0 else 0),
                          T * HV * (6 * D * D + 4 * C * D))
+    m["gdn_walk_pair"] = tuple(x + y for x, y in zip(m["gdn_walk_tape"], m["gdn_walk_bwd"]))
     out_qk = 2 * qkin if det else 2 * acc
     m["gdn_chunk_grad"] = (2 * tape + 2 * qkin + 2 * vin + akk + pv + 2 * scal_v + 2 * scal_q + gam
                            + vin + 2 * scal_v + out_qk,
@@ -144,11 +145,11 @@ COPY_BYTES = 1 << 30  # bytes read (and written) by the calibration copy
 # the order in which their kernel ids first appear: the forward call runs before the backward.
 KERNEL_ORDER = {"k_tables": ["gdn_tables"], "k_intra": ["gdn_intra", "gdn_intra_bwd"],
                 "k_walk_fwd": ["gdn_walk_fwd", "gdn_walk_tape"], "k_write_tag": ["gdn_write_tag"],
-                "k_walk_bwd": ["gdn_walk_bwd"], "k_fill_zero": ["gdn_fill_zero"],
+                "k_walk_pair": ["gdn_walk_pair"], "k_walk_bwd": ["gdn_walk_bwd"], "k_fill_zero": ["gdn_fill_zero"],
                 "k_chunk_grad": ["gdn_chunk_grad"], "k_finalize_qk": ["gdn_finalize_qk"]}
 KERNEL_SOURCE = {"gdn_tables": "gdn_fwd.hip", "gdn_intra": "gdn_fwd.hip", "gdn_intra_bwd": "gdn_fwd.hip",
                  "gdn_walk_fwd": "gdn_fwd.hip", "gdn_walk_tape": "gdn_fwd.hip", "gdn_write_tag": "gdn_bwd.hip",
-                 "gdn_walk_bwd": "gdn_bwd.hip", "gdn_fill_zero": "gdn_bwd.hip", "gdn_chunk_grad": "gdn_bwd.hip",
+                 "gdn_walk_bwd": "gdn_bwd.hip", "gdn_walk_pair": "gdn_bwd.hip", "gdn_fill_zero": "gdn_bwd.hip", "gdn_chunk_grad": "gdn_bwd.hip",
                  "gdn_finalize_qk": "gdn_bwd.hip"}
 
 

@@ -417,8 +417,10 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
 
   LAUNCH("gdn_tables", gdn::launch_tables(a, stream));
   LAUNCH("gdn_intra_bwd", gdn::launch_intra(a, 1, stream));
-  if (!full) LAUNCH("gdn_walk_tape", gdn::launch_walk_fwd(a, 0, 1, stream));
-  LAUNCH("gdn_walk_bwd", gdn::launch_walk_bwd(a, stream));
+  // light: the state tape is replayed; the tape walk and the reverse walk are independent and
+  // share one launch. full: the tape is in the saved set.
+  if (!full) LAUNCH("gdn_walk_pair", gdn::launch_walk_pair(a, stream));
+  else LAUNCH("gdn_walk_bwd", gdn::launch_walk_bwd(a, stream));
   if (!p->deterministic) {
     LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
     LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dkacc, (size_t)s.T * s.H * s.D, stream));

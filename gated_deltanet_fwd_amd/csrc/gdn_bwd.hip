@@ -15,17 +15,11 @@
 //   with dGam = mask(dP o Qk) + dL o (beta Kk), db_i = qh_i.(dO S^T)_i - beta_i (Kh S)_i.dX_i,
 //   Z_i = (Kh dSn)_i . R_i; dg is the in-chunk reverse cumulative sum of dG. dq, dk are the
 //   L2-norm backward of the sums of dQh, dKh over the value heads that share the q/k head.
-#include "gdn_device.h"
+#include "gdn_walks.h"
 
 namespace gdn {
 
 static inline hipStream_t S_(void* s) { return reinterpret_cast<hipStream_t>(s); }
-
-__device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (bf16)(s * (float)v[e]);
-  return v;
-}
 
 // ---------------------------------------------------------------------------------------
 // utilities
@@ -149,227 +143,42 @@ int launch_wy_full(const Args& a, void* stream) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Reverse walk, one workgroup per (document, value head), chunks in reverse. Writes the
-// end-state gradient of every chunk (bf16, transposed) and dh0. Same organisation as the forward
-// walk: D / 16 waves, wave w keeps columns [16 w, 16 w + 16) of dS and every per-chunk
-// intermediate in registers, chaining MFMA results into operands by packing alone (k-permuted
-// fragments, with P^T staged column-permuted to match); LDS holds the double-buffered chunk inputs (K, Q pre-scaled by exp(G) rq, dO, A,
-// P^T and per-token factors), one barrier per chunk.
-template <int D>
-constexpr int bwalk_threads() {
-  return 64 * (D / 16);
-}
-
-template <int D>
-struct BWalkSmem {
-  static constexpr int SK = D + 16;
-  static constexpr int SA = CH + 16;
-  bf16 sK[2][CH * SK];
-  bf16 sQ[2][CH * SK];
-  bf16 sdO[2][CH * SK];
-  bf16 sA[2][CH * SA];
-  bf16 sPT[2][CH * SA]; // columns k-permuted
-  // per token: exp(G_last - G) rk, -beta exp(G) rk (zero past the chunk's end); gamma = exp(G_last)
-  float sc[2][2][CH];
-  float sgam[2];
-};
-
+// Reverse walk (body in gdn_walks.h).
 template <int D, typename TI>
 __global__ __launch_bounds__(bwalk_threads<D>(), 1) void k_walk_bwd(Args a) {
-  if (a.status[0]) return;
-  const ChainMap cm = decode_chain(blockIdx.x, a.N, a.H, a.G, 1);
-  if (!cm.valid) return;
-  const int n = a.seq_order[cm.rank];
-  const int j = cm.j, h = j * a.G + cm.gi;
-  const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
-  constexpr int NT = bwalk_threads<D>();
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  constexpr int NRT = D / 16, KD = D / 32, RP = D / 8;
-  constexpr int PPT = CH * RP / NT, APT = CH * 8 / NT;
-  using SM = BWalkSmem<D>;
-  constexpr int SK = SM::SK, SA = SM::SA;
-  __shared__ __attribute__((aligned(16))) SM sm;
-  const TI* kp = (const TI*)a.k;
-  const TI* qp = (const TI*)a.q;
-  const TI* dop = (const TI*)a.dO;
-  const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
-  const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
-  const int v0 = 16 * w;
-  const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
+  __shared__ __attribute__((aligned(16))) BWalkSmem<D> sm;
+  walk_bwd_body<D, TI>(a, blockIdx.x, sm);
+}
 
-  // staging (rows past the chunk's end re-read its last row; the row factors and the q scale are
-  // zero there and P^T is masked, so they contribute nothing)
-  bf16x8 rK[PPT], rQ[PPT], rD[PPT], rA[APT], rP[APT];
-  float rgq[PPT], rrq[PPT];
-  float sg = 0.f, sglast = 0.f, sbeta = 0.f, srk = 0.f;
-  auto load_chunk = [&](int c) {
-    const int t0 = doc_t0 + (c - c_begin) * CH;
-    const int last = min(CH, doc_t1 - t0) - 1;
-    const TI* kc = kp + ((size_t)t0 * a.H + j) * D;
-    const TI* qc = qp + ((size_t)t0 * a.H + j) * D;
-    const TI* dc = dop + ((size_t)t0 * a.HV + h) * D;
-#pragma unroll
-    for (int it = 0; it < PPT; ++it) {
-      const int p = tid + NT * it, row = p / RP, pc = p % RP, rr = min(row, last);
-      rK[it] = IO<TI>::load8(kc + rr * a.H * D + pc * 8);
-      rQ[it] = IO<TI>::load8(qc + rr * a.H * D + pc * 8);
-      rD[it] = IO<TI>::load8(dc + rr * a.HV * D + pc * 8);
-      // Q rows are staged scaled by exp(G) rq (zero past the end; formed in store_chunk, so no
-      // load result is used before the chunk's compute)
-      rgq[it] = a.gcum[(size_t)(t0 + rr) * a.HV + h];
-      rrq[it] = a.rq[(size_t)(t0 + rr) * a.H + j];
-    }
-    const bf16* ac = akk + ((size_t)t0 * a.HV + h) * CH;
-    const bf16* pc_ = pm + ((size_t)c * a.HV + h) * CH * CH;
-#pragma unroll
-    for (int it = 0; it < APT; ++it) {
-      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
-      rA[it] = *reinterpret_cast<const bf16x8*>(ac + min(row, last) * a.HV * CH + pc * 8);
-      rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
-    }
-    {
-      // per-token scalars of row `lane` (every wave loads them; wave 0 stages them)
-      const size_t rv = (size_t)(t0 + min(lane, last)), rl = (size_t)(t0 + last);
-      sg = a.gcum[rv * a.HV + h];
-      sglast = a.gcum[rl * a.HV + h];
-      sbeta = a.beta[rv * a.HV + h];
-      srk = a.rk[rv * a.H + j];
-    }
-  };
-  auto store_chunk = [&](int b, int c) {
-    const int t0 = doc_t0 + (c - c_begin) * CH;
-    const int len = min(CH, doc_t1 - t0);
-#pragma unroll
-    for (int it = 0; it < PPT; ++it) {
-      const int p = tid + NT * it, row = p / RP, pc = p % RP;
-      *reinterpret_cast<bf16x8*>(&sm.sK[b][row * SK + pc * 8]) = rK[it];
-      *reinterpret_cast<bf16x8*>(&sm.sQ[b][row * SK + pc * 8]) = scale8(rQ[it], row < len ? __expf(rgq[it]) * rrq[it] : 0.f);
-      *reinterpret_cast<bf16x8*>(&sm.sdO[b][row * SK + pc * 8]) = rD[it];
-    }
-#pragma unroll
-    for (int it = 0; it < APT; ++it) {
-      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
-      *reinterpret_cast<bf16x8*>(&sm.sA[b][row * SA + pc * 8]) = rA[it];
-      lds_store_kp8(sm.sPT[b], SA, row, pc, rP[it]);
-    }
-    if (w == 0) {
-      const bool ok = lane < len;
-      sm.sc[b][0][lane] = ok ? __expf(sglast - sg) * srk : 0.f;
-      sm.sc[b][1][lane] = ok ? -sbeta * __expf(sg) * srk : 0.f;
-      if (lane == 0) sm.sgam[b] = __expf(sglast);
-    }
-  };
+// Tape walk and reverse walk in one launch. They are independent (the reverse walk never reads
+// the state tape), and each alone leaves CUs idle once the shorter documents' chains finish.
+// Workgroups alternate kinds in super-groups of 8 (document, q/k head) groups, so both walks of a
+// group run on the same XCD (sharing its K tiles in L2), longest documents first.
+template <int D, typename TI>
+__global__ __launch_bounds__(bwalk_threads<D>(), 1) void k_walk_pair(Args a) {
+  static_assert(walk_threads<D>() == bwalk_threads<D>(), "the two walks use the same workgroup size");
+  __shared__ __attribute__((aligned(16))) union U {
+    WalkSmem<D, false> f;
+    BWalkSmem<D> r;
+  } sm;
+  const int SG = 8 * a.G; // workgroups of one super-group of one kind
+  const int b = blockIdx.x, sg = b / (2 * SG), rem = b - sg * 2 * SG;
+  const int kind = rem / SG, blk = sg * SG + (rem - kind * SG);
+  if (kind == 0) walk_fwd_body<D, TI, false, true, false>(a, blk, sm.f);
+  else walk_bwd_body<D, TI>(a, blk, sm.r);
+}
 
-  f32x4 dS[NRT];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 16 * rt + 4 * lg + i;
-      dS[rt][i] = a.dht ? a.dht[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] : 0.f;
-    }
+template <int D, typename TI>
+static int walk_pair_t(const Args& a, hipStream_t s) {
+  const dim3 grid(2 * chain_blocks(a, 1));
+  hipLaunchKernelGGL((k_walk_pair<D, TI>), grid, dim3(bwalk_threads<D>()), 0, s, a);
+  return (int)hipGetLastError();
+}
 
-  auto step = [&](int b, int c) {
-    const bf16* Kt = sm.sK[b];
-    const bf16* Qt = sm.sQ[b];
-    const bf16* Dt = sm.sdO[b];
-    const bf16* At = sm.sA[b];
-    const bf16* PTt = sm.sPT[b];
-    const float* DKs = sm.sc[b][0];
-    const float* YKs = sm.sc[b][1];
-    const float gam = sm.sgam[b];
-
-    bf16x8 sb[KD];
-#pragma unroll
-    for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(dS[2 * kd], dS[2 * kd + 1]);
-    {
-      // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
-      bf16* tp = reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D + (size_t)(v0 + lr) * D + 8 * lg;
-#pragma unroll
-      for (int kd = 0; kd < KD; ++kd) *reinterpret_cast<bf16x8*>(tp + 32 * kd) = sb[kd];
-    }
-    // dO as operands (k = tokens), shared by P^T dO and (Q')^T dO
-    bf16x8 db[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) db[kt] = lds_tr_kp(Dt, SK, 32 * kt, v0);
-    // dR = P^T dO + diag(exp(G_last - G) rk) K dS
-    bf16x8 drb[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x4 dR[2];
-#pragma unroll
-      for (int hm = 0; hm < 2; ++hm) {
-        const int mt = 2 * kt + hm;
-        f32x4 kd_ = zero4(), pd = zero4();
-#pragma unroll
-        for (int kd = 0; kd < KD; ++kd) kd_ = mfma(lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg), sb[kd], kd_);
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) pd = mfma(lds8(PTt, SA, 16 * mt + lr, 32 * k2 + 8 * lg), db[k2], pd);
-        const float4 dk4 = *reinterpret_cast<const float4*>(DKs + 16 * mt + 4 * lg);
-        dR[hm][0] = __builtin_fmaf(dk4.x, kd_[0], pd[0]);
-        dR[hm][1] = __builtin_fmaf(dk4.y, kd_[1], pd[1]);
-        dR[hm][2] = __builtin_fmaf(dk4.z, kd_[2], pd[2]);
-        dR[hm][3] = __builtin_fmaf(dk4.w, kd_[3], pd[3]);
-      }
-      drb[kt] = pack_kp(dR[0], dR[1]);
-    }
-    // -Y' = -diag(beta b rk) A^T dR
-    bf16x8 yb[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x4 Y[2];
-#pragma unroll
-      for (int hm = 0; hm < 2; ++hm) {
-        const int mt = 2 * kt + hm;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(lds_tr_kp(At, SA, 32 * k2, 16 * mt), drb[k2], acc);
-        const float4 y4 = *reinterpret_cast<const float4*>(YKs + 16 * mt + 4 * lg);
-        Y[hm][0] = y4.x * acc[0];
-        Y[hm][1] = y4.y * acc[1];
-        Y[hm][2] = y4.z * acc[2];
-        Y[hm][3] = y4.w * acc[3];
-      }
-      yb[kt] = pack_kp(Y[0], Y[1]);
-    }
-    // dS <- gamma dS + (Q')^T dO - K^T Y'
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      f32x4 acc = dS[rt] * gam;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        acc = mfma(lds_tr_kp(Qt, SK, 32 * kt, 16 * rt), db[kt], acc);
-        acc = mfma(lds_tr_kp(Kt, SK, 32 * kt, 16 * rt), yb[kt], acc);
-      }
-      dS[rt] = acc;
-    }
-  };
-
-  if (c_begin < c_end) {
-    load_chunk(c_end - 1);
-    store_chunk(0, c_end - 1);
-  }
-  __syncthreads();
-  for (int c = c_end - 1; c >= c_begin; --c) {
-    const int b = (c_end - 1 - c) & 1;
-    // the next chunk in reverse (the first one again at the end, staged into the idle buffer)
-    const int cn = max(c - 1, c_begin);
-    load_chunk(cn);
-    __builtin_amdgcn_sched_barrier(0); // keep every prefetch load ahead of the chunk's compute
-    step(b, c);
-    store_chunk(b ^ 1, cn);
-    __syncthreads();
-  }
-  if (a.dh0) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 16 * rt + 4 * lg + i;
-        a.dh0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] = dS[rt][i];
-      }
-  }
+int launch_walk_pair(const Args& a, void* stream) {
+  const hipStream_t s = S_(stream);
+  if (a.D == 128) return a.dtype == 0 ? walk_pair_t<128, bf16>(a, s) : walk_pair_t<128, float>(a, s);
+  return a.dtype == 0 ? walk_pair_t<64, bf16>(a, s) : walk_pair_t<64, float>(a, s);
 }
 
 template <int D, typename TI>

@@ -65,6 +65,7 @@ int chain_blocks(const Args& a, int ntile);
 int launch_tables(const Args& a, void* stream);
 int launch_intra(const Args& a, int bwd_prep, void* stream);
 int launch_walk_fwd(const Args& a, int write_o, int write_tape, void* stream);
+int launch_walk_pair(const Args& a, void* stream); // tape walk and reverse walk in one launch
 int launch_wy_full(const Args& a, void* stream);
 int launch_walk_bwd(const Args& a, void* stream);
 int launch_chunk_grad(const Args& a, int deterministic, void* stream);

@@ -1,0 +1,516 @@
+// State walks of the chunked gated delta rule on gfx950 (bodies shared by the forward, tape,
+// reverse and paired launches).
+#pragma once
+#include "gdn_device.h"
+
+namespace gdn {
+
+__device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)(s * (float)v[e]);
+  return v;
+}
+
+// ---------------------------------------------------------------------------------------
+// State walk, one workgroup per (document, value head); chunks in order.
+// WRITE_O: write o (and ht). WRITE_TAPE: write the chunk-start state tape (bf16, transposed).
+// FULL: also write v_new = R.
+//
+// D / 16 waves; wave w owns value columns [16 w, 16 w + 16) of the state and keeps them, and
+// every per-chunk intermediate (K S, X, R, the output), in registers. Results of one MFMA become
+// operands of the next by packing alone (k-permuted fragments; A and P are staged with their
+// columns permuted to match, so every row fragment is one 16-byte read), and the state, in
+// natural key order, is the B operand of K S and the A operand of (Q S)^T. The output is formed transposed, so a lane holds four
+// consecutive values of one token's row. The waves never exchange data; LDS holds only the
+// chunk's shared inputs (K, Q, V, A, P and per-token factors), double-buffered, so the next chunk
+// is staged while this one computes, with one barrier per chunk.
+template <int D>
+constexpr int walk_threads() {
+  return 64 * (D / 16);
+}
+
+template <int D, bool WRITE_O>
+struct WalkSmem {
+  static constexpr int SK = D + 16; // token rows of K, Q, V
+  static constexpr int SA = CH + 16; // token rows of A and P, columns k-permuted
+  static constexpr int NQ = WRITE_O ? 2 : 1;
+  static constexpr int LQ = WRITE_O ? CH * SK : 8;
+  static constexpr int LP = WRITE_O ? CH * SA : 8;
+  bf16 sK[2][CH * SK];
+  bf16 sV[2][CH * SK];
+  bf16 sA[2][CH * SA];
+  bf16 sQ[NQ][LQ];
+  bf16 sP[NQ][LP];
+  // per token: exp(G) rk, beta, exp(G_last - G) rk, exp(G) rq (zero past the chunk's end);
+  // gamma = exp(G_last)
+  float sc[2][4][CH];
+  float sgam[2];
+};
+
+template <int D, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL>
+__device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D, WRITE_O>& sm) {
+  if (a.status[0]) return;
+  const ChainMap cm = decode_chain(blk, a.N, a.H, a.G, 1);
+  if (!cm.valid) return;
+  const int n = a.seq_order[cm.rank];
+  const int j = cm.j, h = j * a.G + cm.gi;
+  const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
+  constexpr int NT = walk_threads<D>();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  constexpr int NRT = D / 16;       // state row tiles (key dim)
+  constexpr int KD = D / 32;        // k-steps over the key dim
+  constexpr int RP = D / 8;         // 16-byte pieces per token row of K, Q, V
+  constexpr int PPT = CH * RP / NT; // pieces per thread of a 64 x D token tile (2)
+  constexpr int APT = CH * 8 / NT;  // pieces per thread of a 64 x 64 tile
+  using SM = WalkSmem<D, WRITE_O>;
+  constexpr int SK = SM::SK, SA = SM::SA;
+  const TI* kp = (const TI*)a.k;
+  const TI* qp = (const TI*)a.q;
+  const TI* vp = (const TI*)a.v;
+  const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
+  const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
+  const int v0 = 16 * w;
+  // chunk c of the document starts at token cu[n] + 64 (c - c_begin)
+  const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
+
+  // ---- staging: global -> registers (issued before a chunk's compute) -> LDS (after it).
+  // Rows past the chunk's end re-read its last row: finite values whose contributions vanish
+  // because beta and the row factors are zero there and P is masked.
+  bf16x8 rK[PPT], rV[PPT], rQ[PPT], rA[APT], rP[APT];
+  float sg = 0.f, sglast = 0.f, sbeta = 0.f, srk = 0.f, srq = 0.f;
+  auto load_chunk = [&](int c) {
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int last = min(CH, doc_t1 - t0) - 1;
+    const TI* kc = kp + ((size_t)t0 * a.H + j) * D;
+    const TI* qc = qp + ((size_t)t0 * a.H + j) * D;
+    const TI* vc = vp + ((size_t)t0 * a.HV + h) * D;
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + NT * it, row = min(p / RP, last), pc = p % RP;
+      rK[it] = IO<TI>::load8(kc + row * a.H * D + pc * 8);
+      rV[it] = IO<TI>::load8(vc + row * a.HV * D + pc * 8);
+      if (WRITE_O) rQ[it] = IO<TI>::load8(qc + row * a.H * D + pc * 8);
+    }
+    const bf16* ac = akk + ((size_t)t0 * a.HV + h) * CH;
+    const bf16* pc_ = pm + ((size_t)c * a.HV + h) * CH * CH;
+#pragma unroll
+    for (int it = 0; it < APT; ++it) {
+      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+      rA[it] = *reinterpret_cast<const bf16x8*>(ac + min(row, last) * a.HV * CH + pc * 8);
+      if (WRITE_O) rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
+    }
+    {
+      // per-token scalars of row `lane` (every wave loads them; wave 0 stages them)
+      const size_t rv = (size_t)(t0 + min(lane, last)), rl = (size_t)(t0 + last);
+      sg = a.gcum[rv * a.HV + h];
+      sglast = a.gcum[rl * a.HV + h];
+      sbeta = a.beta[rv * a.HV + h];
+      srk = a.rk[rv * a.H + j];
+      if (WRITE_O) srq = a.rq[rv * a.H + j];
+    }
+  };
+  auto store_chunk = [&](int b, int c) {
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int len = min(CH, doc_t1 - t0);
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + NT * it, row = p / RP, pc = p % RP;
+      *reinterpret_cast<bf16x8*>(&sm.sK[b][row * SK + pc * 8]) = rK[it];
+      *reinterpret_cast<bf16x8*>(&sm.sV[b][row * SK + pc * 8]) = rV[it];
+      if (WRITE_O) *reinterpret_cast<bf16x8*>(&sm.sQ[b][row * SK + pc * 8]) = rQ[it];
+    }
+#pragma unroll
+    for (int it = 0; it < APT; ++it) {
+      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+      lds_store_kp8(sm.sA[b], SA, row, pc, rA[it]);
+      if (WRITE_O) lds_store_kp8(sm.sP[b], SA, row, pc, rP[it]);
+    }
+    if (w == 0) {
+      const bool ok = lane < len;
+      const float eb = __expf(sg);
+      sm.sc[b][0][lane] = ok ? eb * srk : 0.f;
+      sm.sc[b][1][lane] = ok ? sbeta : 0.f;
+      sm.sc[b][2][lane] = ok ? __expf(sglast - sg) * srk : 0.f;
+      if (WRITE_O) sm.sc[b][3][lane] = ok ? eb * srq : 0.f;
+      if (lane == 0) sm.sgam[b] = __expf(sglast);
+    }
+  };
+
+  // ---- state: rows 16 rt + 4 lg + i (key), column v0 + lr (value)
+  f32x4 S[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * rt + 4 * lg + i;
+      S[rt][i] = a.has_h0 ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] : 0.f;
+    }
+
+  auto step = [&](int b, int c) {
+    const bf16* Kt = sm.sK[b];
+    const bf16* Vt = sm.sV[b];
+    const bf16* At = sm.sA[b];
+    const bf16* Qt = sm.sQ[WRITE_O ? b : 0];
+    const bf16* Pt = sm.sP[WRITE_O ? b : 0];
+    const float* BKs = sm.sc[b][0];
+    const float* Bs = sm.sc[b][1];
+    const float* DKs = sm.sc[b][2];
+    const float* BQs = sm.sc[b][3];
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int len = min(CH, doc_t1 - t0);
+    const float gam = sm.sgam[b];
+
+    // the state as operands in natural key order (k = key dim)
+    bf16x8 sb[KD];
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(S[2 * kd], S[2 * kd + 1]);
+    if (WRITE_TAPE) {
+      // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
+      bf16* tp = reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D + (size_t)(v0 + lr) * D + 8 * lg;
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) *reinterpret_cast<bf16x8*>(tp + 32 * kd) = sb[kd];
+    }
+    // K S (64 tokens x 16 columns) and (Q S)^T (16 columns x 64 tokens)
+    f32x4 ks[4], qsT[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) ks[mt] = qsT[mt] = zero4();
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        ks[mt] = mfma(lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg), sb[kd], ks[mt]);
+        if (WRITE_O) qsT[mt] = mfma(sb[kd], lds8(Qt, SK, 16 * mt + lr, 32 * kd + 8 * lg), qsT[mt]);
+      }
+    // X = diag(beta) (V - diag(b rk) K S)
+    bf16x8 xb[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 X[2];
+#pragma unroll
+      for (int hm = 0; hm < 2; ++hm) {
+        const int mt = 2 * kt + hm, r0 = 16 * mt + 4 * lg;
+        const float4 bk4 = *reinterpret_cast<const float4*>(BKs + r0);
+        const float4 be4 = *reinterpret_cast<const float4*>(Bs + r0);
+        const float bk[4] = {bk4.x, bk4.y, bk4.z, bk4.w}, be[4] = {be4.x, be4.y, be4.z, be4.w};
+        const bf16x4 vv = lds_tr4c(Vt, SK, 16 * mt, v0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[hm][i] = be[i] * __builtin_fmaf(-bk[i], ks[mt][i], (float)vv[i]);
+      }
+      xb[kt] = pack_kp(X[0], X[1]);
+    }
+    // R = A X
+    f32x4 R[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      R[mt] = zero4();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) R[mt] = mfma(lds8(At, SA, 16 * mt + lr, 32 * kt + 8 * lg), xb[kt], R[mt]);
+    }
+    if (FULL) {
+      // rows past the chunk's end go to the discard area (no branch around the stores)
+      bf16* vn = reinterpret_cast<bf16*>(a.vnew) + ((size_t)t0 * a.HV + h) * D + v0 + lr;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * lg + i;
+          bf16* dst = r < len ? vn + (size_t)r * a.HV * D : reinterpret_cast<bf16*>(a.discard) + lane;
+          *dst = (bf16)R[mt][i];
+        }
+    }
+    // operands of R (for (P R)^T) and of diag(exp(G_last - G) rk) R (for the state update)
+    bf16x8 rb[2], rdb[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if (WRITE_O) rb[kt] = pack_kp(R[2 * kt], R[2 * kt + 1]);
+      f32x4 d[2];
+#pragma unroll
+      for (int hm = 0; hm < 2; ++hm) {
+        const float4 dk4 = *reinterpret_cast<const float4*>(DKs + 16 * (2 * kt + hm) + 4 * lg);
+        d[hm][0] = dk4.x * R[2 * kt + hm][0];
+        d[hm][1] = dk4.y * R[2 * kt + hm][1];
+        d[hm][2] = dk4.z * R[2 * kt + hm][2];
+        d[hm][3] = dk4.w * R[2 * kt + hm][3];
+      }
+      rdb[kt] = pack_kp(d[0], d[1]);
+    }
+    // O^T = diag-column(b rq) (Q S)^T + (P R)^T; lane holds O[t][v0 + 4 lg .. +3], t = 16 mt + lr
+    if (WRITE_O) {
+      TI* op = (TI*)a.o + ((size_t)t0 * a.HV + h) * D + v0 + 4 * lg;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) acc = mfma(rb[kt], lds8(Pt, SA, 16 * mt + lr, 32 * kt + 8 * lg), acc);
+        const int t = 16 * mt + lr;
+        const float sq = BQs[t];
+        float ov[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = __builtin_fmaf(sq, qsT[mt][i], acc[i]);
+        // tokens past the chunk's end go to the discard area: every lane stores, so no branch
+        // hides the number of outstanding stores from the wait counts
+        IO<TI>::store4(t < len ? op + (size_t)t * a.HV * D : reinterpret_cast<TI*>(a.discard) + 4 * lane, ov);
+      }
+    }
+    // S <- gamma S + K^T diag(exp(G_last - G) rk) R
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x4 acc = S[rt] * gam;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc = mfma(lds_tr_kp(Kt, SK, 32 * kt, 16 * rt), rdb[kt], acc);
+      S[rt] = acc;
+    }
+  };
+
+  if (c_begin < c_end) {
+    load_chunk(c_begin);
+    store_chunk(0, c_begin);
+  }
+  __syncthreads();
+  for (int c = c_begin; c < c_end; ++c) {
+    const int b = (c - c_begin) & 1;
+    // the next chunk (the last one again at the end: staged into the idle buffer, never read);
+    // unconditional, so the loads stay in flight across the whole step
+    const int cn = min(c + 1, c_end - 1);
+    load_chunk(cn);
+    __builtin_amdgcn_sched_barrier(0); // keep every prefetch load ahead of the chunk's compute
+    step(b, c);
+    store_chunk(b ^ 1, cn);
+    __syncthreads();
+  }
+  if (WRITE_O && a.want_ht) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * rt + 4 * lg + i;
+        a.ht[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] = S[rt][i];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Reverse walk, one workgroup per (document, value head), chunks in reverse. Writes the
+// end-state gradient of every chunk (bf16, transposed) and dh0. Same organisation as the forward
+// walk: D / 16 waves, wave w keeps columns [16 w, 16 w + 16) of dS and every per-chunk
+// intermediate in registers, chaining MFMA results into operands by packing alone (k-permuted
+// fragments, with P^T staged column-permuted to match); LDS holds the double-buffered chunk inputs (K, Q pre-scaled by exp(G) rq, dO, A,
+// P^T and per-token factors), one barrier per chunk.
+template <int D>
+constexpr int bwalk_threads() {
+  return 64 * (D / 16);
+}
+
+template <int D>
+struct BWalkSmem {
+  static constexpr int SK = D + 16;
+  static constexpr int SA = CH + 16;
+  bf16 sK[2][CH * SK];
+  bf16 sQ[2][CH * SK];
+  bf16 sdO[2][CH * SK];
+  bf16 sA[2][CH * SA];
+  bf16 sPT[2][CH * SA]; // columns k-permuted
+  // per token: exp(G_last - G) rk, -beta exp(G) rk (zero past the chunk's end); gamma = exp(G_last)
+  float sc[2][2][CH];
+  float sgam[2];
+};
+
+template <int D, typename TI>
+__device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<D>& sm) {
+  if (a.status[0]) return;
+  const ChainMap cm = decode_chain(blk, a.N, a.H, a.G, 1);
+  if (!cm.valid) return;
+  const int n = a.seq_order[cm.rank];
+  const int j = cm.j, h = j * a.G + cm.gi;
+  const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
+  constexpr int NT = bwalk_threads<D>();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  constexpr int NRT = D / 16, KD = D / 32, RP = D / 8;
+  constexpr int PPT = CH * RP / NT, APT = CH * 8 / NT;
+  using SM = BWalkSmem<D>;
+  constexpr int SK = SM::SK, SA = SM::SA;
+  const TI* kp = (const TI*)a.k;
+  const TI* qp = (const TI*)a.q;
+  const TI* dop = (const TI*)a.dO;
+  const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
+  const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
+  const int v0 = 16 * w;
+  const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
+
+  // staging (rows past the chunk's end re-read its last row; the row factors and the q scale are
+  // zero there and P^T is masked, so they contribute nothing)
+  bf16x8 rK[PPT], rQ[PPT], rD[PPT], rA[APT], rP[APT];
+  float rgq[PPT], rrq[PPT];
+  float sg = 0.f, sglast = 0.f, sbeta = 0.f, srk = 0.f;
+  auto load_chunk = [&](int c) {
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int last = min(CH, doc_t1 - t0) - 1;
+    const TI* kc = kp + ((size_t)t0 * a.H + j) * D;
+    const TI* qc = qp + ((size_t)t0 * a.H + j) * D;
+    const TI* dc = dop + ((size_t)t0 * a.HV + h) * D;
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + NT * it, row = p / RP, pc = p % RP, rr = min(row, last);
+      rK[it] = IO<TI>::load8(kc + rr * a.H * D + pc * 8);
+      rQ[it] = IO<TI>::load8(qc + rr * a.H * D + pc * 8);
+      rD[it] = IO<TI>::load8(dc + rr * a.HV * D + pc * 8);
+      // Q rows are staged scaled by exp(G) rq (zero past the end; formed in store_chunk, so no
+      // load result is used before the chunk's compute)
+      rgq[it] = a.gcum[(size_t)(t0 + rr) * a.HV + h];
+      rrq[it] = a.rq[(size_t)(t0 + rr) * a.H + j];
+    }
+    const bf16* ac = akk + ((size_t)t0 * a.HV + h) * CH;
+    const bf16* pc_ = pm + ((size_t)c * a.HV + h) * CH * CH;
+#pragma unroll
+    for (int it = 0; it < APT; ++it) {
+      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+      rA[it] = *reinterpret_cast<const bf16x8*>(ac + min(row, last) * a.HV * CH + pc * 8);
+      rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
+    }
+    {
+      // per-token scalars of row `lane` (every wave loads them; wave 0 stages them)
+      const size_t rv = (size_t)(t0 + min(lane, last)), rl = (size_t)(t0 + last);
+      sg = a.gcum[rv * a.HV + h];
+      sglast = a.gcum[rl * a.HV + h];
+      sbeta = a.beta[rv * a.HV + h];
+      srk = a.rk[rv * a.H + j];
+    }
+  };
+  auto store_chunk = [&](int b, int c) {
+    const int t0 = doc_t0 + (c - c_begin) * CH;
+    const int len = min(CH, doc_t1 - t0);
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + NT * it, row = p / RP, pc = p % RP;
+      *reinterpret_cast<bf16x8*>(&sm.sK[b][row * SK + pc * 8]) = rK[it];
+      *reinterpret_cast<bf16x8*>(&sm.sQ[b][row * SK + pc * 8]) = scale8(rQ[it], row < len ? __expf(rgq[it]) * rrq[it] : 0.f);
+      *reinterpret_cast<bf16x8*>(&sm.sdO[b][row * SK + pc * 8]) = rD[it];
+    }
+#pragma unroll
+    for (int it = 0; it < APT; ++it) {
+      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+      *reinterpret_cast<bf16x8*>(&sm.sA[b][row * SA + pc * 8]) = rA[it];
+      lds_store_kp8(sm.sPT[b], SA, row, pc, rP[it]);
+    }
+    if (w == 0) {
+      const bool ok = lane < len;
+      sm.sc[b][0][lane] = ok ? __expf(sglast - sg) * srk : 0.f;
+      sm.sc[b][1][lane] = ok ? -sbeta * __expf(sg) * srk : 0.f;
+      if (lane == 0) sm.sgam[b] = __expf(sglast);
+    }
+  };
+
+  f32x4 dS[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * rt + 4 * lg + i;
+      dS[rt][i] = a.dht ? a.dht[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] : 0.f;
+    }
+
+  auto step = [&](int b, int c) {
+    const bf16* Kt = sm.sK[b];
+    const bf16* Qt = sm.sQ[b];
+    const bf16* Dt = sm.sdO[b];
+    const bf16* At = sm.sA[b];
+    const bf16* PTt = sm.sPT[b];
+    const float* DKs = sm.sc[b][0];
+    const float* YKs = sm.sc[b][1];
+    const float gam = sm.sgam[b];
+
+    bf16x8 sb[KD];
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(dS[2 * kd], dS[2 * kd + 1]);
+    {
+      // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
+      bf16* tp = reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D + (size_t)(v0 + lr) * D + 8 * lg;
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) *reinterpret_cast<bf16x8*>(tp + 32 * kd) = sb[kd];
+    }
+    // dO as operands (k = tokens), shared by P^T dO and (Q')^T dO
+    bf16x8 db[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) db[kt] = lds_tr_kp(Dt, SK, 32 * kt, v0);
+    // dR = P^T dO + diag(exp(G_last - G) rk) K dS
+    bf16x8 drb[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 dR[2];
+#pragma unroll
+      for (int hm = 0; hm < 2; ++hm) {
+        const int mt = 2 * kt + hm;
+        f32x4 kd_ = zero4(), pd = zero4();
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd) kd_ = mfma(lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg), sb[kd], kd_);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) pd = mfma(lds8(PTt, SA, 16 * mt + lr, 32 * k2 + 8 * lg), db[k2], pd);
+        const float4 dk4 = *reinterpret_cast<const float4*>(DKs + 16 * mt + 4 * lg);
+        dR[hm][0] = __builtin_fmaf(dk4.x, kd_[0], pd[0]);
+        dR[hm][1] = __builtin_fmaf(dk4.y, kd_[1], pd[1]);
+        dR[hm][2] = __builtin_fmaf(dk4.z, kd_[2], pd[2]);
+        dR[hm][3] = __builtin_fmaf(dk4.w, kd_[3], pd[3]);
+      }
+      drb[kt] = pack_kp(dR[0], dR[1]);
+    }
+    // -Y' = -diag(beta b rk) A^T dR
+    bf16x8 yb[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 Y[2];
+#pragma unroll
+      for (int hm = 0; hm < 2; ++hm) {
+        const int mt = 2 * kt + hm;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(lds_tr_kp(At, SA, 32 * k2, 16 * mt), drb[k2], acc);
+        const float4 y4 = *reinterpret_cast<const float4*>(YKs + 16 * mt + 4 * lg);
+        Y[hm][0] = y4.x * acc[0];
+        Y[hm][1] = y4.y * acc[1];
+        Y[hm][2] = y4.z * acc[2];
+        Y[hm][3] = y4.w * acc[3];
+      }
+      yb[kt] = pack_kp(Y[0], Y[1]);
+    }
+    // dS <- gamma dS + (Q')^T dO - K^T Y'
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x4 acc = dS[rt] * gam;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        acc = mfma(lds_tr_kp(Qt, SK, 32 * kt, 16 * rt), db[kt], acc);
+        acc = mfma(lds_tr_kp(Kt, SK, 32 * kt, 16 * rt), yb[kt], acc);
+      }
+      dS[rt] = acc;
+    }
+  };
+
+  if (c_begin < c_end) {
+    load_chunk(c_end - 1);
+    store_chunk(0, c_end - 1);
+  }
+  __syncthreads();
+  for (int c = c_end - 1; c >= c_begin; --c) {
+    const int b = (c_end - 1 - c) & 1;
+    // the next chunk in reverse (the first one again at the end, staged into the idle buffer)
+    const int cn = max(c - 1, c_begin);
+    load_chunk(cn);
+    __builtin_amdgcn_sched_barrier(0); // keep every prefetch load ahead of the chunk's compute
+    step(b, c);
+    store_chunk(b ^ 1, cn);
+    __syncthreads();
+  }
+  if (a.dh0) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * rt + 4 * lg + i;
+        a.dh0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] = dS[rt][i];
+      }
+  }
+}
+
+} // namespace gdn
