@@ -11,7 +11,7 @@ checkpointed (fwd + recompute + bwd) rates, the roofline of the dominant kernel 
 per-launch duration measured by HIP events on the launch stream during the timed region, and
 the FP64 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload pack262k] [--deterministic]
+    python bench.py [--steps K] [--warmup W] [--workload pack262k] [--atomic]
                     [--no-cpu-baseline] [--gpus 1]
 """
 from __future__ import annotations
@@ -245,7 +245,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="pack262k")
-    ap.add_argument("--deterministic", action="store_true", help="deterministic dq/dk reduction")
+    ap.add_argument("--atomic", action="store_true",
+                    help="float-atomic dq/dk reduction (default: the deterministic fixed-order reduction)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fwd-only and ckpt timings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -278,7 +279,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = syn.make_inputs(w, device=dev)
-    det = bool(args.deterministic)
+    det = not args.atomic
     p = G.problem_for(w, save_mode=G.SAVE_LIGHT, deterministic=det)
     saved = torch.empty(G.gdn_saved_bytes(p), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(G.gdn_workspace_bytes(p, G.OP_FWD), dtype=torch.uint8, device=dev)

@@ -218,6 +218,8 @@ struct GradSmem {
   bf16 sA[CH * SA];
   float sG[CH], sB[CH], srk[CH], srq[CH];
   float sRow[2][4][CH];
+  float sRowM[2][CH]; // per column half: row sums of dGam o Gam
+  float sCol[4][CH];  // per row tile: column sums of dGam o Gam
   float sred[8];
   union U {
     struct Sl {
@@ -231,10 +233,11 @@ struct GradSmem {
       bf16 sdXT[DC * SA];
     } b;
     struct Tl {
-      float sM[CH][CH + 1];
       bf16 sT1t[CH * SA];
       bf16 sT2[CH * SA];
-      bf16 sT3[CH * SA];
+      bf16 sT3[CH * SA];  // dA^T, then M1^T
+      bf16 sE1t[CH * SA]; // (dKk diag(rk))^T
+      bf16 sE2[CH * SA];  // dKk^T diag(rk), row-major
     } t;
   } u;
 };
@@ -462,13 +465,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     auto& T = sm.u.t;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      zp[i] = sum16(zp[i]);
-      dbx[i] = sum16(dbx[i]);
-      dbr[i] = sum16(dbr[i]);
-      dbo[i] = sum16(dbo[i]);
+      zp[i] = row_sum16(zp[i]);
+      dbx[i] = row_sum16(dbx[i]);
+      dbr[i] = row_sum16(dbr[i]);
+      dbo[i] = row_sum16(dbo[i]);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sdot += __shfl_xor(sdot, off);
+    sdot = col_sum4(row_sum16(sdot));
     __syncthreads(); // slice tiles are dead: the union switches to the tail layout
     if (lane == 0) sm.sred[w] = sdot;
     if (lr == 0) {
@@ -518,51 +520,56 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       lds_store4_t(T.sT3, SA, 16 * ct + lr, row0 + lg * 4, m1[c2][0], m1[c2][1], m1[c2][2], m1[c2][3]); // M1^T
     }
     __syncthreads();
-    // dL = -A^T M1 (strictly lower)
-    float dbl[4] = {0.f, 0.f, 0.f, 0.f}, dkk[2][4];
+    // dL = -A^T M1 (strictly lower); dKk = dL o (beta Gam) goes to two tiles, one per term of
+    // (dKk + dKk^T) diag(rk); row and column sums of dGam o Gam are reduced per wave (DPP rows,
+    // lane-group columns) into per-half and per-row-tile partials
+    float dbl[4] = {0.f, 0.f, 0.f, 0.f}, rsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int ct = 2 * half + c2, cc = 16 * ct + lr;
+      const float rkc = sm.srk[cc];
       f32x4 acc = zero4();
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
         acc = mfma(lds_tr8(sm.sA, SA, k2 * 32, row0), lds8(T.sT3, SA, 16 * ct + lr, k2 * 32 + lg * 8), acc);
+      float e1[4], e2[4], csum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i;
         const float dl = r > cc ? -acc[i] : 0.f;
         dbl[i] += dl * gm[c2][i] * Kk[c2][i];
-        dkk[c2][i] = dl * beta_r[i] * gm[c2][i];
+        const float dkk = dl * beta_r[i] * gm[c2][i];
         dgam[c2][i] += dl * beta_r[i] * Kk[c2][i];
-        T.sM[r][cc] = dgam[c2][i] * gm[c2][i];
+        const float mm = dgam[c2][i] * gm[c2][i];
+        rsum[i] += mm;
+        csum += mm;
+        e1[i] = dkk * rkc;     // (dKk diag(rk))[r][cc], stored transposed
+        e2[i] = dkk * rk_r[i]; // (dKk^T diag(rk))[cc][r]
       }
+      csum = col_sum4(csum);
+      if (lg == 0) sm.sCol[rt][cc] = csum;
+      lds_store4_t(T.sE1t, SA, cc, row0 + lg * 4, e1[0], e1[1], e1[2], e1[3]);
+      lds_store4_t(T.sE2, SA, cc, row0 + lg * 4, e2[0], e2[1], e2[2], e2[3]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dbl[i] = sum16(dbl[i]);
+    for (int i = 0; i < 4; ++i) {
+      dbl[i] = row_sum16(dbl[i]);
+      rsum[i] = row_sum16(rsum[i]);
+    }
     if (lr == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.sRow[half][3][row0 + lg * 4 + i] = dbl[i];
-    }
-    __syncthreads(); // done reading M1^T
-    // dKs = dKk + dKk^T (symmetric, zero diagonal), columns scaled by rk
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = row0 + lg * 4 + i, cc = 16 * (2 * half + c2) + lr;
-        if (r > cc) {
-          T.sT3[r * SA + cc] = (bf16)(dkk[c2][i] * sm.srk[cc]);
-          T.sT3[cc * SA + r] = (bf16)(dkk[c2][i] * sm.srk[r]);
-        } else if (r == cc) {
-          T.sT3[r * SA + r] = (bf16)0.f;
-        }
+        sm.sRow[half][3][row0 + lg * 4 + i] = dbl[i];
+        sm.sRowM[half][row0 + lg * 4 + i] = rsum[i];
       }
+    }
     __syncthreads();
     // dQh += (dQk rk) K ; dKh += (dQk rq)^T Q + (dKs rk) K
     {
       const bf16x8 a1[2] = {lds_tr8(T.sT1t, SA, 0, row0), lds_tr8(T.sT1t, SA, 32, row0)};
       const bf16x8 a2[2] = {lds8(T.sT2, SA, arow, lg * 8), lds8(T.sT2, SA, arow, 32 + lg * 8)};
-      const bf16x8 a3[2] = {lds8(T.sT3, SA, arow, lg * 8), lds8(T.sT3, SA, arow, 32 + lg * 8)};
+      const bf16x8 e1[2] = {lds_tr8(T.sE1t, SA, 0, row0), lds_tr8(T.sE1t, SA, 32, row0)};
+      const bf16x8 e2[2] = {lds8(T.sE2, SA, arow, lg * 8), lds8(T.sE2, SA, arow, 32 + lg * 8)};
 #pragma unroll
       for (int t = 0; t < NT2; ++t) {
         const int dcol = 16 * (half * NT2 + t);
@@ -571,26 +578,22 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
           const bf16x8 bK = lds_tr8(sm.sK, SK, k2 * 32, dcol);
           dQacc[t] = mfma(a1[k2], bK, dQacc[t]);
           dKacc[t] = mfma(a2[k2], lds_tr8(sm.sQ, SK, k2 * 32, dcol), dKacc[t]);
-          dKacc[t] = mfma(a3[k2], bK, dKacc[t]);
+          dKacc[t] = mfma(e1[k2], bK, dKacc[t]);
+          dKacc[t] = mfma(e2[k2], bK, dKacc[t]);
         }
       }
     }
     if (w == 0) {
       const int r = lane;
-      float rows = 0.f, cols = 0.f;
-      for (int x = 0; x < CH; ++x) {
-        rows += T.sM[r][x];
-        cols += T.sM[x][r];
-      }
+      const float rows = sm.sRowM[0][r] + sm.sRowM[1][r];
+      const float cols = sm.sCol[0][r] + sm.sCol[1][r] + sm.sCol[2][r] + sm.sCol[3][r];
       const bool ok = r < len;
       const float dec = ok ? __expf(glast - sm.sG[r]) : 0.f;
       const float z = sm.sRow[0][0][r] + sm.sRow[1][0][r];
       const float db = sm.sRow[0][1][r] + sm.sRow[1][1][r];
       const float dbeta = sm.sRow[0][2][r] + sm.sRow[1][2][r] + sm.sRow[0][3][r] + sm.sRow[1][3][r];
       const float zd = ok ? z * dec : 0.f;
-      float zsum = zd;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) zsum += __shfl_xor(zsum, off);
+      const float zsum = col_sum4(row_sum16(zd));
       float dG = ok ? rows - cols + __expf(sm.sG[r]) * db - zd : 0.f;
       float sd = 0.f;
 #pragma unroll
@@ -637,8 +640,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qd[i] = sum16(qd[i]);
-        kd[i] = sum16(kd[i]);
+        qd[i] = row_sum16(qd[i]);
+        kd[i] = row_sum16(kd[i]);
       }
       __syncthreads();
       if (lr == 0) {
