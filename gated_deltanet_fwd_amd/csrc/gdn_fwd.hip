@@ -125,6 +125,12 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
   const TI* kp = (const TI*)a.k;
   const TI* qp = (const TI*)a.q;
 
+  // the first batch's per-token g and beta (backward: gcum) of this wave's value head, loaded
+  // together with K and Q so that their latencies overlap
+  const int h_pre = j * a.G + min(w, a.G - 1), r_pre = t0 + min(lane, len - 1);
+  const float pre_g = BWD ? a.gcum[(size_t)r_pre * a.HV + h_pre] : a.g[(size_t)r_pre * a.HV + h_pre];
+  const float pre_b = BWD ? 0.f : a.beta[(size_t)r_pre * a.HV + h_pre];
+
   // this wave's 16 rows of K and Q (MFMA A fragments), their squared norms
   const int ar = 16 * w + lr;
   const bool ok = ar < len;
@@ -196,11 +202,12 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
     if (w < nb) {
       const int h = j * a.G + hb + w, r = lane;
       float x;
+      const size_t rr = (size_t)(t0 + min(r, len - 1)) * a.HV + h;
       if (BWD) {
-        x = r < len ? a.gcum[(size_t)(t0 + r) * a.HV + h] : 0.f;
+        x = r < len ? (hb == 0 ? pre_g : a.gcum[rr]) : 0.f;
       } else {
-        const float gv = r < len ? a.g[(size_t)(t0 + r) * a.HV + h] : 0.f;
-        const float bv = r < len ? a.beta[(size_t)(t0 + r) * a.HV + h] : 0.f;
+        const float gv = r < len ? (hb == 0 ? pre_g : a.g[rr]) : 0.f;
+        const float bv = r < len ? (hb == 0 ? pre_b : a.beta[rr]) : 0.f;
         x = gv;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
