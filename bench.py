@@ -94,8 +94,13 @@ def step_roofline(T, HV, D, io_bytes):
 
 
 def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source file and every header beside it (the kernels include them)."""
+    import glob
+    h = hashlib.sha256()
+    for p in [path] + sorted(glob.glob(os.path.join(os.path.dirname(path), "*.h"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel, workload):
