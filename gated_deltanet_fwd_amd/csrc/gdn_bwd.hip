@@ -221,6 +221,7 @@ struct GradSmem {
   float sRowM[2][CH]; // per column half: row sums of dGam o Gam
   float sCol[4][CH];  // per row tile: column sums of dGam o Gam
   float sred[8];
+  f32x4 sKQ[2][8][2][64]; // Kk, Qk: each wave's own C tiles, parked for the per-head tails
   union U {
     struct Sl {
       bf16 sS[DC * SK];
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   const int j = DET ? (int)blockIdx.y : (int)blockIdx.y / a.G;
   const int h_first = DET ? j * a.G : (int)blockIdx.y;
   const int h_count = DET ? a.G : 1;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rt = w & 3, half = w >> 2;
   const int lr = lane & 15, lg = lane >> 4;
   const int row0 = 16 * rt;      // rows of this wave's product tiles
@@ -289,30 +290,28 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     sm.srq[tid] = ok ? a.rq[(size_t)(t0 + tid) * a.H + j] : 0.f;
   }
   __syncthreads();
-  f32x4 Kk[2], Qk[2];
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    Kk[c2] = Qk[c2] = zero4();
+    f32x4 Kk = zero4(), Qk = zero4();
     const int ct = 2 * half + c2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 bk = lds8(sm.sK, SK, 16 * ct + lr, ks * 32 + lg * 8);
-      Kk[c2] = mfma(lds8(sm.sK, SK, arow, ks * 32 + lg * 8), bk, Kk[c2]);
-      Qk[c2] = mfma(lds8(sm.sQ, SK, arow, ks * 32 + lg * 8), bk, Qk[c2]);
+      Kk = mfma(lds8(sm.sK, SK, arow, ks * 32 + lg * 8), bk, Kk);
+      Qk = mfma(lds8(sm.sQ, SK, arow, ks * 32 + lg * 8), bk, Qk);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = row0 + lg * 4 + i, cc = 16 * ct + lr;
-      Kk[c2][i] *= sm.srk[r] * sm.srk[cc];
-      Qk[c2][i] *= sm.srq[r] * sm.srk[cc];
+      Kk[i] *= sm.srk[r] * sm.srk[cc];
+      Qk[i] *= sm.srq[r] * sm.srk[cc];
     }
+    sm.sKQ[0][w][c2][lane] = Kk;
+    sm.sKQ[1][w][c2][lane] = Qk;
   }
-  float rk_r[4], rq_r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rk_r[i] = sm.srk[row0 + lg * 4 + i];
-    rq_r[i] = sm.srq[row0 + lg * 4 + i];
-  }
+  // norms of this lane's C rows, re-read from LDS where used
+  auto rk4 = [&]() { return *reinterpret_cast<const f32x4*>(sm.srk + row0 + lg * 4); };
+  auto rq4 = [&]() { return *reinterpret_cast<const f32x4*>(sm.srq + row0 + lg * 4); };
 
   f32x4 dQacc[NT2], dKacc[NT2];
 #pragma unroll
@@ -334,6 +333,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
 
   for (int hh = 0; hh < h_count; ++hh) {
     const int h = h_first + hh;
+    // Lane indices re-derived from an opaque copy of the thread id in every head: otherwise the
+    // compiler hoists dozens of lane-dependent addresses out of the head loop and spills.
+    int tid_o = threadIdx.x;
+    if (DET) asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), rt = w & 3, half = w >> 2, row0 = 16 * rt, arow = row0 + lr;
     __syncthreads(); // the previous head's tail is done with the shared tiles
     {
       const int r = tid >> 3, pc = tid & 7;
@@ -406,6 +411,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) pdv = mfma(fpt[k2], lds_tr8(B.sdO, SDO, k2 * 32, cs), pdv);
       float xu[4], x[4], dr[4];
+      const f32x4 rk_r = rk4(), rq_r = rq4();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i, cc = cs + lr;
@@ -427,12 +433,13 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         dX = mfma(lds_tr8(sm.sA, SA, k2 * 32, row0), lds8(B.sdRT, SA, cs + lr, k2 * 32 + lg * 8), dX);
       }
       TI* dvp = (TI*)a.dv;
+      const f32x4 rk_r2 = rk4();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i, cc = cs + lr;
-        zp[i] += rk_r[i] * kdv[i] * R[i];
+        zp[i] += rk_r2[i] * kdv[i] * R[i];
         dbx[i] += xu[i] * dX[i];
-        dbr[i] -= beta_r[i] * rk_r[i] * ksv[i] * dX[i];
+        dbr[i] -= beta_r[i] * rk_r2[i] * ksv[i] * dX[i];
         if (r < len) IO<TI>::store1(dvp + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + cc, beta_r[i] * dX[i]);
       }
       lds_store4_t(B.sRT, SA, cs + lr, row0 + lg * 4, R[0], R[1], R[2], R[3]);
@@ -483,9 +490,11 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       }
     }
     float gm[2][4], dgam[2][4];
+    const f32x4 rq_r = rq4();
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int ct = 2 * half + c2, cc = 16 * ct + lr;
+      const f32x4 Qk = sm.sKQ[1][w][c2][lane];
       float t1[4], t2[4], t3[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -493,7 +502,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         const bool lo = r >= cc;
         gm[c2][i] = lo ? __expf(sm.sG[r] - sm.sG[cc]) : 0.f;
         const float dqk = lo ? dP[c2][i] * gm[c2][i] : 0.f;
-        dgam[c2][i] = lo ? dP[c2][i] * Qk[c2][i] : 0.f;
+        dgam[c2][i] = lo ? dP[c2][i] * Qk[i] : 0.f;
         t1[i] = dqk * sm.srk[cc];
         t2[i] = dqk * rq_r[i];
         t3[i] = dA[c2][i];
@@ -524,10 +533,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     // (dKk + dKk^T) diag(rk); row and column sums of dGam o Gam are reduced per wave (DPP rows,
     // lane-group columns) into per-half and per-row-tile partials
     float dbl[4] = {0.f, 0.f, 0.f, 0.f}, rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 rk_r = rk4();
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int ct = 2 * half + c2, cc = 16 * ct + lr;
       const float rkc = sm.srk[cc];
+      const f32x4 Kk = sm.sKQ[0][w][c2][lane];
       f32x4 acc = zero4();
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
@@ -537,9 +548,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i;
         const float dl = r > cc ? -acc[i] : 0.f;
-        dbl[i] += dl * gm[c2][i] * Kk[c2][i];
+        dbl[i] += dl * gm[c2][i] * Kk[i];
         const float dkk = dl * beta_r[i] * gm[c2][i];
-        dgam[c2][i] += dl * beta_r[i] * Kk[c2][i];
+        dgam[c2][i] += dl * beta_r[i] * Kk[i];
         const float mm = dgam[c2][i] * gm[c2][i];
         rsum[i] += mm;
         csum += mm;
@@ -629,6 +640,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     TI* dqp = (TI*)a.dq;
     TI* dkp = (TI*)a.dk;
     float qd[4] = {0.f, 0.f, 0.f, 0.f}, kd[4] = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 rk_r = rk4(), rq_r = rq4();
     if (a.l2norm) {
 #pragma unroll
       for (int t = 0; t < NT2; ++t)
