@@ -216,6 +216,7 @@ struct GradSmem {
   bf16 sK[CH * SK];
   bf16 sQ[CH * SK];
   bf16 sA[CH * SA];
+  bf16 sP[CH * SA];
   float sG[CH], sB[CH], srk[CH], srq[CH];
   float sRow[2][4][CH];
   float sRowM[2][CH]; // per column half: row sums of dGam o Gam
@@ -273,21 +274,58 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   const bf16* dstape = reinterpret_cast<const bf16*>(a.dstape);
   const bf16* qkt = reinterpret_cast<const bf16*>(a.qk);
 
-  // ---- K, Q rows and their norms; Kk = Kh Kh^T, Qk = Qh Kh^T on this wave's tiles
-  for (int idx = tid; idx < CH * (D / 8); idx += GRAD_THREADS) {
-    const int r = idx / (D / 8), pc = idx % (D / 8);
-    bf16x8 kv = zero8(), qv = zero8();
-    if (r < len) {
-      kv = IO<TI>::load8(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
-      qv = IO<TI>::load8(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
-    }
-    *reinterpret_cast<bf16x8*>(sm.sK + r * SK + pc * 8) = kv;
-    *reinterpret_cast<bf16x8*>(sm.sQ + r * SK + pc * 8) = qv;
+  // Prefetch registers. Every load is unconditional (rows clamped to the chunk, rows past its end
+  // zeroed when staged), so the loads of one batch are in flight together and waited for once.
+  bf16x8 nS, ndS, nx; // slice: S^T / dSn^T piece; dO piece (threads < 256) or V piece (threads >= 256)
+  bf16x8 nA, nP;      // head: A and P row pieces
+  float nGB;          // head: G (wave 0) or beta (other waves) of row tid % 64
+  auto prefetch = [&](int h, int cv, int tid) {
+    const int dvl = min(tid / (D / 8), DC - 1), pc = tid % (D / 8); // 32 rows x D/8 pieces
+    const size_t off = ((size_t)c * a.HV + h) * D * D + (size_t)(cv * DC + dvl) * D + pc * 8;
+    nS = *reinterpret_cast<const bf16x8*>(htape + off);
+    ndS = *reinterpret_cast<const bf16x8*>(dstape + off);
+    const int u = tid & 255, r = min(u >> 2, len - 1), pv = u & 3;
+    const TI* src = tid < 256 ? dop : vp;
+    nx = IO<TI>::load8(src + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + pv * 8);
+  };
+  auto store_head = [&](int tid) {
+    const int r = tid >> 3, pc = tid & 7;
+    *reinterpret_cast<bf16x8*>(sm.sA + r * SA + pc * 8) = keep8(nA, r < len);
+    *reinterpret_cast<bf16x8*>(sm.sP + r * SA + pc * 8) = keep8(nP, r < len);
+    if (tid < 2 * CH) (tid < CH ? sm.sG : sm.sB)[tid & 63] = keepf(nGB, (tid & 63) < len);
+  };
+  auto prefetch_head = [&](int h, int tid) {
+    const int r = min(tid >> 3, len - 1), pc = tid & 7;
+    nA = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8);
+    const int rr = min(tid & 63, len - 1);
+    nGB = ((tid >> 6) == 0 ? a.gcum : a.beta)[(size_t)(t0 + rr) * a.HV + h];
+    nP = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + r * CH + pc * 8);
+    prefetch(h, 0, tid);
+  };
+
+  // ---- K, Q rows and their norms (the first head's tiles are loaded alongside); Kk = Kh Kh^T,
+  // Qk = Qh Kh^T on this wave's tiles
+  constexpr int KQ_IT = CH * (D / 8) / GRAD_THREADS;
+  static_assert(KQ_IT * GRAD_THREADS == CH * (D / 8), "K/Q staging covers the tile");
+  bf16x8 kv[KQ_IT], qv[KQ_IT];
+#pragma unroll
+  for (int it = 0; it < KQ_IT; ++it) {
+    const int idx = tid + it * GRAD_THREADS, r = min(idx / (D / 8), len - 1), pc = idx % (D / 8);
+    kv[it] = IO<TI>::load8(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
+    qv[it] = IO<TI>::load8(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
+  }
+  const int rr0 = min(lane, len - 1);
+  const float rkv = a.rk[(size_t)(t0 + rr0) * a.H + j], rqv = a.rq[(size_t)(t0 + rr0) * a.H + j];
+  prefetch_head(h_first, tid);
+#pragma unroll
+  for (int it = 0; it < KQ_IT; ++it) {
+    const int idx = tid + it * GRAD_THREADS, r = idx / (D / 8), pc = idx % (D / 8);
+    *reinterpret_cast<bf16x8*>(sm.sK + r * SK + pc * 8) = keep8(kv[it], r < len);
+    *reinterpret_cast<bf16x8*>(sm.sQ + r * SK + pc * 8) = keep8(qv[it], r < len);
   }
   if (tid < CH) {
-    const bool ok = tid < len;
-    sm.srk[tid] = ok ? a.rk[(size_t)(t0 + tid) * a.H + j] : 0.f;
-    sm.srq[tid] = ok ? a.rq[(size_t)(t0 + tid) * a.H + j] : 0.f;
+    sm.srk[tid] = keepf(rkv, tid < len);
+    sm.srq[tid] = keepf(rqv, tid < len);
   }
   __syncthreads();
 #pragma unroll
@@ -309,6 +347,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     sm.sKQ[0][w][c2][lane] = Kk;
     sm.sKQ[1][w][c2][lane] = Qk;
   }
+  store_head(tid); // the first head's tiles (not read above)
   // norms of this lane's C rows, re-read from LDS where used
   auto rk4 = [&]() { return *reinterpret_cast<const f32x4*>(sm.srk + row0 + lg * 4); };
   auto rq4 = [&]() { return *reinterpret_cast<const f32x4*>(sm.srq + row0 + lg * 4); };
@@ -316,20 +355,6 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   f32x4 dQacc[NT2], dKacc[NT2];
 #pragma unroll
   for (int t = 0; t < NT2; ++t) dQacc[t] = dKacc[t] = zero4();
-
-  // slice prefetch registers
-  bf16x8 nS, ndS, nx; // S^T / dSn^T piece; dO piece (threads < 256) or V piece (threads >= 256)
-  auto prefetch = [&](int h, int cv) {
-    const int dvl = tid / (D / 8), pc = tid % (D / 8); // 32 rows x D/8 pieces = 512 (D = 128)
-    if (dvl < DC) {
-      const size_t off = ((size_t)c * a.HV + h) * D * D + (size_t)(cv * DC + dvl) * D + pc * 8;
-      nS = *reinterpret_cast<const bf16x8*>(htape + off);
-      ndS = *reinterpret_cast<const bf16x8*>(dstape + off);
-    }
-    const int u = tid & 255, r = min(u >> 2, len - 1), pv = u & 3;
-    const TI* src = tid < 256 ? dop : vp;
-    nx = IO<TI>::load8(src + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + pv * 8); // rows past len zeroed when staged
-  };
 
   for (int hh = 0; hh < h_count; ++hh) {
     const int h = h_first + hh;
@@ -339,25 +364,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     if (DET) asm volatile("" : "+v"(tid_o));
     const int tid = tid_o, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), rt = w & 3, half = w >> 2, row0 = 16 * rt, arow = row0 + lr;
-    __syncthreads(); // the previous head's tail is done with the shared tiles
-    {
-      const int r = tid >> 3, pc = tid & 7;
-      const bf16x8 av =
-          r < len ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) : zero8();
-      *reinterpret_cast<bf16x8*>(sm.sA + r * SA + pc * 8) = av;
-    }
-    if (tid < CH) {
-      const bool ok = tid < len;
-      sm.sG[tid] = ok ? a.gcum[(size_t)(t0 + tid) * a.HV + h] : 0.f;
-      sm.sB[tid] = ok ? a.beta[(size_t)(t0 + tid) * a.HV + h] : 0.f;
-    }
-    const float gam = a.gamma[(size_t)c * a.HV + h];
-    bf16x8 fpt[2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-      fpt[k2] = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + arow * CH + k2 * 32 + lg * 8);
-    prefetch(h, 0);
-    __syncthreads();
+    __syncthreads(); // this head's A, P, G and beta are staged
     const float glast = sm.sG[len - 1];
     // per-row factors: this lane's C rows (r) and A-fragment row (arow)
     float brow[4], beta_r[4], dec_r[4];
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         if (tid < 256) *reinterpret_cast<bf16x8*>(B.sdO + r * SDO + pv * 8) = xv;
         else *reinterpret_cast<bf16x8*>(B.sV + r * SV + pv * 8) = xv;
       }
-      if (cv + 1 < NDC) prefetch(h, cv + 1);
+      if (cv + 1 < NDC) prefetch(h, cv + 1, tid);
       __syncthreads();
 
       // this wave's 16 x 16 tile of the slice: rows row0.., slice columns 16*half..
@@ -409,7 +416,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         kdv = mfma(fk, lds8(B.sdS, SK, cs + lr, ks * 32 + lg * 8), kdv);
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) pdv = mfma(fpt[k2], lds_tr8(B.sdO, SDO, k2 * 32, cs), pdv);
+      for (int k2 = 0; k2 < 2; ++k2) pdv = mfma(lds8(sm.sP, SA, arow, k2 * 32 + lg * 8), lds_tr8(B.sdO, SDO, k2 * 32, cs), pdv);
       float xu[4], x[4], dr[4];
       const f32x4 rk_r = rk4(), rq_r = rq4();
 #pragma unroll
@@ -468,7 +475,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       }
     }
 
-    // ---- per-head tail
+    // ---- per-head tail; the next head's tiles load meanwhile
+    if (hh + 1 < h_count) prefetch_head(h + 1, tid);
     auto& T = sm.u.t;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -595,7 +603,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       }
     }
     if (w == 0) {
-      const int r = lane;
+      // lane l takes row 63 - l, so the in-chunk reverse cumulative sum is a prefix sum over lanes
+      const int r = 63 - lane;
       const float rows = sm.sRowM[0][r] + sm.sRowM[1][r];
       const float cols = sm.sCol[0][r] + sm.sCol[1][r] + sm.sCol[2][r] + sm.sCol[3][r];
       const bool ok = r < len;
@@ -604,18 +613,13 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       const float db = sm.sRow[0][1][r] + sm.sRow[1][1][r];
       const float dbeta = sm.sRow[0][2][r] + sm.sRow[1][2][r] + sm.sRow[0][3][r] + sm.sRow[1][3][r];
       const float zd = ok ? z * dec : 0.f;
-      const float zsum = col_sum4(row_sum16(zd));
+      const float zsum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_prefix_sum(zd)), 63));
       float dG = ok ? rows - cols + __expf(sm.sG[r]) * db - zd : 0.f;
       float sd = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) sd += sm.sred[q];
-      if (r == len - 1) dG += gam * sd + zsum;
-      float xs = dG;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_down(xs, off);
-        if (lane + off < 64) xs += y;
-      }
+      if (r == len - 1) dG += __expf(glast) * sd + zsum; // gamma = exp(G_last)
+      const float xs = wave_prefix_sum(dG);
       if (ok) {
         a.dg[(size_t)(t0 + r) * a.HV + h] = xs;
         a.dbeta[(size_t)(t0 + r) * a.HV + h] = dbeta;
@@ -632,6 +636,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
             atomicAdd(a.dkacc + ((size_t)(t0 + r) * a.H + j) * D + dk, dKacc[t][i]);
           }
         }
+    }
+    if (hh + 1 < h_count) {
+      __syncthreads(); // this head's tail is done with the shared tiles
+      store_head(tid);
     }
   }
 

@@ -33,6 +33,21 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
+// v if keep, else zeros; f if keep, else 0. The mask is opaque to the compiler, so a value that
+// was just loaded stays an unconditional load (a select on it lets the compiler move the load
+// into a branch, and the branch's join then waits for every outstanding load).
+__device__ __forceinline__ bf16x8 keep8(bf16x8 v, bool keep) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  unsigned m = keep ? ~0u : 0u;
+  asm volatile("" : "+v"(m));
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) & m);
+}
+__device__ __forceinline__ float keepf(float f, bool keep) {
+  unsigned m = keep ? ~0u : 0u;
+  asm volatile("" : "+v"(m));
+  return __builtin_bit_cast(float, __builtin_bit_cast(unsigned, f) & m);
+}
+
 // Fragment read from an LDS tile stored row-major with `stride` elements per row:
 // 8 consecutive elements of row `row` starting at column `col` (16-byte aligned).
 __device__ __forceinline__ bf16x8 lds8(const bf16* base, int stride, int row, int col) {
@@ -230,6 +245,19 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane l gets the sum over lanes 0..l):
+// Hillis-Steele shifts within 16-lane rows, then DPP broadcasts of lane 15 into rows 1 and 3 and
+// of lane 31 into rows 2 and 3. Lanes whose DPP source is absent add the zero "old" operand.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
   return x;
 }
 
