@@ -205,6 +205,7 @@ int launch_walk_bwd(const Args& a, void* stream) {
 // transpose-reads. The value-dimension contractions feed dQh and dKh directly through row-scaled
 // A fragments: diag(b) dO S^T, diag(exp(G_last - G)) R dSn^T and -diag(beta b) dX S^T.
 constexpr int GRAD_THREADS = 512;
+constexpr int GRAD_MAXG = 8; // value heads per q/k head whose dg, dbeta wait in LDS (more: stored per head)
 
 template <int D>
 struct GradSmem {
@@ -223,6 +224,7 @@ struct GradSmem {
   float sCol[4][CH];  // per row tile: column sums of dGam o Gam
   float sred[8];
   f32x4 sKQ[2][8][2][64]; // Kk, Qk: each wave's own C tiles, parked for the per-head tails
+  float sDGB[GRAD_MAXG][2][CH]; // dg, dbeta of each head, written out after the last head
   union U {
     struct Sl {
       bf16 sS[DC * SK];
@@ -300,7 +302,6 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     const int rr = min(tid & 63, len - 1);
     nGB = ((tid >> 6) == 0 ? a.gcum : a.beta)[(size_t)(t0 + rr) * a.HV + h];
     nP = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + r * CH + pc * 8);
-    prefetch(h, 0, tid);
   };
 
   // ---- K, Q rows and their norms (the first head's tiles are loaded alongside); Kk = Kh Kh^T,
@@ -317,6 +318,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   const int rr0 = min(lane, len - 1);
   const float rkv = a.rk[(size_t)(t0 + rr0) * a.H + j], rqv = a.rq[(size_t)(t0 + rr0) * a.H + j];
   prefetch_head(h_first, tid);
+  prefetch(h_first, 0, tid);
 #pragma unroll
   for (int it = 0; it < KQ_IT; ++it) {
     const int idx = tid + it * GRAD_THREADS, r = idx / (D / 8), pc = idx % (D / 8);
@@ -401,7 +403,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         if (tid < 256) *reinterpret_cast<bf16x8*>(B.sdO + r * SDO + pv * 8) = xv;
         else *reinterpret_cast<bf16x8*>(B.sV + r * SV + pv * 8) = xv;
       }
+      // the next slice, or the next head's first (this head's again after the last head): always
+      // a load, so no branch leaves the wait counts unsure which registers are still loading
       if (cv + 1 < NDC) prefetch(h, cv + 1, tid);
+      else prefetch(hh + 1 < h_count ? h + 1 : h, 0, tid);
       __syncthreads();
 
       // this wave's 16 x 16 tile of the slice: rows row0.., slice columns 16*half..
@@ -620,7 +625,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       for (int q = 0; q < 8; ++q) sd += sm.sred[q];
       if (r == len - 1) dG += __expf(glast) * sd + zsum; // gamma = exp(G_last)
       const float xs = wave_prefix_sum(dG);
-      if (ok) {
+      if (hh < GRAD_MAXG) {
+        sm.sDGB[hh][0][r] = xs;
+        sm.sDGB[hh][1][r] = dbeta;
+      } else if (ok) {
         a.dg[(size_t)(t0 + r) * a.HV + h] = xs;
         a.dbeta[(size_t)(t0 + r) * a.HV + h] = dbeta;
       }
@@ -643,6 +651,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     }
   }
 
+  // dg, dbeta of the heads held in LDS (the last head's are visible after one more barrier)
+  __syncthreads();
+  for (int idx = tid; idx < min(h_count, GRAD_MAXG) * 2 * CH; idx += GRAD_THREADS) {
+    const int hh = idx / (2 * CH), k = (idx / CH) & 1, r = idx % CH;
+    if (r < len) (k ? a.dbeta : a.dg)[(size_t)(t0 + r) * a.HV + h_first + hh] = sm.sDGB[hh][k][r];
+  }
   if (DET) {
     // L2-norm backward of the group sums: dx = r (dxh - xh (xh . dxh)), xh = r x
     TI* dqp = (TI*)a.dq;

@@ -107,6 +107,8 @@ EDGE = [
     syn.custom("edge_g4_h0", [100, 33], 1, 4, 64, "bf16", has_h0=True, want_ht=True, seed=10),
     syn.custom("edge_empty_docs", [0, 0, 17, 0], 1, 3, 128, "bf16", has_h0=True, want_ht=True, has_dht=True,
                seed=11),
+    # more value heads per q/k head than the deterministic chunk-gradient kernel parks in LDS
+    syn.custom("edge_g10", [90, 40], 1, 10, 64, "bf16", seed=12),
 ]
 
 
