@@ -101,8 +101,9 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
       if (WRITE_O) rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
     }
     {
-      // per-token scalars of row `lane` (every wave loads them; wave 0 stages them)
-      const size_t rv = (size_t)(t0 + min(lane, last)), rl = (size_t)(t0 + last);
+      // per-token scalars of row `lane`, staged by wave 0; the other waves load one row (the
+      // loads stay unconditional, and touch one cache line instead of 64)
+      const size_t rl = (size_t)(t0 + last), rv = w == 0 ? (size_t)(t0 + min(lane, last)) : rl;
       sg = a.gcum[rv * a.HV + h];
       sglast = a.gcum[rl * a.HV + h];
       sbeta = a.beta[rv * a.HV + h];
@@ -370,8 +371,9 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
       rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
     }
     {
-      // per-token scalars of row `lane` (every wave loads them; wave 0 stages them)
-      const size_t rv = (size_t)(t0 + min(lane, last)), rl = (size_t)(t0 + last);
+      // per-token scalars of row `lane`, staged by wave 0; the other waves load one row (the
+      // loads stay unconditional, and touch one cache line instead of 64)
+      const size_t rl = (size_t)(t0 + last), rv = w == 0 ? (size_t)(t0 + min(lane, last)) : rl;
       sg = a.gcum[rv * a.HV + h];
       sglast = a.gcum[rl * a.HV + h];
       sbeta = a.beta[rv * a.HV + h];
