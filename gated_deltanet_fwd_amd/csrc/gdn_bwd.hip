@@ -299,7 +299,8 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   auto prefetch_head = [&](int h, int tid) {
     const int r = min(tid >> 3, len - 1), pc = tid & 7;
     nA = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8);
-    const int rr = min(tid & 63, len - 1);
+    // waves 0 and 1 gather 64 rows; the others read one row (one cache line, no branch)
+    const int rr = tid < 2 * CH ? min(tid & 63, len - 1) : 0;
     nGB = ((tid >> 6) == 0 ? a.gcum : a.beta)[(size_t)(t0 + rr) * a.HV + h];
     nP = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + r * CH + pc * 8);
   };
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     kv[it] = IO<TI>::load8(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
     qv[it] = IO<TI>::load8(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
   }
-  const int rr0 = min(lane, len - 1);
+  const int rr0 = tid < CH ? min(lane, len - 1) : 0; // only wave 0 stages the norms
   const float rkv = a.rk[(size_t)(t0 + rr0) * a.H + j], rqv = a.rq[(size_t)(t0 + rr0) * a.H + j];
   prefetch_head(h_first, tid);
   prefetch(h_first, 0, tid);

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
 
   // the first batch's per-token g and beta (backward: gcum) of this wave's value head, loaded
   // together with K and Q so that their latencies overlap
-  const int h_pre = j * a.G + min(w, a.G - 1), r_pre = t0 + min(lane, len - 1);
+  const int h_pre = j * a.G + min(w, a.G - 1), r_pre = t0 + (w < a.G ? min(lane, len - 1) : 0); // waves past G: one line
   const float pre_g = BWD ? a.gcum[(size_t)r_pre * a.HV + h_pre] : a.g[(size_t)r_pre * a.HV + h_pre];
   const float pre_b = BWD ? 0.f : a.beta[(size_t)r_pre * a.HV + h_pre];
 
