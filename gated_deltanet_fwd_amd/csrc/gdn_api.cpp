@@ -105,7 +105,7 @@ SavedLayout saved_layout(const Sizes& s, int full) {
 }
 
 struct WorkLayout {
-  size_t seq_c0, c_t0, c_len, seq_order, status, discard, rk, rq, qk, htape, dstape, dqacc, dkacc, total;
+  size_t seq_c0, c_t0, c_len, seq_order, pair_order, status, discard, rk, rq, qk, htape, dstape, dqacc, dkacc, total;
 };
 
 WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
@@ -120,6 +120,7 @@ WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
   L.c_t0 = take((size_t)s.NT * 4);
   L.c_len = take((size_t)s.NT * 4);
   L.seq_order = take((size_t)s.N * 4);
+  L.pair_order = take((size_t)(s.N * s.H + 7) / 8 * 2 * 4);
   L.status = take(4);
   L.discard = take(gdn::kDiscardBytes);
   L.rk = take((size_t)s.T * s.H * 4);
@@ -237,6 +238,7 @@ void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
   a.c_t0 = (int*)(b + W.c_t0);
   a.c_len = (int*)(b + W.c_len);
   a.seq_order = (int*)(b + W.seq_order);
+  a.pair_order = (int*)(b + W.pair_order);
   a.status = (int*)(b + W.status);
   a.discard = b + W.discard;
   a.rk = (float*)(b + W.rk);

@@ -152,8 +152,9 @@ __global__ __launch_bounds__(bwalk_threads<D>(), 1) void k_walk_bwd(Args a) {
 
 // Tape walk and reverse walk in one launch. They are independent (the reverse walk never reads
 // the state tape), and each alone leaves CUs idle once the shorter documents' chains finish.
-// Workgroups alternate kinds in super-groups of 8 (document, q/k head) groups, so both walks of a
-// group run on the same XCD (sharing its K tiles in L2), longest documents first.
+// Workgroups come in segments of one super-group (8 (document, q/k head) groups times G value
+// heads, the G heads of a group on one XCD) of one kind, in the order the chunk tables computed:
+// longest estimated run time first.
 template <int D, typename TI>
 __global__ __launch_bounds__(bwalk_threads<D>(), 1) void k_walk_pair(Args a) {
   static_assert(walk_threads<D>() == bwalk_threads<D>(), "the two walks use the same workgroup size");
@@ -162,9 +163,10 @@ __global__ __launch_bounds__(bwalk_threads<D>(), 1) void k_walk_pair(Args a) {
     BWalkSmem<D> r;
   } sm;
   const int SG = 8 * a.G; // workgroups of one super-group of one kind
-  const int b = blockIdx.x, sg = b / (2 * SG), rem = b - sg * 2 * SG;
-  const int kind = rem / SG, blk = sg * SG + (rem - kind * SG);
-  if (kind == 0) walk_fwd_body<D, TI, false, true, false>(a, blk, sm.f);
+  const int b = blockIdx.x, seg = b / SG;
+  const int code = a.pair_order[seg];
+  const int blk = (code & 0x3fffffff) * SG + (b - seg * SG);
+  if ((code >> 30) == 0) walk_fwd_body<D, TI, false, true, false>(a, blk, sm.f);
   else walk_bwd_body<D, TI>(a, blk, sm.r);
 }
 

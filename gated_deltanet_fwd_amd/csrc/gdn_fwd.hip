@@ -18,10 +18,10 @@ namespace gdn {
 
 // ---------------------------------------------------------------------------------------
 // Chunk tables from the device copy of cu_seqlens (one workgroup of 1024 threads).
-__global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu, int N, int NT, int64_t T,
+__global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu, int N, int H, int NT, int64_t T,
                                                  int* __restrict__ seq_c0, int* __restrict__ c_t0,
                                                  int* __restrict__ c_len, int* __restrict__ seq_order,
-                                                 int* __restrict__ status) {
+                                                 int* __restrict__ pair_order, int* __restrict__ status) {
   __shared__ int s_scan[1024];
   __shared__ int s_carry, s_bad;
   const int tid = threadIdx.x;
@@ -87,6 +87,36 @@ __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu,
       rank += (Lm > Ln) || (Lm == Ln && m < n);
     }
     seq_order[rank] = n;
+  }
+  // Launch order of the paired walks: the reverse-walk and tape-walk super-groups (8 (document,
+  // q/k head) groups each, documents longest first) merged by estimated run time, chunks times
+  // 5 for a reverse-walk step and 4 for a tape-walk step, longest first, so that the workgroups
+  // left waiting for a free CU are the shortest. Each item's place is its index in its own list
+  // plus the number of items of the other list that precede it (both lists are sorted).
+  // Without the longest-first document order, the kinds simply alternate.
+  __syncthreads();
+  const int nsg = (N * H + 7) / 8;
+  auto steps = [&](int s) {
+    const int n = seq_order[min(8 * s / H, N - 1)];
+    return seq_c0[n + 1] - seq_c0[n];
+  };
+  for (int i = tid; i < 2 * nsg; i += 1024) {
+    const int kind = i / nsg, s = i - kind * nsg; // kind 1: reverse walk
+    int pos;
+    if (bad || N > 8192) {
+      pos = 2 * s + kind;
+    } else {
+      const long w = (long)steps(s) * (kind ? 5 : 4);
+      int lo = 0, hi = nsg; // items of the other list that precede this one: a prefix [0, lo)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const long wo = (long)steps(mid) * (kind ? 4 : 5);
+        if (kind ? wo > w : wo >= w) lo = mid + 1; // ties: the reverse walk first
+        else hi = mid;
+      }
+      pos = s + lo;
+    }
+    pair_order[pos] = s | (kind << 30);
   }
 }
 
@@ -306,8 +336,8 @@ __global__ __launch_bounds__(walk_threads<D>(), 1) void k_walk_fwd(Args a) {
 static inline hipStream_t S_(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int launch_tables(const Args& a, void* stream) {
-  hipLaunchKernelGGL(k_tables, dim3(1), dim3(1024), 0, S_(stream), a.cu, a.N, a.NT, a.T, a.seq_c0, a.c_t0,
-                     a.c_len, a.seq_order, a.status);
+  hipLaunchKernelGGL(k_tables, dim3(1), dim3(1024), 0, S_(stream), a.cu, a.N, a.H, a.NT, a.T, a.seq_c0, a.c_t0,
+                     a.c_len, a.seq_order, a.pair_order, a.status);
   return (int)hipGetLastError();
 }
 

@@ -54,6 +54,10 @@ struct Args {
   uint16_t* dstape;// bf16 [NT, HV, d(value), d(key)]: gradient of each chunk's end state, transposed
   float* dqacc;    // f32 [T, H, d] (atomic reduction only)
   float* dkacc;    // f32 [T, H, d] (atomic reduction only)
+  // (Fields are appended here: moving the offsets of the fields above has cost the walks several
+  // per cent, for reasons the generated loop code does not show.)
+  int* pair_order; // [2 ceil(N H / 8)] super-groups of the paired walk launch, longest first
+                   // (bit 30: reverse walk, else tape walk; low bits: super-group)
 };
 
 // Bytes of the workspace area that takes the stores of lanes past a chunk's end.
