@@ -126,8 +126,8 @@ __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu,
 // gamma and Akk = (I + L)^-1 (saved).
 //
 // K K^T and the q.k products run on MFMA; each wave keeps 16 rows of K K^T in registers. The
-// inverse runs one value head per wave: every lane owns one column c of A and forward-substitutes
-// it, x_i = -sum_{m<i} L_im x_m (x_c = 1), reading rows of L from LDS as broadcasts.
+// inverse runs one value head per wave, by 16 x 16 blocks: forward substitution for the four
+// diagonal blocks (one column of one block per lane), fp32 MFMA for the six blocks below them.
 template <int D, typename TI, bool BWD>
 __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
   if (a.status[0]) return;
@@ -284,27 +284,82 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
         }
     __syncthreads();
     if (w < nb) {
-      const int h = j * a.G + hb + w, col = lane;
-      float x[CH];
+      // (I + L)^-1 by 16 x 16 blocks. D_b = (I + L_bb)^-1 by forward substitution, lane (b, col)
+      // forming column col of D_b; then the blocks below the diagonal, one block diagonal at a
+      // time, A_ij = -D_i sum_{k=j}^{i-1} L_ik A_kj (A_jj = D_j), on fp32 MFMA 16x16x4 with the k
+      // index permuted (at k-step e, lane l supplies k = 4 (l / 16) + e) so that a product's
+      // result is the next product's B operand as it stands.
+      float (*Lw)[SL] = u.L[w];
+      const int blk = lane >> 4, col = lane & 15, r16 = lane & 15, g4 = 4 * (lane >> 4);
+      float x[16];
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const float* Lrow = &Lw[16 * blk + i][16 * blk];
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int m = 0; m + 4 <= i; m += 4) {
-          const float4 l4 = *reinterpret_cast<const float4*>(&u.L[w][i][m]);
+          const float4 l4 = *reinterpret_cast<const float4*>(Lrow + m);
           s0 = __builtin_fmaf(l4.x, x[m], s0);
           s1 = __builtin_fmaf(l4.y, x[m + 1], s1);
-          s2 = __builtin_fmaf(l4.z, x[m + 2], s2);
-          s3 = __builtin_fmaf(l4.w, x[m + 3], s3);
+          s0 = __builtin_fmaf(l4.z, x[m + 2], s0);
+          s1 = __builtin_fmaf(l4.w, x[m + 3], s1);
         }
 #pragma unroll
-        for (int m = (i / 4) * 4; m < i; ++m) s0 = __builtin_fmaf(u.L[w][i][m], x[m], s0);
-        x[i] = i < col ? 0.f : (i == col ? 1.f : -((s0 + s1) + (s2 + s3)));
+        for (int m = (i / 4) * 4; m < i; ++m) s0 = __builtin_fmaf(Lrow[m], x[m], s0);
+        x[i] = i < col ? 0.f : (i == col ? 1.f : -(s0 + s1));
       }
-      // stage the inverse (bf16) in this wave's own L area, row-major
-      bf16* stage = reinterpret_cast<bf16*>(&u.L[w][0][0]);
+      // D_b row-major over the diagonal block of L (read above), D_b^T over the zero block to its
+      // right (b < 3: only D_0..D_2 are right operands)
 #pragma unroll
-      for (int i = 0; i < CH; ++i) stage[i * (CH + PAD) + col] = (bf16)x[i];
+      for (int i = 0; i < 16; ++i) Lw[16 * blk + i][16 * blk + col] = x[i];
+      if (blk < 3) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(&Lw[16 * blk + col][16 * (blk + 1) + 4 * q]) =
+              make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+      }
+      // left operand X (rows R.., columns C.. of the area): X[l % 16][4 (l / 16) + e] for k-step e;
+      // a right operand read from its stored transpose has the same form
+      auto frag = [&](int R, int C) {
+        const float4 v = *reinterpret_cast<const float4*>(&Lw[R + r16][C + g4]);
+        return f32x4{v.x, v.y, v.z, v.w};
+      };
+      auto mm = [](f32x4 x4, f32x4 y4, f32x4 acc) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x4[0], y4[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x4[1], y4[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x4[2], y4[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x4[3], y4[3], acc, 0, 0, 0);
+        return acc;
+      };
+      const f32x4 D0t = frag(0, 16), D1t = frag(16, 32), D2t = frag(32, 48);
+      const f32x4 D1 = frag(16, 16), D2 = frag(32, 32), D3 = frag(48, 48);
+      const f32x4 L10 = frag(16, 0), L21 = frag(32, 16), L32 = frag(48, 32);
+      const f32x4 L20 = frag(32, 0), L31 = frag(48, 16), L30 = frag(48, 0);
+      const f32x4 z = zero4();
+      const f32x4 A10 = -mm(D1, mm(L10, D0t, z), z);
+      const f32x4 A21 = -mm(D2, mm(L21, D1t, z), z);
+      const f32x4 A32 = -mm(D3, mm(L32, D2t, z), z);
+      const f32x4 A20 = -mm(D2, mm(L21, A10, mm(L20, D0t, z)), z);
+      const f32x4 A31 = -mm(D3, mm(L32, A21, mm(L31, D1t, z)), z);
+      const f32x4 A30 = -mm(D3, mm(L32, A20, mm(L31, A10, mm(L30, D0t, z))), z);
+      // stage the inverse (bf16) over the same area, row-major; every fp32 read above comes first
+      asm volatile("" ::: "memory");
+      bf16* stage = reinterpret_cast<bf16*>(&Lw[0][0]);
+      constexpr int SS = CH + PAD;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) stage[(16 * blk + i) * SS + 16 * blk + col] = (bf16)x[i];
+      auto put = [&](int bi, int bj, f32x4 v) { // result layout: rows 4 (l / 16) + e, column l % 16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) stage[(16 * bi + g4 + e) * SS + 16 * bj + r16] = (bf16)v[e];
+      };
+      put(1, 0, A10);
+      put(2, 1, A21);
+      put(3, 2, A32);
+      put(2, 0, A20);
+      put(3, 1, A31);
+      put(3, 0, A30);
+      for (int cc = 16 * (lane / 16 + 1); cc < CH; cc += 8) // zeros right of the diagonal blocks
+        *reinterpret_cast<bf16x8*>(stage + lane * SS + cc) = zero8();
     }
     __syncthreads();
     if (w < nb) {
