@@ -145,9 +145,9 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
     bf16 k[CH * SK];
     bf16 q[CH * SK];
   };
-  union Smem {
+  union Smem { // the backward pass builds no L: its smaller footprint lets more workgroups share a CU
     KQ kq;
-    float L[NB][CH][SL];
+    float L[BWD ? 1 : NB][CH][SL];
   };
   __shared__ __attribute__((aligned(16))) Smem u;
   __shared__ float srk[CH], srq[CH];
