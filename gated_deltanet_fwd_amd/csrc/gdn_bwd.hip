@@ -70,9 +70,9 @@ __global__ __launch_bounds__(NTHREADS) void k_wy_full(Args a) {
   const TI* vp = (const TI*)a.v;
   if (tid < CH) {
     const bool ok = tid < len;
-    sG[tid] = ok ? a.gcum[(size_t)(t0 + tid) * a.HV + h] : 0.f;
+    sG[tid] = ok ? a.gcum[(size_t)h * a.T + t0 + tid] : 0.f;
     sB[tid] = ok ? a.beta[(size_t)(t0 + tid) * a.HV + h] : 0.f;
-    srk[tid] = ok ? a.rk[(size_t)(t0 + tid) * a.H + j] : 0.f;
+    srk[tid] = ok ? a.rk[(size_t)j * a.T + t0 + tid] : 0.f;
   }
   __syncthreads();
   for (int idx = tid; idx < CH * (D / 8); idx += NTHREADS) {
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     nA = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8);
     // waves 0 and 1 gather 64 rows; the others read one row (one cache line, no branch)
     const int rr = tid < 2 * CH ? min(tid & 63, len - 1) : 0;
-    nGB = ((tid >> 6) == 0 ? a.gcum : a.beta)[(size_t)(t0 + rr) * a.HV + h];
+    nGB = *((tid >> 6) == 0 ? a.gcum + (size_t)h * a.T + t0 + rr : a.beta + (size_t)(t0 + rr) * a.HV + h);
     nP = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + r * CH + pc * 8);
   };
 
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     qv[it] = IO<TI>::load8(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
   }
   const int rr0 = tid < CH ? min(lane, len - 1) : 0; // only wave 0 stages the norms
-  const float rkv = a.rk[(size_t)(t0 + rr0) * a.H + j], rqv = a.rq[(size_t)(t0 + rr0) * a.H + j];
+  const float rkv = a.rk[(size_t)j * a.T + t0 + rr0], rqv = a.rq[(size_t)j * a.T + t0 + rr0];
   prefetch_head(h_first, tid);
   prefetch(h_first, 0, tid);
 #pragma unroll
@@ -745,7 +745,7 @@ __global__ __launch_bounds__(NTHREADS) void k_finalize_qk(Args a) {
   for (int which = 0; which < 2; ++which) {
     float x[PER], g[PER];
     float dot = 0.f;
-    const float r = rn[which][row];
+    const float r = rn[which][(row % a.H) * a.T + row / a.H]; // norms are head-major
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int d = lane + 64 * e;

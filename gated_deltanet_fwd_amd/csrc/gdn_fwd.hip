@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
   // the first batch's per-token g and beta (backward: gcum) of this wave's value head, loaded
   // together with K and Q so that their latencies overlap
   const int h_pre = j * a.G + min(w, a.G - 1), r_pre = t0 + (w < a.G ? min(lane, len - 1) : 0); // waves past G: one line
-  const float pre_g = BWD ? a.gcum[(size_t)r_pre * a.HV + h_pre] : a.g[(size_t)r_pre * a.HV + h_pre];
+  const float pre_g = BWD ? a.gcum[(size_t)h_pre * a.T + r_pre] : a.g[(size_t)r_pre * a.HV + h_pre];
   const float pre_b = BWD ? 0.f : a.beta[(size_t)r_pre * a.HV + h_pre];
 
   // this wave's 16 rows of K and Q (MFMA A fragments), their squared norms
@@ -196,8 +196,8 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
     srk[ar] = ok ? rkv : 0.f;
     srq[ar] = ok ? rqv : 0.f;
     if (ok) {
-      a.rk[(size_t)(t0 + ar) * a.H + j] = rkv;
-      a.rq[(size_t)(t0 + ar) * a.H + j] = rqv;
+      a.rk[(size_t)j * a.T + t0 + ar] = rkv;
+      a.rq[(size_t)j * a.T + t0 + ar] = rqv;
     }
   }
   __syncthreads();
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
       float x;
       const size_t rr = (size_t)(t0 + min(r, len - 1)) * a.HV + h;
       if (BWD) {
-        x = r < len ? (hb == 0 ? pre_g : a.gcum[rr]) : 0.f;
+        x = r < len ? (hb == 0 ? pre_g : a.gcum[(size_t)h * a.T + t0 + min(r, len - 1)]) : 0.f;
       } else {
         const float gv = r < len ? (hb == 0 ? pre_g : a.g[rr]) : 0.f;
         const float bv = r < len ? (hb == 0 ? pre_b : a.beta[rr]) : 0.f;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
           if (lane >= off) x += y;
         }
         sB[w][r] = bv;
-        if (r < len) a.gcum[(size_t)(t0 + r) * a.HV + h] = x;
+        if (r < len) a.gcum[(size_t)h * a.T + t0 + r] = x;
         if (r == len - 1) a.gamma[(size_t)c * a.HV + h] = __expf(x);
       }
       sG[w][r] = x;

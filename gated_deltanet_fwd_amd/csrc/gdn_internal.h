@@ -33,7 +33,8 @@ struct Args {
   float* dh0;
   // saved set
   uint16_t* akk;   // bf16 [T, HV, 64]: row i of the chunk's (I + L)^-1 at the token of row i
-  float* gcum;     // f32  [T, HV]: in-chunk inclusive cumulative log decay
+  float* gcum;     // f32  [HV, T]: in-chunk inclusive cumulative log decay (head-major, so that
+                   // a chunk's 64 tokens of one head are one 256-byte run)
   float* gamma;    // f32  [NT, HV]: exp(gcum of the chunk's last token)
   uint16_t* htape; // bf16 [NT, HV, d(value), d(key)]: state at each chunk start, transposed
   uint16_t* vnew;  // bf16 [T, HV, d]: R = U - W S (full form only)
@@ -47,8 +48,8 @@ struct Args {
   int* seq_order;  // [N] documents, longest first
   int* status;     // [1] nonzero if the device tables disagree with the host's chunk count
   void* discard;   // [kDiscardBytes] target of stores from lanes past a chunk's end (never read)
-  float* rk;       // [T, H] inverse L2 norms of k rows (1 when the norm is off)
-  float* rq;       // [T, H] inverse L2 norms of q rows
+  float* rk;       // [H, T] inverse L2 norms of k rows (1 when the norm is off), head-major
+  float* rq;       // [H, T] inverse L2 norms of q rows, head-major
   uint16_t* qk;    // bf16 [NT, HV, 64, 64] P = exp(G_q - G_k) qh.kh masked to q >= k, per value head
                    // (row-major P for the forward, P^T for the backward)
   uint16_t* dstape;// bf16 [NT, HV, d(value), d(key)]: gradient of each chunk's end state, transposed

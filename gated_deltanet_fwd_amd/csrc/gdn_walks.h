@@ -104,11 +104,11 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
       // per-token scalars of row `lane`, staged by wave 0; the other waves load one row (the
       // loads stay unconditional, and touch one cache line instead of 64)
       const size_t rl = (size_t)(t0 + last), rv = w == 0 ? (size_t)(t0 + min(lane, last)) : rl;
-      sg = a.gcum[rv * a.HV + h];
-      sglast = a.gcum[rl * a.HV + h];
+      sg = a.gcum[(size_t)h * a.T + rv];
+      sglast = a.gcum[(size_t)h * a.T + rl];
       sbeta = a.beta[rv * a.HV + h];
-      srk = a.rk[rv * a.H + j];
-      if (WRITE_O) srq = a.rq[rv * a.H + j];
+      srk = a.rk[(size_t)j * a.T + rv];
+      if (WRITE_O) srq = a.rq[(size_t)j * a.T + rv];
     }
   };
   auto store_chunk = [&](int b, int c) {
@@ -359,8 +359,8 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
       rD[it] = IO<TI>::load8(dc + rr * a.HV * D + pc * 8);
       // Q rows are staged scaled by exp(G) rq (zero past the end; formed in store_chunk, so no
       // load result is used before the chunk's compute)
-      rgq[it] = a.gcum[(size_t)(t0 + rr) * a.HV + h];
-      rrq[it] = a.rq[(size_t)(t0 + rr) * a.H + j];
+      rgq[it] = a.gcum[(size_t)h * a.T + t0 + rr];
+      rrq[it] = a.rq[(size_t)j * a.T + t0 + rr];
     }
     const bf16* ac = akk + ((size_t)t0 * a.HV + h) * CH;
     const bf16* pc_ = pm + ((size_t)c * a.HV + h) * CH * CH;
@@ -374,10 +374,10 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
       // per-token scalars of row `lane`, staged by wave 0; the other waves load one row (the
       // loads stay unconditional, and touch one cache line instead of 64)
       const size_t rl = (size_t)(t0 + last), rv = w == 0 ? (size_t)(t0 + min(lane, last)) : rl;
-      sg = a.gcum[rv * a.HV + h];
-      sglast = a.gcum[rl * a.HV + h];
+      sg = a.gcum[(size_t)h * a.T + rv];
+      sglast = a.gcum[(size_t)h * a.T + rl];
       sbeta = a.beta[rv * a.HV + h];
-      srk = a.rk[rv * a.H + j];
+      srk = a.rk[(size_t)j * a.T + rv];
     }
   };
   auto store_chunk = [&](int b, int c) {

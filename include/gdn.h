@@ -63,7 +63,7 @@ extern "C" {
 #define GDN_DTYPE_F32 1
 
 /* saved-set forms (README saved-set table quoted in flashinfer PR #8542):
- * LIGHT keeps Akk (the inverse of I + L per chunk, bf16 [T, HV, 64]), gcum (f32 [T, HV]) and
+ * LIGHT keeps Akk (the inverse of I + L per chunk, bf16 [T, HV, 64]), gcum (f32 [HV, T]) and
  * gamma (f32 [NT, HV]); the backward replays the state tape. FULL also keeps the state tape
  * (bf16 [NT, HV, d, d]), v_new (bf16 [T, HV, d]), w and u (bf16 [T, HV, d]) and Aqk
  * (bf16 [T, HV, 64]); the backward then skips the replay walk. Both forms give bitwise
