@@ -129,7 +129,7 @@ __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu,
 // inverse runs one value head per wave, by 16 x 16 blocks: forward substitution for the four
 // diagonal blocks (one column of one block per lane), fp32 MFMA for the six blocks below them.
 template <int D, typename TI, bool BWD>
-__global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
+__global__ __launch_bounds__(NTHREADS, 3) void k_intra(Args a) {
   if (a.status[0]) return;
   const int c = blockIdx.x, j = blockIdx.y;
   const int len = a.c_len[c];
@@ -140,7 +140,9 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
   constexpr int SK = D + PAD;
   constexpr int SL = CH + 4; // fp32 row stride of L: 16-byte aligned rows
   constexpr int KS = D / 32;
-  constexpr int NB = 4;      // value heads per batch, one wave each
+  // value heads per batch, one wave each; three keep the LDS footprint within a third of the CU,
+  // so three workgroups share one
+  constexpr int NB = 3;
   struct KQ {
     bf16 k[CH * SK];
     bf16 q[CH * SK];
@@ -161,27 +163,32 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
   const float pre_g = BWD ? a.gcum[(size_t)h_pre * a.T + r_pre] : a.g[(size_t)r_pre * a.HV + h_pre];
   const float pre_b = BWD ? 0.f : a.beta[(size_t)r_pre * a.HV + h_pre];
 
-  // this wave's 16 rows of K and Q (MFMA A fragments), their squared norms
+  // this wave's 16 rows of K and Q (MFMA A fragments), their squared norms. The loads are
+  // unconditional (rows past the chunk's end re-read its last row and are zeroed through a mask
+  // the compiler cannot see through), so all of them are in flight together.
   const int ar = 16 * w + lr;
   const bool ok = ar < len;
+  const size_t roff = ((size_t)(t0 + min(ar, len - 1)) * a.H + j) * D + lg * 8;
+  float kf[KS][8], qf[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    IO<TI>::load8f(kp + roff + ks * 32, kf[ks]);
+    IO<TI>::load8f(qp + roff + ks * 32, qf[ks]);
+  }
+  unsigned okm = ok ? ~0u : 0u;
+  asm volatile("" : "+v"(okm));
   bf16x8 fk[KS], fq[KS];
   float ssk = 0.f, ssq = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    float kf[8], qf[8];
-    if (ok) {
-      IO<TI>::load8f(kp + ((size_t)(t0 + ar) * a.H + j) * D + ks * 32 + lg * 8, kf);
-      IO<TI>::load8f(qp + ((size_t)(t0 + ar) * a.H + j) * D + ks * 32 + lg * 8, qf);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = qf[e] = 0.f;
-    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ssk += kf[e] * kf[e];
-      ssq += qf[e] * qf[e];
-      fk[ks][e] = (bf16)kf[e];
-      fq[ks][e] = (bf16)qf[e];
+      const float kv = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, kf[ks][e]) & okm);
+      const float qv = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, qf[ks][e]) & okm);
+      ssk += kv * kv;
+      ssq += qv * qv;
+      fk[ks][e] = (bf16)kv;
+      fq[ks][e] = (bf16)qv;
     }
     *reinterpret_cast<bf16x8*>(u.kq.k + ar * SK + ks * 32 + lg * 8) = fk[ks];
     *reinterpret_cast<bf16x8*>(u.kq.q + ar * SK + ks * 32 + lg * 8) = fq[ks];
@@ -195,10 +202,6 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
     const float rqv = a.l2norm ? 1.f / sqrtf(ssq + 1e-6f) : 1.f;
     srk[ar] = ok ? rkv : 0.f;
     srq[ar] = ok ? rqv : 0.f;
-    if (ok) {
-      a.rk[(size_t)j * a.T + t0 + ar] = rkv;
-      a.rq[(size_t)j * a.T + t0 + ar] = rqv;
-    }
   }
   __syncthreads();
 
@@ -238,12 +241,7 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
       } else {
         const float gv = r < len ? (hb == 0 ? pre_g : a.g[rr]) : 0.f;
         const float bv = r < len ? (hb == 0 ? pre_b : a.beta[rr]) : 0.f;
-        x = gv;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(x, off);
-          if (lane >= off) x += y;
-        }
+        x = wave_prefix_sum(gv);
         sB[w][r] = bv;
         if (r < len) a.gcum[(size_t)h * a.T + t0 + r] = x;
         if (r == len - 1) a.gamma[(size_t)c * a.HV + h] = __expf(x);
@@ -253,9 +251,17 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
     __syncthreads();
     // P_qk = exp(G_q - G_k) qh.kh for q >= k, per value head: the forward stores P[q][k], the
     // backward P^T[k][q]; both are [cc][r..r+3] of this wave's tile
+    // Every element's exponential is computed and then masked through an opaque mask (keepf): with
+    // a select the compiler branches around each one, and every branch waits for its own LDS reads.
+    // G of this lane's rows (16 w + 4 lg + i) and columns (16 ct + lr) are read once per head.
     for (int b = 0; b < nb; ++b) {
       const int h = j * a.G + hb + b;
       bf16* pout = reinterpret_cast<bf16*>(a.qk) + ((size_t)c * a.HV + h) * CH * CH;
+      const float4 gr4 = *reinterpret_cast<const float4*>(&sG[b][16 * w + lg * 4]);
+      const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
+      float gc[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) gc[ct] = sG[b][16 * ct + lr];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int cc = 16 * ct + lr;
@@ -264,8 +270,9 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * w + lg * 4 + i;
           const int qi = BWD ? r : cc, ki = BWD ? cc : r;
-          const float e = __expf(fminf(sG[b][qi] - sG[b][ki], 0.f));
-          v[i] = qi >= ki ? e * qk[ct][i] : 0.f;
+          const float gq = BWD ? gr[i] : gc[ct], gk = BWD ? gc[ct] : gr[i];
+          const float e = __expf(fminf(gq - gk, 0.f));
+          v[i] = keepf(e * qk[ct][i], qi >= ki);
         }
         lds_store4_t(pout, CH, cc, 16 * w + lg * 4, v[0], v[1], v[2], v[3]);
       }
@@ -274,14 +281,21 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
       __syncthreads();
       continue;
     }
-    for (int b = 0; b < nb; ++b)
+    for (int b = 0; b < nb; ++b) {
+      const float4 gr4 = *reinterpret_cast<const float4*>(&sG[b][16 * w + lg * 4]);
+      const float4 br4 = *reinterpret_cast<const float4*>(&sB[b][16 * w + lg * 4]);
+      const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w}, br[4] = {br4.x, br4.y, br4.z, br4.w};
+      float gc[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) gc[ct] = sG[b][16 * ct + lr];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * w + lg * 4 + i, cc = 16 * ct + lr;
-          u.L[b][r][cc] = r > cc ? sB[b][r] * __expf(sG[b][r] - sG[b][cc]) * kk[ct][i] : 0.f;
+          u.L[b][r][cc] = keepf(br[i] * __expf(gr[i] - gc[ct]) * kk[ct][i], r > cc);
         }
+    }
     __syncthreads();
     if (w < nb) {
       // (I + L)^-1 by 16 x 16 blocks. D_b = (I + L_bb)^-1 by forward substitution, lane (b, col)
@@ -365,15 +379,25 @@ __global__ __launch_bounds__(NTHREADS) void k_intra(Args a) {
     if (w < nb) {
       const int h = j * a.G + hb + w;
       const bf16* stage = reinterpret_cast<const bf16*>(&u.L[w][0][0]);
+      // the lane index is made opaque here, so the compiler cannot compute these addresses at the
+      // top of the kernel and keep (or spill) them until now
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int it = 0; it < CH / 8; ++it) {
-        const int r = it * 8 + (lane >> 3), pc = lane & 7;
+        const int r = it * 8 + (ln >> 3), pc = ln & 7;
         if (r < len)
           *reinterpret_cast<bf16x8*>(aout + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) =
               lds8(stage, CH + PAD, r, pc * 8);
       }
     }
     __syncthreads();
+  }
+  // the norms go out last: a store issued earlier would be waited for at the first wait on a
+  // later load (memory operations complete in order)
+  if (tid < len) {
+    a.rk[(size_t)j * a.T + t0 + tid] = srk[tid];
+    a.rq[(size_t)j * a.T + t0 + tid] = srq[tid];
   }
 }
 
