@@ -505,18 +505,23 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         sm.sRow[half][2][r] = dbx[i];
       }
     }
+    // Gam = exp(G_r - G_c) on and below the diagonal: computed for every element and masked
+    // (keepf), since a select makes the compiler branch around each exponential and wait for its
+    // LDS reads inside every branch
     float gm[2][4], dgam[2][4];
     const f32x4 rq_r = rq4();
+    const f32x4 g_r = *reinterpret_cast<const f32x4*>(sm.sG + row0 + lg * 4);
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int ct = 2 * half + c2, cc = 16 * ct + lr;
       const f32x4 Qk = sm.sKQ[1][w][c2][lane];
+      const float g_c = sm.sG[cc];
       float t1[4], t2[4], t3[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i;
         const bool lo = r >= cc;
-        gm[c2][i] = lo ? __expf(sm.sG[r] - sm.sG[cc]) : 0.f;
+        gm[c2][i] = keepf(__expf(g_r[i] - g_c), lo);
         const float dqk = lo ? dP[c2][i] * gm[c2][i] : 0.f;
         dgam[c2][i] = lo ? dP[c2][i] * Qk[i] : 0.f;
         t1[i] = dqk * sm.srk[cc];
@@ -616,13 +621,14 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       const float rows = sm.sRowM[0][r] + sm.sRowM[1][r];
       const float cols = sm.sCol[0][r] + sm.sCol[1][r] + sm.sCol[2][r] + sm.sCol[3][r];
       const bool ok = r < len;
-      const float dec = ok ? __expf(glast - sm.sG[r]) : 0.f;
+      const float g_r1 = sm.sG[r];
+      const float dec = keepf(__expf(glast - g_r1), ok);
       const float z = sm.sRow[0][0][r] + sm.sRow[1][0][r];
       const float db = sm.sRow[0][1][r] + sm.sRow[1][1][r];
       const float dbeta = sm.sRow[0][2][r] + sm.sRow[1][2][r] + sm.sRow[0][3][r] + sm.sRow[1][3][r];
       const float zd = ok ? z * dec : 0.f;
       const float zsum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_prefix_sum(zd)), 63));
-      float dG = ok ? rows - cols + __expf(sm.sG[r]) * db - zd : 0.f;
+      float dG = keepf(rows - cols + __expf(g_r1) * db - zd, ok);
       float sd = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) sd += sm.sred[q];
@@ -701,12 +707,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i, dk = 16 * (half * NT2 + t) + lr;
-        if (r >= len) continue;
         float dqv = dQacc[t][i], dkv = dKacc[t][i];
-        if (a.l2norm) {
+        if (a.l2norm) { // (rows past the chunk's end hold zeros in LDS and are not stored)
           dqv = rq_r[i] * (dqv - rq_r[i] * (float)sm.sQ[r * SK + dk] * qd[i]);
           dkv = rk_r[i] * (dkv - rk_r[i] * (float)sm.sK[r * SK + dk] * kd[i]);
         }
+        if (r >= len) continue;
         IO<TI>::store1(dqp + ((size_t)(t0 + r) * a.H + j) * D + dk, dqv);
         IO<TI>::store1(dkp + ((size_t)(t0 + r) * a.H + j) * D + dk, dkv);
       }

@@ -229,6 +229,16 @@ struct IO<float> {
   }
 };
 
+// Raw buffer resource over [base, base + bytes) (gfx9 word 3). A buffer store whose offset lies
+// past the end is dropped by the hardware, so lanes past a chunk's end store without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_store16(const bf16x8& v, __amdgpu_buffer_rsrc_t r, int off_bytes) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off_bytes, 0, 0);
+}
+
 // Sum over the 16 lanes that share l / 16 (the lanes of one MFMA output row group).
 __device__ __forceinline__ float sum16(float x) {
   x += __shfl_xor(x, 1);

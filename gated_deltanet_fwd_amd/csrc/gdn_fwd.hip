@@ -379,16 +379,12 @@ __global__ __launch_bounds__(NTHREADS, 3) void k_intra(Args a) {
     if (w < nb) {
       const int h = j * a.G + hb + w;
       const bf16* stage = reinterpret_cast<const bf16*>(&u.L[w][0][0]);
-      // the lane index is made opaque here, so the compiler cannot compute these addresses at the
-      // top of the kernel and keep (or spill) them until now
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
+      // rows of the chunk only: stores past the buffer's end (rows >= len) are dropped
+      const __amdgpu_buffer_rsrc_t ar_ = make_rsrc(aout + (size_t)t0 * a.HV * CH, len * a.HV * CH * (int)sizeof(bf16));
 #pragma unroll
       for (int it = 0; it < CH / 8; ++it) {
-        const int r = it * 8 + (ln >> 3), pc = ln & 7;
-        if (r < len)
-          *reinterpret_cast<bf16x8*>(aout + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) =
-              lds8(stage, CH + PAD, r, pc * 8);
+        const int r = it * 8 + (lane >> 3), pc = lane & 7;
+        buf_store16(lds8(stage, CH + PAD, r, pc * 8), ar_, ((r * a.HV + h) * CH + pc * 8) * (int)sizeof(bf16));
       }
     }
     __syncthreads();
