@@ -236,7 +236,8 @@ struct GradSmem {
       bf16 sXT[DC * SA];
       bf16 sdRT[DC * SA];
       bf16 sRT[DC * SA];
-      bf16 sdXT[DC * SA];
+      bf16 sRTd[DC * SA]; // R^T with the rows of R scaled by exp(G_last - G)
+      bf16 sdXT[DC * SA]; // dX^T with the rows of dX scaled by -beta exp(G)
     } b;
     struct Tl {
       bf16 sT1t[CH * SA];
@@ -381,8 +382,6 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       dec_r[i] = __expf(glast - sm.sG[r]);
     }
     const float a_b = __expf(sm.sG[arow]);
-    const float a_dec = __expf(glast - sm.sG[arow]);
-    const float a_nbb = -sm.sB[arow] * a_b;
 
     float zp[4] = {0.f, 0.f, 0.f, 0.f}, dbx[4] = {0.f, 0.f, 0.f, 0.f}, dbr[4] = {0.f, 0.f, 0.f, 0.f},
           dbo[4] = {0.f, 0.f, 0.f, 0.f};
@@ -457,15 +456,20 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         dbr[i] -= beta_r[i] * rk_r2[i] * ksv[i] * dX[i];
         if (r < len) IO<TI>::store1(dvp + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + cc, beta_r[i] * dX[i]);
       }
+      // R and dX are stored transposed (the A operands below), also with their row factors applied
+      // here, on the fp32 values (one rounding to bf16 instead of two)
       lds_store4_t(B.sRT, SA, cs + lr, row0 + lg * 4, R[0], R[1], R[2], R[3]);
-      lds_store4_t(B.sdXT, SA, cs + lr, row0 + lg * 4, dX[0], dX[1], dX[2], dX[3]);
+      lds_store4_t(B.sRTd, SA, cs + lr, row0 + lg * 4, R[0] * dec_r[0], R[1] * dec_r[1], R[2] * dec_r[2],
+                   R[3] * dec_r[3]);
+      lds_store4_t(B.sdXT, SA, cs + lr, row0 + lg * 4, dX[0] * (-beta_r[0] * brow[0]), dX[1] * (-beta_r[1] * brow[1]),
+                   dX[2] * (-beta_r[2] * brow[2]), dX[3] * (-beta_r[3] * brow[3]));
       __syncthreads();
 
       // value-dimension contractions over this slice (32 = one MFMA k-step)
       const bf16x8 aO = lds8(B.sdO, SDO, arow, lg * 8);
       const bf16x8 aOb = scale8(aO, a_b);
-      const bf16x8 aR = scale8(lds_tr8(B.sRT, SA, 0, row0), a_dec);
-      const bf16x8 aX = scale8(lds_tr8(B.sdXT, SA, 0, row0), a_nbb);
+      const bf16x8 aR = lds_tr8(B.sRTd, SA, 0, row0);
+      const bf16x8 aX = lds_tr8(B.sdXT, SA, 0, row0);
 #pragma unroll
       for (int t = 0; t < NT2; ++t) {
         const int dcol = 16 * (half * NT2 + t);
