@@ -1,6 +1,8 @@
 // Host side of the C ABI in include/gdn.h: validation, buffer layouts, saved-set tagging and the
 // launch sequence of each call. No device memory is allocated or freed here and nothing
-// synchronises; every launch goes to the caller's stream.
+// synchronises. Launches go to the caller's stream; when one document's chain work dominates,
+// the other documents' intra and walk launches go to a second stream of the library's own
+// (one per device, default priority), forked from and joined back into the caller's stream.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
@@ -120,7 +122,7 @@ WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
   L.c_t0 = take((size_t)s.NT * 4);
   L.c_len = take((size_t)s.NT * 4);
   L.seq_order = take((size_t)s.N * 4);
-  L.pair_order = take((size_t)(s.N * s.H + 7) / 8 * 2 * 4);
+  L.pair_order = take(((size_t)(s.N * s.H + 7) / 8 + 1) * 2 * 4);
   L.status = take(4);
   L.discard = take(gdn::kDiscardBytes);
   L.rk = take((size_t)s.T * s.H * 4);
@@ -208,13 +210,14 @@ void timing_end(const char* name, hipEvent_t start, void* stream) {
   g_pending.push_back({name, start, e});
 }
 
-#define LAUNCH(name, x)                                                                  \
+#define LAUNCH_ON(st, name, x)                                                           \
   do {                                                                                   \
-    hipEvent_t t0_ = timing_begin(stream);                                               \
+    hipEvent_t t0_ = timing_begin(st);                                                   \
     const int e_ = (x);                                                                  \
-    timing_end(name, t0_, stream);                                                       \
+    timing_end(name, t0_, st);                                                           \
     if (e_ != 0) return fail(GDN_EHIP, "%s: %s", #x, hipGetErrorString((hipError_t)e_)); \
   } while (0)
+#define LAUNCH(name, x) LAUNCH_ON(stream, name, x)
 
 void fill_common(gdn::Args& a, const Sizes& s, const gdn_problem* p) {
   std::memset(&a, 0, sizeof a);
@@ -230,6 +233,90 @@ void fill_common(gdn::Args& a, const Sizes& s, const gdn_problem* p) {
   a.has_h0 = p->has_h0 ? 1 : 0;
   a.want_ht = p->want_ht ? 1 : 0;
   a.full = p->save_mode == GDN_SAVE_FULL ? 1 : 0;
+  gdn::whole_range(a);
+}
+
+// Two-part launch plan. The walks are serial over a document's chunks, so the longest document
+// sets their run time while the others' chains finish early and leave CUs idle. When it is
+// clearly the longest (at least 5/4 of the next one, and at least 64 chunks), its intra and walk
+// launches (part A) run on the caller's stream and the other documents' (part B) on a second
+// stream: its walk then starts after its own intra launch rather than after everyone's, and
+// part B fills the CUs that part A leaves free.
+struct Split {
+  bool on = false;
+  int n0 = 0;          // the longest document (ties: the lowest index), rank 0 of the tables
+  int cA0 = 0, cA = 0; // its chunks: [cA0, cA0 + cA)
+};
+
+Split plan_split(const gdn_problem* p, const Sizes& s) {
+  Split sp;
+  if (s.N < 2 || s.N > 8192) return sp; // the device tables keep the identity order above 8192
+  const int32_t* cu = p->cu_seqlens_host;
+  // rank 0 of the device tables: the most tokens, ties to the lowest index
+  int len0 = -1;
+  for (int n = 0; n < s.N; ++n)
+    if (cu[n + 1] - cu[n] > len0) {
+      len0 = cu[n + 1] - cu[n];
+      sp.n0 = n;
+    }
+  int c1 = 0;
+  for (int n = 0; n < s.N; ++n) {
+    const int c = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    if (n < sp.n0) sp.cA0 += c;
+    else if (n == sp.n0) sp.cA = c;
+    if (n != sp.n0 && c > c1) c1 = c;
+  }
+  sp.on = sp.cA >= 64 && 4 * sp.cA >= 5 * c1;
+  return sp;
+}
+
+void range_a(gdn::Args& a, const Split& sp) {
+  a.grp_off = 0;
+  a.grp_end = a.H;
+  a.pair_off = 2 * ((a.N * a.H - a.H + 7) / 8);
+  a.c_base = sp.cA0;
+  a.c_skip_at = 0x7fffffff;
+  a.c_skip = 0;
+  a.c_count = sp.cA;
+}
+
+void range_b(gdn::Args& a, const Split& sp) {
+  a.grp_off = a.H;
+  a.grp_end = a.N * a.H;
+  a.pair_off = 0;
+  a.c_base = 0;
+  a.c_skip_at = sp.cA0;
+  a.c_skip = sp.cA;
+  a.c_count = a.NT - sp.cA;
+}
+
+// The library's second stream on the current device, created on first use and kept for the
+// life of the process; NULL if it cannot be created (the calls then use one stream).
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64];
+  static bool tried[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!tried[dev]) {
+    tried[dev] = true;
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess) streams[dev] = st;
+  }
+  return streams[dev];
+}
+
+// Orders `to` after the work enqueued so far on `from` (an event of its own per call, so that
+// concurrent calls never share one).
+int stream_wait(hipStream_t from, hipStream_t to) {
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return fail(GDN_EHIP, "hipEventCreate failed");
+  hipError_t r = hipEventRecord(e, from);
+  if (r == hipSuccess) r = hipStreamWaitEvent(to, e, 0);
+  hipEventDestroy(e);
+  if (r != hipSuccess) return fail(GDN_EHIP, "stream fork/join: %s", hipGetErrorString(r));
+  return GDN_OK;
 }
 
 void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
@@ -316,10 +403,26 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
   bind_workspace(a, W, workspace);
   bind_saved(a, L, saved);
 
+  const bool walk = write_o || full;
+  const Split sp = walk ? plan_split(p, s) : Split{};
+  hipStream_t side = sp.on ? side_stream() : nullptr;
+  if (side) a.grp_split = a.H;
   LAUNCH("gdn_tables", gdn::launch_tables(a, stream));
-  LAUNCH("gdn_intra", gdn::launch_intra(a, 0, stream));
-  if (write_o) LAUNCH("gdn_walk_fwd", gdn::launch_walk_fwd(a, 1, full, stream));
-  else if (full) LAUNCH("gdn_walk_tape", gdn::launch_walk_fwd(a, 0, 1, stream));
+  const char* walk_name = write_o ? "gdn_walk_fwd" : "gdn_walk_tape";
+  if (!side) {
+    LAUNCH("gdn_intra", gdn::launch_intra(a, 0, stream));
+    if (walk) LAUNCH(walk_name, gdn::launch_walk_fwd(a, write_o, full, stream));
+  } else {
+    gdn::Args aa = a, ab = a;
+    range_a(aa, sp);
+    range_b(ab, sp);
+    LAUNCH("gdn_intra", gdn::launch_intra(aa, 0, stream));
+    CHECK(stream_wait((hipStream_t)stream, side));
+    LAUNCH(walk_name, gdn::launch_walk_fwd(aa, write_o, full, stream));
+    LAUNCH_ON(side, "gdn_intra", gdn::launch_intra(ab, 0, side));
+    LAUNCH_ON(side, walk_name, gdn::launch_walk_fwd(ab, write_o, full, side));
+    CHECK(stream_wait(side, (hipStream_t)stream));
+  }
   if (full) LAUNCH("gdn_wy_full", gdn::launch_wy_full(a, stream));
   const uint64_t h = problem_hash(p);
   const uint64_t words[4] = {kMagic, (uint64_t)GDN_ABI_VERSION, (uint64_t)p->save_mode, h};
@@ -417,12 +520,31 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   bind_saved(a, L, const_cast<void*>(saved));
   if (!full) a.htape = (uint16_t*)((char*)workspace + W.htape);
 
+  const Split sp = plan_split(p, s);
+  hipStream_t side = sp.on ? side_stream() : nullptr;
+  if (side) a.grp_split = a.H;
   LAUNCH("gdn_tables", gdn::launch_tables(a, stream));
-  LAUNCH("gdn_intra_bwd", gdn::launch_intra(a, 1, stream));
   // light: the state tape is replayed; the tape walk and the reverse walk are independent and
   // share one launch. full: the tape is in the saved set.
-  if (!full) LAUNCH("gdn_walk_pair", gdn::launch_walk_pair(a, stream));
-  else LAUNCH("gdn_walk_bwd", gdn::launch_walk_bwd(a, stream));
+  auto walks = [&](const gdn::Args& x, hipStream_t st) -> int {
+    if (!full) LAUNCH_ON(st, "gdn_walk_pair", gdn::launch_walk_pair(x, st));
+    else LAUNCH_ON(st, "gdn_walk_bwd", gdn::launch_walk_bwd(x, st));
+    return GDN_OK;
+  };
+  if (!side) {
+    LAUNCH("gdn_intra_bwd", gdn::launch_intra(a, 1, stream));
+    CHECK(walks(a, (hipStream_t)stream));
+  } else {
+    gdn::Args aa = a, ab = a;
+    range_a(aa, sp);
+    range_b(ab, sp);
+    LAUNCH("gdn_intra_bwd", gdn::launch_intra(aa, 1, stream));
+    CHECK(stream_wait((hipStream_t)stream, side));
+    CHECK(walks(aa, (hipStream_t)stream));
+    LAUNCH_ON(side, "gdn_intra_bwd", gdn::launch_intra(ab, 1, side));
+    CHECK(walks(ab, side));
+    CHECK(stream_wait(side, (hipStream_t)stream));
+  }
   if (!p->deterministic) {
     LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
     LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dkacc, (size_t)s.T * s.H * s.D, stream));

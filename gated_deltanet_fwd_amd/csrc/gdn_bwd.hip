@@ -164,7 +164,7 @@ __global__ __launch_bounds__(bwalk_threads<D>(), 1) void k_walk_pair(Args a) {
   } sm;
   const int SG = 8 * a.G; // workgroups of one super-group of one kind
   const int b = blockIdx.x, seg = b / SG;
-  const int code = a.pair_order[seg];
+  const int code = a.pair_order[a.pair_off + seg];
   const int blk = (code & 0x3fffffff) * SG + (b - seg * SG);
   if ((code >> 30) == 0) walk_fwd_body<D, TI, false, true, false>(a, blk, sm.f);
   else walk_bwd_body<D, TI>(a, blk, sm.r);
@@ -253,7 +253,7 @@ struct GradSmem {
 template <int D, typename TI, bool DET>
 __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   if (a.status[0]) return;
-  const int c = blockIdx.x;
+  const int c = launch_chunk(a, blockIdx.x);
   const int len = a.c_len[c];
   if (len <= 0) return;
   const int t0 = a.c_t0[c];
@@ -725,9 +725,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
 
 template <int D, typename TI>
 static int chunk_grad_t(const Args& a, int det, hipStream_t s) {
-  if (a.NT == 0) return 0;
-  if (det) hipLaunchKernelGGL((k_chunk_grad<D, TI, true>), dim3(a.NT, a.H), dim3(GRAD_THREADS), 0, s, a);
-  else hipLaunchKernelGGL((k_chunk_grad<D, TI, false>), dim3(a.NT, a.HV), dim3(GRAD_THREADS), 0, s, a);
+  if (a.c_count == 0) return 0;
+  if (det) hipLaunchKernelGGL((k_chunk_grad<D, TI, true>), dim3(a.c_count, a.H), dim3(GRAD_THREADS), 0, s, a);
+  else hipLaunchKernelGGL((k_chunk_grad<D, TI, false>), dim3(a.c_count, a.HV), dim3(GRAD_THREADS), 0, s, a);
   return (int)hipGetLastError();
 }
 

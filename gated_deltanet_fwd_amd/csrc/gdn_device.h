@@ -288,21 +288,26 @@ struct ChainMap {
   int rank, j, gi, tile;
   bool valid;
 };
-__device__ __forceinline__ ChainMap decode_chain(int b, int N, int H, int G, int ntile) {
-  const int GS = G * ntile;
+__device__ __forceinline__ ChainMap decode_chain(int b, const Args& a, int ntile) {
+  const int H = a.H, GS = a.G * ntile;
   const int sg = b / (8 * GS);
   const int rem = b - sg * 8 * GS;
   const int x = rem & 7;
   const int s = rem >> 3;
-  const long group = (long)sg * 8 + x; // (rank, j) in rank-major order
+  const long group = (long)a.grp_off + (long)sg * 8 + x; // (rank, j) in rank-major order
   ChainMap m;
-  m.valid = group < (long)N * H;
+  m.valid = group < (long)a.grp_end;
   const int grp = (int)group;
   m.rank = grp / H;
   m.j = grp - m.rank * H;
   m.gi = s / ntile;
   m.tile = s - m.gi * ntile;
   return m;
+}
+
+// Chunk processed by workgroup x of a chunk-parallel launch (see Args::c_base).
+__device__ __forceinline__ int launch_chunk(const Args& a, int x) {
+  return a.c_base + x + (x >= a.c_skip_at ? a.c_skip : 0);
 }
 
 } // namespace gdn

@@ -21,7 +21,8 @@ namespace gdn {
 __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu, int N, int H, int NT, int64_t T,
                                                  int* __restrict__ seq_c0, int* __restrict__ c_t0,
                                                  int* __restrict__ c_len, int* __restrict__ seq_order,
-                                                 int* __restrict__ pair_order, int* __restrict__ status) {
+                                                 int* __restrict__ pair_order, int* __restrict__ status,
+                                                 int grp_split) {
   __shared__ int s_scan[1024];
   __shared__ int s_carry, s_bad;
   const int tid = threadIdx.x;
@@ -93,30 +94,36 @@ __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu,
   // 5 for a reverse-walk step and 4 for a tape-walk step, longest first, so that the workgroups
   // left waiting for a free CU are the shortest. Each item's place is its index in its own list
   // plus the number of items of the other list that precede it (both lists are sorted).
-  // Without the longest-first document order, the kinds simply alternate.
+  // Without the longest-first document order, the kinds simply alternate. Two orders are built,
+  // one per launch: the groups [grp_split, N H), then the groups [0, grp_split) after it.
   __syncthreads();
-  const int nsg = (N * H + 7) / 8;
-  auto steps = [&](int s) {
-    const int n = seq_order[min(8 * s / H, N - 1)];
-    return seq_c0[n + 1] - seq_c0[n];
-  };
-  for (int i = tid; i < 2 * nsg; i += 1024) {
-    const int kind = i / nsg, s = i - kind * nsg; // kind 1: reverse walk
-    int pos;
-    if (bad || N > 8192) {
-      pos = 2 * s + kind;
-    } else {
-      const long w = (long)steps(s) * (kind ? 5 : 4);
-      int lo = 0, hi = nsg; // items of the other list that precede this one: a prefix [0, lo)
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const long wo = (long)steps(mid) * (kind ? 4 : 5);
-        if (kind ? wo > w : wo >= w) lo = mid + 1; // ties: the reverse walk first
-        else hi = mid;
+  int out0 = 0;
+  for (int part = 0; part < 2; ++part) {
+    const int g_lo = part == 0 ? grp_split : 0, g_hi = part == 0 ? N * H : grp_split;
+    const int nsg = (g_hi - g_lo + 7) / 8;
+    auto steps = [&](int s) {
+      const int n = seq_order[min((g_lo + 8 * s) / H, N - 1)];
+      return seq_c0[n + 1] - seq_c0[n];
+    };
+    for (int i = tid; i < 2 * nsg; i += 1024) {
+      const int kind = i / nsg, s = i - kind * nsg; // kind 1: reverse walk
+      int pos;
+      if (bad || N > 8192) {
+        pos = 2 * s + kind;
+      } else {
+        const long w = (long)steps(s) * (kind ? 5 : 4);
+        int lo = 0, hi = nsg; // items of the other list that precede this one: a prefix [0, lo)
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          const long wo = (long)steps(mid) * (kind ? 4 : 5);
+          if (kind ? wo > w : wo >= w) lo = mid + 1; // ties: the reverse walk first
+          else hi = mid;
+        }
+        pos = s + lo;
       }
-      pos = s + lo;
+      pair_order[out0 + pos] = s | (kind << 30);
     }
-    pair_order[pos] = s | (kind << 30);
+    out0 += 2 * nsg;
   }
 }
 
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu,
 template <int D, typename TI, bool BWD>
 __global__ __launch_bounds__(NTHREADS, 3) void k_intra(Args a) {
   if (a.status[0]) return;
-  const int c = blockIdx.x, j = blockIdx.y;
+  const int c = launch_chunk(a, blockIdx.x), j = blockIdx.y;
   const int len = a.c_len[c];
   if (len <= 0) return;
   const int t0 = a.c_t0[c];
@@ -412,14 +419,14 @@ static inline hipStream_t S_(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 int launch_tables(const Args& a, void* stream) {
   hipLaunchKernelGGL(k_tables, dim3(1), dim3(1024), 0, S_(stream), a.cu, a.N, a.H, a.NT, a.T, a.seq_c0, a.c_t0,
-                     a.c_len, a.seq_order, a.pair_order, a.status);
+                     a.c_len, a.seq_order, a.pair_order, a.status, a.grp_split);
   return (int)hipGetLastError();
 }
 
 template <int D, typename TI>
 static int intra_t(const Args& a, int bwd, hipStream_t s) {
-  if (a.NT == 0) return 0;
-  const dim3 grid(a.NT, a.H);
+  if (a.c_count == 0) return 0;
+  const dim3 grid(a.c_count, a.H);
   if (bwd) hipLaunchKernelGGL((k_intra<D, TI, true>), grid, dim3(NTHREADS), 0, s, a);
   else hipLaunchKernelGGL((k_intra<D, TI, false>), grid, dim3(NTHREADS), 0, s, a);
   return (int)hipGetLastError();
@@ -433,7 +440,18 @@ int launch_intra(const Args& a, int bwd_prep, void* stream) {
 
 // Number of workgroups of a chain launch: (document, q/k head) groups padded to a multiple of 8
 // (one per XCD), times the G value heads and the value tiles of each group.
-int chain_blocks(const Args& a, int ntile) { return ((a.N * a.H + 7) / 8) * 8 * a.G * ntile; }
+int chain_blocks(const Args& a, int ntile) { return ((a.grp_end - a.grp_off + 7) / 8) * 8 * a.G * ntile; }
+
+void whole_range(Args& a) {
+  a.grp_off = 0;
+  a.grp_end = a.N * a.H;
+  a.pair_off = 0;
+  a.c_base = 0;
+  a.c_skip_at = 0x7fffffff;
+  a.c_skip = 0;
+  a.c_count = a.NT;
+  a.grp_split = 0;
+}
 
 template <int D, typename TI>
 static int walk_t(const Args& a, int write_o, int write_tape, hipStream_t s) {

@@ -57,14 +57,25 @@ struct Args {
   float* dkacc;    // f32 [T, H, d] (atomic reduction only)
   // (Fields are appended here: moving the offsets of the fields above has cost the walks several
   // per cent, for reasons the generated loop code does not show.)
-  int* pair_order; // [2 ceil(N H / 8)] super-groups of the paired walk launch, longest first
-                   // (bit 30: reverse walk, else tape walk; low bits: super-group)
+  int* pair_order; // [2 (ceil(N H / 8) + 1)] super-groups of the paired walk launches, longest
+                   // first (bit 30: reverse walk, else tape walk; low bits: super-group)
+  // Part of the problem covered by one launch (the longest document's work and the others' run
+  // on two streams). Chain launches cover the (document rank, q/k head) groups [grp_off, grp_end)
+  // and read their paired-walk order from pair_order + pair_off. Chunk launches cover c_count
+  // chunks: launch index x is chunk c_base + x, plus c_skip from x = c_skip_at on (the other
+  // part's chunks form one contiguous range, which is skipped).
+  int grp_off, grp_end, pair_off;
+  int c_base, c_skip_at, c_skip, c_count;
+  int grp_split; // k_tables: paired-walk orders of the groups [grp_split, N H), then [0, grp_split)
 };
 
 // Bytes of the workspace area that takes the stores of lanes past a chunk's end.
 constexpr size_t kDiscardBytes = 4096;
 
 int chain_blocks(const Args& a, int ntile);
+
+// Whole-problem launch ranges (every group, every chunk, no split of the paired-walk order).
+void whole_range(Args& a);
 
 // Launchers (defined in the .hip translation units). Each returns a hipError_t as int.
 int launch_tables(const Args& a, void* stream);

@@ -50,7 +50,7 @@ struct WalkSmem {
 template <int D, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL>
 __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D, WRITE_O>& sm) {
   if (a.status[0]) return;
-  const ChainMap cm = decode_chain(blk, a.N, a.H, a.G, 1);
+  const ChainMap cm = decode_chain(blk, a, 1);
   if (!cm.valid) return;
   const int n = a.seq_order[cm.rank];
   const int j = cm.j, h = j * a.G + cm.gi;
@@ -320,7 +320,7 @@ struct BWalkSmem {
 template <int D, typename TI>
 __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<D>& sm) {
   if (a.status[0]) return;
-  const ChainMap cm = decode_chain(blk, a.N, a.H, a.G, 1);
+  const ChainMap cm = decode_chain(blk, a, 1);
   if (!cm.valid) return;
   const int n = a.seq_order[cm.rank];
   const int j = cm.j, h = j * a.G + cm.gi;

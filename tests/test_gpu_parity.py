@@ -109,6 +109,10 @@ EDGE = [
                seed=11),
     # more value heads per q/k head than the deterministic chunk-gradient kernel parks in LDS
     syn.custom("edge_g10", [90, 40], 1, 10, 64, "bf16", seed=12),
+    # the longest document (79 chunks) is far longer than the others and sits between them: its
+    # intra and walk launches run apart from the others', whose chunk range wraps around it
+    syn.custom("split_mid", [700, 5000, 129, 1000], 2, 6, 128, "bf16", has_h0=True, want_ht=True, has_dht=True,
+               seed=13),
 ]
 
 
@@ -133,6 +137,19 @@ def test_light_equals_full_bitwise():
     inp = _dev(syn.make_inputs(w))
     a = _run(w, inp, save_mode=G.SAVE_LIGHT, det=True)
     b = _run(w, inp, save_mode=G.SAVE_FULL, det=True)
+    for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_split_launch_light_full_recompute_bitwise():
+    """With the longest document's work on its own stream: light, full and checkpointed runs agree
+    bitwise (the full forward writes the state tape from the split walk, the full backward runs
+    the split reverse walk alone)."""
+    w = [x for x in EDGE if x.name == "split_mid"][0]
+    inp = _dev(syn.make_inputs(w))
+    a = _run(w, inp, save_mode=G.SAVE_LIGHT, det=True)
+    b = _run(w, inp, save_mode=G.SAVE_FULL, det=True, recompute=True)
+    assert torch.equal(b["saved"], b["saved_recompute"])
     for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
         assert torch.equal(a[k], b[k]), k
 
