@@ -191,7 +191,6 @@ def summarize_pmc(fetch_dir, write_dir, out_dir, workload):
     each scaled by bytes / reading of the same counter on the calibration copy (COPY_BYTES read and
     written by one copy kernel, the run's last torch elementwise kernel). Writes
     pmc_<kernel>_<workload>.json per kernel into out_dir and prints a table."""
-    import statistics
     res, scales = {}, {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
@@ -208,20 +207,25 @@ def summarize_pmc(fetch_dir, write_dir, out_dir, workload):
             if n:
                 res.setdefault(n, {}).setdefault(counter, []).append(float(r["Counter_Value"]) * scales[counter])
     os.makedirs(out_dir, exist_ok=True)
-    lines = ["| kernel | launches | FETCH bytes/launch | WRITE bytes/launch | HBM GB/launch |",
+    # a kernel may run as two launches per call (one per part of a split launch plan): traffic is
+    # summed per fwd+bwd step (gdn_tables runs once per call, twice per step)
+    n_steps = max(1, len(res.get("gdn_tables", {}).get("FETCH_SIZE", [])) // 2)
+    lines = ["| kernel | launches/step | FETCH bytes/step | WRITE bytes/step | HBM GB/step |",
              "|---|---|---|---|---|"]
     for name, c in sorted(res.items()):
         if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
             continue
-        fb, wb = statistics.median(c["FETCH_SIZE"]), statistics.median(c["WRITE_SIZE"])
+        fb, wb = sum(c["FETCH_SIZE"]) / n_steps, sum(c["WRITE_SIZE"]) / n_steps
+        per_step = len(c["FETCH_SIZE"]) / n_steps
         src = KERNEL_SOURCE[name]
-        rec = {"kernel": name, "workload": workload, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-               "bytes_per_launch": fb + wb, "launches": len(c["FETCH_SIZE"]), "source": src,
+        rec = {"kernel": name, "workload": workload, "fetch_bytes_per_step": fb, "write_bytes_per_step": wb,
+               "bytes_per_step": fb + wb, "launches_per_step": per_step, "bytes_per_launch": (fb + wb) / per_step,
+               "source": src,
                "source_sha": source_sha(os.path.join(ROOT, "gated_deltanet_fwd_amd", "csrc", src)),
                "copy_scale_bytes_per_unit": scales}
         with open(os.path.join(out_dir, "pmc_%s_%s.json" % (name, workload)), "w") as f:
             json.dump(rec, f, indent=1)
-        lines.append("| `%s` | %d | %.4e | %.4e | %.3f |" % (name, len(c["FETCH_SIZE"]), fb, wb, (fb + wb) / 1e9))
+        lines.append("| `%s` | %g | %.4e | %.4e | %.3f |" % (name, per_step, fb, wb, (fb + wb) / 1e9))
     print("\n".join(lines))
     print("\ncalibration: bytes per counter unit %s (copy of %d bytes read and written)" % (scales, COPY_BYTES))
 

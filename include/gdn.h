@@ -26,9 +26,14 @@
  *   cu_seqlens  [N + 1]      int32, cu_seqlens[0] = 0, nondecreasing, cu_seqlens[N] = T
  *
  * Ownership: the caller allocates every buffer (outputs, the saved set, the workspace). The
- * library never allocates or frees device memory, never synchronises, and enqueues work only
- * on the stream it is given (a hipStream_t; NULL = the default stream). Inputs are not
- * modified. Calls are reentrant; calls that share a workspace or saved buffer must not overlap.
+ * library never allocates or frees device memory and never synchronises the host. Work is
+ * enqueued on the stream it is given (a hipStream_t; NULL = the default stream): all of it runs
+ * after the work enqueued there before the call and before the work enqueued there after it.
+ * When one document is much longer than the others, gdn_fwd, gdn_fwd_recompute (full mode) and
+ * gdn_bwd fork part of their launches onto a second stream the library creates once per device
+ * (default priority, kept until the process ends) and join it back with events, so this
+ * ordering holds as for one stream. Inputs are not modified. Calls are reentrant; calls that
+ * share a workspace or saved buffer must not overlap.
  *
  * Errors: every entry returns GDN_OK or an error code; gdn_last_error() gives a message for
  * the calling thread. All validation (shapes, cu_seqlens, sizes, pointers, alignment, the
