@@ -230,6 +230,43 @@ def summarize_pmc(fetch_dir, write_dir, out_dir, workload):
     print("\ncalibration: bytes per counter unit %s (copy of %d bytes read and written)" % (scales, COPY_BYTES))
 
 
+def summarize_mfma(pmc_dir, command):
+    """MFMA work and utilisation per library kernel from one rocprofv3 --pmc run of this script with
+    the derived counters MfmaUtil (MFMA-busy SIMD cycles / (GPU-active cycles x SIMDs), per cent),
+    MfmaFlopsBF16 and MfmaFlopsF32 (MFMA operations x 512). Durations are the dispatch timestamps of
+    the same run (the profiler runs dispatches one at a time). Prints a markdown table per step."""
+    rows = _csv_rows(pmc_dir, "counter_collection.csv")
+    names = _kernel_names(rows)
+    disp = {}
+    for r in rows:
+        n = names[r["Kernel_Id"]]
+        if not n:
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": n, "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    n_steps = max(1, sum(1 for d in disp.values() if d["name"] == "gdn_tables") // 2)
+    agg = {}
+    for d in disp.values():
+        a = agg.setdefault(d["name"], {"n": 0, "ns": 0.0, "bf16": 0.0, "f32": 0.0, "util_ns": 0.0})
+        a["n"] += 1
+        a["ns"] += d["ns"]
+        a["bf16"] += d.get("MfmaFlopsBF16", 0.0)
+        a["f32"] += d.get("MfmaFlopsF32", 0.0)
+        a["util_ns"] += d.get("MfmaUtil", 0.0) * d["ns"]
+    lines = ["Command (from the repository root on one MI355X):", "", "```", command, "```", "",
+             "| kernel | launches/step | ms/step (profiled) | bf16 MFMA TFLOP/step | f32 MFMA TFLOP/step "
+             "| MFMA busy (% of SIMD cycles) | bf16 MFMA TFLOP/s | of 2.5 PFLOP/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for n, a in sorted(agg.items(), key=lambda x: -x[1]["ns"]):
+        if a["bf16"] == 0 and a["f32"] == 0:
+            continue
+        sec = a["ns"] * 1e-9
+        lines.append("| `%s` | %g | %.3f | %.3f | %.3f | %.1f | %.1f | %.3f |" % (
+            n, a["n"] / n_steps, 1e3 * sec / n_steps, a["bf16"] / n_steps / 1e12, a["f32"] / n_steps / 1e12,
+            a["util_ns"] / a["ns"], a["bf16"] / sec / 1e12, a["bf16"] / sec / PEAK_BF16))
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, command):
     """Per-kernel count, total and average duration from a rocprofv3 --kernel-trace CSV."""
     import statistics
@@ -264,11 +301,17 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with "
                          "--copy-calibration into per-kernel HBM traffic records; no GPU is used")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "COMMAND"),
+                    help="MFMA utilisation and work per kernel from a rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 "
+                         "MfmaFlopsF32 run of this script; no GPU")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
                     help="per-kernel durations from a rocprofv3 --kernel-trace run of this script; no GPU")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, workload=args.workload)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
@@ -276,7 +319,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (it would shard the "
-              "q/k-head groups or the sequence across GPUs; see DESIGN.md)", file=sys.stderr)
+              "q/k-head groups or the sequence across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
