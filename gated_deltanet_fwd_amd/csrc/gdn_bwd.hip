@@ -361,6 +361,22 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   f32x4 dQacc[NT2], dKacc[NT2];
 #pragma unroll
   for (int t = 0; t < NT2; ++t) dQacc[t] = dKacc[t] = zero4();
+  // qh . dQacc on this lane's C rows, over this lane's columns
+  auto qdot_acc = [&](int row0, int lg, int half, int lr) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int t = 0; t < NT2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lg * 4 + i, dk = 16 * (half * NT2 + t) + lr;
+        acc[i] += (float)sm.sQ[r * SK + dk] * dQacc[t][i];
+      }
+    const f32x4 rq_r = *reinterpret_cast<const f32x4*>(sm.srq + row0 + lg * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= rq_r[i];
+    return acc;
+  };
+  f32x4 qprev = zero4(); // qdot_acc() after the previous head
 
   for (int hh = 0; hh < h_count; ++hh) {
     const int h = h_first + hh;
@@ -383,8 +399,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     }
     const float a_b = __expf(sm.sG[arow]);
 
-    float zp[4] = {0.f, 0.f, 0.f, 0.f}, dbx[4] = {0.f, 0.f, 0.f, 0.f}, dbr[4] = {0.f, 0.f, 0.f, 0.f},
-          dbo[4] = {0.f, 0.f, 0.f, 0.f};
+    float zp[4] = {0.f, 0.f, 0.f, 0.f}, dbx[4] = {0.f, 0.f, 0.f, 0.f}, dbr[4] = {0.f, 0.f, 0.f, 0.f};
     float sdot = 0.f;
     f32x4 dP[2], dA[2];
     dP[0] = dP[1] = dA[0] = dA[1] = zero4();
@@ -413,28 +428,24 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
 
       // this wave's 16 x 16 tile of the slice: rows row0.., slice columns 16*half..
       const int cs = 16 * half;
-      f32x4 ksv = zero4(), kdv = zero4(), qsv = zero4(), pdv = zero4();
+      f32x4 ksv = zero4(), kdv = zero4(), pdv = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 bS = lds8(B.sS, SK, cs + lr, ks * 32 + lg * 8);
         const bf16x8 fk = lds8(sm.sK, SK, arow, ks * 32 + lg * 8);
-        ksv = mfma(fk, bS, ksv);
-        qsv = mfma(lds8(sm.sQ, SK, arow, ks * 32 + lg * 8), bS, qsv);
+        ksv = mfma(fk, lds8(B.sS, SK, cs + lr, ks * 32 + lg * 8), ksv);
         kdv = mfma(fk, lds8(B.sdS, SK, cs + lr, ks * 32 + lg * 8), kdv);
       }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) pdv = mfma(lds8(sm.sP, SA, arow, k2 * 32 + lg * 8), lds_tr8(B.sdO, SDO, k2 * 32, cs), pdv);
       float xu[4], x[4], dr[4];
-      const f32x4 rk_r = rk4(), rq_r = rq4();
+      const f32x4 rk_r = rk4();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i, cc = cs + lr;
         const float vv = (float)B.sV[r * SV + cc];
-        const float dov = (float)B.sdO[r * SDO + cc];
         xu[i] = vv - brow[i] * rk_r[i] * ksv[i];
         x[i] = beta_r[i] * xu[i];
         dr[i] = pdv[i] + dec_r[i] * rk_r[i] * kdv[i];
-        dbo[i] += rq_r[i] * qsv[i] * dov;
       }
       lds_store4_t(B.sXT, SA, cs + lr, row0 + lg * 4, x[0], x[1], x[2], x[3]);
       lds_store4_t(B.sdRT, SA, cs + lr, row0 + lg * 4, dr[0], dr[1], dr[2], dr[3]);
@@ -490,6 +501,14 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     // ---- per-head tail; the next head's tiles load meanwhile
     if (hh + 1 < h_count) prefetch_head(h + 1, tid);
     auto& T = sm.u.t;
+    // b_i (Qh S dO^T)_ii: the slices added diag(b) dO S^T of this head to dQacc, so it is the
+    // growth of qh_i . dQacc_i over the slice loop
+    float dbo[4];
+    {
+      const f32x4 qn = qdot_acc(row0, lg, half, lr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dbo[i] = qn[i] - qprev[i];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       zp[i] = row_sum16(zp[i]);
@@ -505,7 +524,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i;
         sm.sRow[half][0][r] = zp[i];
-        sm.sRow[half][1][r] = dbo[i] + dbr[i];
+        sm.sRow[half][1][r] = dbo[i] + brow[i] * dbr[i];
         sm.sRow[half][2][r] = dbx[i];
       }
     }
@@ -619,6 +638,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         }
       }
     }
+    qprev = qdot_acc(row0, lg, half, lr); // dQacc is complete for this head
     if (w == 0) {
       // lane l takes row 63 - l, so the in-chunk reverse cumulative sum is a prefix sum over lanes
       const int r = 63 - lane;
@@ -632,7 +652,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       const float dbeta = sm.sRow[0][2][r] + sm.sRow[1][2][r] + sm.sRow[0][3][r] + sm.sRow[1][3][r];
       const float zd = ok ? z * dec : 0.f;
       const float zsum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_prefix_sum(zd)), 63));
-      float dG = keepf(rows - cols + __expf(g_r1) * db - zd, ok);
+      float dG = keepf(rows - cols + db - zd, ok); // db carries its factor exp(G)
       float sd = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) sd += sm.sred[q];
