@@ -15,6 +15,8 @@
 //   with dGam = mask(dP o Qk) + dL o (beta Kk), db_i = qh_i.(dO S^T)_i - beta_i (Kh S)_i.dX_i,
 //   Z_i = (Kh dSn)_i . R_i; dg is the in-chunk reverse cumulative sum of dG. dq, dk are the
 //   L2-norm backward of the sums of dQh, dKh over the value heads that share the q/k head.
+#include <atomic>
+
 #include "gdn_walks.h"
 
 namespace gdn {
@@ -253,12 +255,24 @@ struct GradSmem {
 template <int D, typename TI, bool DET>
 __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   if (a.status[0]) return;
-  const int c = launch_chunk(a, blockIdx.x);
-  const int len = a.c_len[c];
-  if (len <= 0) return;
-  const int t0 = a.c_t0[c];
-  const int j = DET ? (int)blockIdx.y : (int)blockIdx.y / a.G;
-  const int h_first = DET ? j * a.G : (int)blockIdx.y;
+  // Persistent: workgroup b takes items b, b + gridDim.x, ... (item = chunk x per-chunk index y;
+  // y is the q/k head, or the value head in atomic mode). The next item's first loads are issued
+  // during the current item's last head and before its epilogue, so they are in flight while it
+  // finishes instead of at the start of a new workgroup.
+  const int nj = DET ? a.H : a.HV;
+  const int n_items = a.c_count * nj;
+  int item = blockIdx.x;
+  if (item >= n_items) return;
+  int c, j, h_first, len, t0;
+  auto decode = [&](int it, int& ci, int& ji, int& hi, int& li, int& ti) {
+    const int x = it / nj, y = it - x * nj;
+    ci = launch_chunk(a, x);
+    ji = DET ? y : y / a.G;
+    hi = DET ? y * a.G : y;
+    li = __builtin_amdgcn_readfirstlane(a.c_len[ci]); // uniform: kept in scalar registers
+    ti = __builtin_amdgcn_readfirstlane(a.c_t0[ci]);
+  };
+  decode(item, c, j, h_first, len, t0);
   const int h_count = DET ? a.G : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rt = w & 3, half = w >> 2;
@@ -284,7 +298,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   bf16x8 nS, ndS, nx; // slice: S^T / dSn^T piece; dO piece (threads < 256) or V piece (threads >= 256)
   bf16x8 nA, nP;      // head: A and P row pieces
   float nGB;          // head: G (wave 0) or beta (other waves) of row tid % 64
-  auto prefetch = [&](int h, int cv, int tid) {
+  auto prefetch = [&](int c, int t0, int len, int h, int cv, int tid) {
     const int dvl = min(tid / (D / 8), DC - 1), pc = tid % (D / 8); // 32 rows x D/8 pieces
     const size_t off = ((size_t)c * a.HV + h) * D * D + (size_t)(cv * DC + dvl) * D + pc * 8;
     nS = *reinterpret_cast<const bf16x8*>(htape + off);
@@ -293,13 +307,13 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     const TI* src = tid < 256 ? dop : vp;
     nx = IO<TI>::load8(src + ((size_t)(t0 + r) * a.HV + h) * D + cv * DC + pv * 8);
   };
-  auto store_head = [&](int tid) {
+  auto store_head = [&](int len, int tid) {
     const int r = tid >> 3, pc = tid & 7;
     *reinterpret_cast<bf16x8*>(sm.sA + r * SA + pc * 8) = keep8(nA, r < len);
     *reinterpret_cast<bf16x8*>(sm.sP + r * SA + pc * 8) = keep8(nP, r < len);
     if (tid < 2 * CH) (tid < CH ? sm.sG : sm.sB)[tid & 63] = keepf(nGB, (tid & 63) < len);
   };
-  auto prefetch_head = [&](int h, int tid) {
+  auto prefetch_head = [&](int c, int t0, int len, int h, int tid) {
     const int r = min(tid >> 3, len - 1), pc = tid & 7;
     nA = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8);
     // waves 0 and 1 gather 64 rows; the others read one row (one cache line, no branch)
@@ -308,21 +322,40 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     nP = *reinterpret_cast<const bf16x8*>(qkt + ((size_t)c * a.HV + h) * CH * CH + r * CH + pc * 8);
   };
 
-  // ---- K, Q rows and their norms (the first head's tiles are loaded alongside); Kk = Kh Kh^T,
-  // Qk = Qh Kh^T on this wave's tiles
+  // K, Q rows and their norms of an item
   constexpr int KQ_IT = CH * (D / 8) / GRAD_THREADS;
   static_assert(KQ_IT * GRAD_THREADS == CH * (D / 8), "K/Q staging covers the tile");
   bf16x8 kv[KQ_IT], qv[KQ_IT];
+  float rkv, rqv;
+  auto load_kq = [&](int t0, int len, int j, int tid) {
 #pragma unroll
-  for (int it = 0; it < KQ_IT; ++it) {
-    const int idx = tid + it * GRAD_THREADS, r = min(idx / (D / 8), len - 1), pc = idx % (D / 8);
-    kv[it] = IO<TI>::load8(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
-    qv[it] = IO<TI>::load8(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
-  }
-  const int rr0 = tid < CH ? min(lane, len - 1) : 0; // only wave 0 stages the norms
-  const float rkv = a.rk[(size_t)j * a.T + t0 + rr0], rqv = a.rq[(size_t)j * a.T + t0 + rr0];
-  prefetch_head(h_first, tid);
-  prefetch(h_first, 0, tid);
+    for (int it = 0; it < KQ_IT; ++it) {
+      const int idx = tid + it * GRAD_THREADS, r = min(idx / (D / 8), len - 1), pc = idx % (D / 8);
+      kv[it] = IO<TI>::load8(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
+      qv[it] = IO<TI>::load8(qp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8);
+    }
+    const int rr0 = tid < CH ? min(tid & 63, len - 1) : 0; // only wave 0 stages the norms
+    rkv = a.rk[(size_t)j * a.T + t0 + rr0];
+    rqv = a.rq[(size_t)j * a.T + t0 + rr0];
+  };
+  load_kq(t0, len, j, tid);
+  prefetch_head(c, t0, len, h_first, tid);
+  prefetch(c, t0, len, h_first, 0, tid);
+
+  for (;;) {
+  // lane indices re-derived from an opaque thread id per item, as in the head loop below (else
+  // lane-dependent addresses are hoisted out of the item loop and held in registers throughout)
+  int tid_i = threadIdx.x;
+  asm volatile("" : "+v"(tid_i));
+  const int tid = tid_i, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w & 3, half = w >> 2, lr = lane & 15, lg = lane >> 4, row0 = 16 * rt, arow = row0 + lr;
+  // the next item (this one again after the last: its loads then repeat this item's, unused)
+  const int item_n = item + (int)gridDim.x;
+  const bool has_next = item_n < n_items;
+  int c_n, j_n, hf_n, len_n, t0_n;
+  decode(has_next ? item_n : item, c_n, j_n, hf_n, len_n, t0_n);
+
+  // ---- stage K, Q and the norms; Kk = Kh Kh^T, Qk = Qh Kh^T on this wave's tiles
 #pragma unroll
   for (int it = 0; it < KQ_IT; ++it) {
     const int idx = tid + it * GRAD_THREADS, r = idx / (D / 8), pc = idx % (D / 8);
@@ -353,7 +386,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     sm.sKQ[0][w][c2][lane] = Kk;
     sm.sKQ[1][w][c2][lane] = Qk;
   }
-  store_head(tid); // the first head's tiles (not read above)
+  store_head(len, tid); // the first head's tiles (not read above)
   // norms of this lane's C rows, re-read from LDS where used
   auto rk4 = [&]() { return *reinterpret_cast<const f32x4*>(sm.srk + row0 + lg * 4); };
   auto rq4 = [&]() { return *reinterpret_cast<const f32x4*>(sm.srq + row0 + lg * 4); };
@@ -420,10 +453,13 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         if (tid < 256) *reinterpret_cast<bf16x8*>(B.sdO + r * SDO + pv * 8) = xv;
         else *reinterpret_cast<bf16x8*>(B.sV + r * SV + pv * 8) = xv;
       }
-      // the next slice, or the next head's first (this head's again after the last head): always
-      // a load, so no branch leaves the wait counts unsure which registers are still loading
-      if (cv + 1 < NDC) prefetch(h, cv + 1, tid);
-      else prefetch(hh + 1 < h_count ? h + 1 : h, 0, tid);
+      // the next slice, the next head's first, or after the last head the next item's first:
+      // always a load, so no branch leaves the wait counts unsure which registers are loading
+      {
+        const bool nslice = cv + 1 < NDC, nitem = !nslice && hh + 1 == h_count;
+        prefetch(nitem ? c_n : c, nitem ? t0_n : t0, nitem ? len_n : len, nslice ? h : nitem ? hf_n : h + 1,
+                 nslice ? cv + 1 : 0, tid);
+      }
       __syncthreads();
 
       // this wave's 16 x 16 tile of the slice: rows row0.., slice columns 16*half..
@@ -498,8 +534,11 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       }
     }
 
-    // ---- per-head tail; the next head's tiles load meanwhile
-    if (hh + 1 < h_count) prefetch_head(h + 1, tid);
+    // ---- per-head tail; the next head's (or the next item's first head's) tiles load meanwhile
+    {
+      const bool nitem = hh + 1 == h_count;
+      prefetch_head(nitem ? c_n : c, nitem ? t0_n : t0, nitem ? len_n : len, nitem ? hf_n : h + 1, tid);
+    }
     auto& T = sm.u.t;
     // b_i (Qh S dO^T)_ii: the slices added diag(b) dO S^T of this head to dQacc, so it is the
     // growth of qh_i . dQacc_i over the slice loop
@@ -680,9 +719,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     }
     if (hh + 1 < h_count) {
       __syncthreads(); // this head's tail is done with the shared tiles
-      store_head(tid);
+      store_head(len, tid);
     }
   }
+  load_kq(t0_n, len_n, j_n, tid); // the next item's K, Q rows and norms, in flight during the epilogue
 
   // dg, dbeta of the heads held in LDS (the last head's are visible after one more barrier)
   __syncthreads();
@@ -741,13 +781,38 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         IO<TI>::store1(dkp + ((size_t)(t0 + r) * a.H + j) * D + dk, dkv);
       }
   }
+  if (!has_next) break;
+  __syncthreads(); // the epilogue's reads of K, Q, the norms and the row sums are done
+  item = item_n;
+  c = c_n;
+  j = j_n;
+  h_first = hf_n;
+  len = len_n;
+  t0 = t0_n;
+  }
 }
 
 template <int D, typename TI>
 static int chunk_grad_t(const Args& a, int det, hipStream_t s) {
   if (a.c_count == 0) return 0;
-  if (det) hipLaunchKernelGGL((k_chunk_grad<D, TI, true>), dim3(a.c_count, a.H), dim3(GRAD_THREADS), 0, s, a);
-  else hipLaunchKernelGGL((k_chunk_grad<D, TI, false>), dim3(a.c_count, a.HV), dim3(GRAD_THREADS), 0, s, a);
+  // one persistent workgroup per resident slot (CUs x workgroups per CU, found once per process)
+  static std::atomic<int> slots[2]{{0}, {0}};
+  int n = slots[det].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int dev = 0, ncu = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return (int)hipErrorInvalidDevice;
+    const hipError_t e = det ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_chunk_grad<D, TI, true>, GRAD_THREADS, 0)
+                             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_chunk_grad<D, TI, false>, GRAD_THREADS, 0);
+    if (e != hipSuccess) return (int)e;
+    n = ncu * (per > 0 ? per : 1);
+    slots[det].store(n, std::memory_order_relaxed);
+  }
+  const long items = (long)a.c_count * (det ? a.H : a.HV);
+  const dim3 grid((unsigned)(items < n ? items : n));
+  if (det) hipLaunchKernelGGL((k_chunk_grad<D, TI, true>), grid, dim3(GRAD_THREADS), 0, s, a);
+  else hipLaunchKernelGGL((k_chunk_grad<D, TI, false>), grid, dim3(GRAD_THREADS), 0, s, a);
   return (int)hipGetLastError();
 }
 
