@@ -5,6 +5,7 @@
 // (one per device, default priority), forked from and joined back into the caller's stream.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -107,7 +108,8 @@ SavedLayout saved_layout(const Sizes& s, int full) {
 }
 
 struct WorkLayout {
-  size_t seq_c0, c_t0, c_len, seq_order, pair_order, status, discard, rk, rq, qk, htape, dstape, dqacc, dkacc, total;
+  size_t seq_c0, c_t0, c_len, seq_order, pair_order, status, discard, rk, rq, qk, htape, dstape, dqacc, dkacc, state,
+      total;
 };
 
 WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
@@ -128,6 +130,8 @@ WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
   L.rk = take((size_t)s.T * s.H * 4);
   L.rq = take((size_t)s.T * s.H * 4);
   L.qk = take((size_t)s.NT * s.HV * kChunk * kChunk * 2);
+  // the state handed from one piece of the longest document's walk to the next
+  if (op != GDN_OP_BWD) L.state = take((size_t)s.HV * s.D * s.D * 4);
   if (op == GDN_OP_BWD) {
     if (!full) L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
     L.dstape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
@@ -337,6 +341,9 @@ void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
   if (W.dkacc) a.dkacc = (float*)(b + W.dkacc);
 }
 
+// Workspace area that holds the state between the pieces of a split walk (forward ops only).
+float* piece_state(const WorkLayout& W, void* ws) { return W.state ? (float*)((char*)ws + W.state) : nullptr; }
+
 void bind_saved(gdn::Args& a, const SavedLayout& L, void* saved) {
   char* b = (char*)saved;
   a.akk = (uint16_t*)(b + L.akk);
@@ -416,11 +423,51 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
     gdn::Args aa = a, ab = a;
     range_a(aa, sp);
     range_b(ab, sp);
-    LAUNCH("gdn_intra", gdn::launch_intra(aa, 0, stream));
+    // The longest document in pieces of at least 384 chunks (at most 4): each piece's walk needs
+    // only that piece's intra launch, and starts from the state the previous piece left in the
+    // workspace (f32, so the result is the same as one walk over the document).
+    const int pieces = std::max(1, std::min(4, sp.cA / 384));
+    float* st = piece_state(W, workspace);
+    gdn::Args ap[4];
+    for (int i = 0; i < pieces; ++i) {
+      ap[i] = aa;
+      const int lo = (int)((long)sp.cA * i / pieces), hi = (int)((long)sp.cA * (i + 1) / pieces);
+      ap[i].c_base = sp.cA0 + lo;
+      ap[i].c_count = hi - lo;
+      ap[i].piece_lo = lo;
+      ap[i].piece_hi = hi;
+      ap[i].state_in = i > 0 ? st : nullptr;
+      ap[i].state_out = i + 1 < pieces ? st : nullptr;
+      if (i + 1 < pieces) ap[i].want_ht = 0;
+    }
+    LAUNCH("gdn_intra", gdn::launch_intra(ap[0], 0, stream));
     CHECK(stream_wait((hipStream_t)stream, side));
-    LAUNCH(walk_name, gdn::launch_walk_fwd(aa, write_o, full, stream));
+    hipEvent_t ready[4] = {nullptr, nullptr, nullptr, nullptr};
+    for (int i = 1; i < pieces; ++i) {
+      LAUNCH_ON(side, "gdn_intra", gdn::launch_intra(ap[i], 0, side));
+      if (hipEventCreateWithFlags(&ready[i], hipEventDisableTiming) != hipSuccess ||
+          hipEventRecord(ready[i], side) != hipSuccess) {
+        for (hipEvent_t e : ready)
+          if (e) hipEventDestroy(e);
+        return fail(GDN_EHIP, "piece event failed");
+      }
+    }
     LAUNCH_ON(side, "gdn_intra", gdn::launch_intra(ab, 0, side));
     LAUNCH_ON(side, walk_name, gdn::launch_walk_fwd(ab, write_o, full, side));
+    int rc = GDN_OK;
+    for (int i = 0; i < pieces && rc == GDN_OK; ++i) {
+      if (i > 0 && hipStreamWaitEvent((hipStream_t)stream, ready[i], 0) != hipSuccess)
+        rc = fail(GDN_EHIP, "piece event wait failed");
+      else {
+        hipEvent_t t0_ = timing_begin(stream);
+        const int e_ = gdn::launch_walk_fwd(ap[i], write_o, full, stream);
+        timing_end(walk_name, t0_, stream);
+        if (e_ != 0) rc = fail(GDN_EHIP, "%s: %s", walk_name, hipGetErrorString((hipError_t)e_));
+      }
+    }
+    for (hipEvent_t e : ready)
+      if (e) hipEventDestroy(e);
+    if (rc != GDN_OK) return rc;
     CHECK(stream_wait(side, (hipStream_t)stream));
   }
   if (full) LAUNCH("gdn_wy_full", gdn::launch_wy_full(a, stream));

@@ -451,6 +451,10 @@ void whole_range(Args& a) {
   a.c_skip = 0;
   a.c_count = a.NT;
   a.grp_split = 0;
+  a.piece_lo = 0;
+  a.piece_hi = 0x7fffffff;
+  a.state_in = nullptr;
+  a.state_out = nullptr;
 }
 
 template <int D, typename TI>

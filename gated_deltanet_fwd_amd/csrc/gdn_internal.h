@@ -67,6 +67,13 @@ struct Args {
   int grp_off, grp_end, pair_off;
   int c_base, c_skip_at, c_skip, c_count;
   int grp_split; // k_tables: paired-walk orders of the groups [grp_split, N H), then [0, grp_split)
+  // Forward and tape walks over a piece of each document: its chunks [piece_lo, piece_hi) counted
+  // from the document's first. state_in (if set) replaces h0 as the starting state and state_out
+  // (if set) receives the final state, both f32 [HV, d, d]: a launch that uses them covers one
+  // document, and consecutive pieces hand the state over through them.
+  int piece_lo, piece_hi;
+  const float* state_in;
+  float* state_out;
 };
 
 // Bytes of the workspace area that takes the stores of lanes past a chunk's end.

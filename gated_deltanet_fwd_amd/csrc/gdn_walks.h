@@ -54,7 +54,9 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
   if (!cm.valid) return;
   const int n = a.seq_order[cm.rank];
   const int j = cm.j, h = j * a.G + cm.gi;
-  const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
+  // this launch's piece of the document: chunks [piece_lo, piece_hi) from its first
+  const int c_begin = a.seq_c0[n] + a.piece_lo;
+  const int c_end = a.seq_c0[n] + min(a.seq_c0[n + 1] - a.seq_c0[n], a.piece_hi);
   constexpr int NT = walk_threads<D>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -71,8 +73,8 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
   const int v0 = 16 * w;
-  // chunk c of the document starts at token cu[n] + 64 (c - c_begin)
-  const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
+  // chunk c of the piece starts at token doc_t0 + 64 (c - c_begin)
+  const int doc_t0 = a.cu[n] + a.piece_lo * CH, doc_t1 = a.cu[n + 1];
 
   // ---- staging: global -> registers (issued before a chunk's compute) -> LDS (after it).
   // Rows past the chunk's end re-read its last row: finite values whose contributions vanish
@@ -145,7 +147,9 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 16 * rt + 4 * lg + i;
-      S[rt][i] = a.has_h0 ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] : 0.f;
+      S[rt][i] = a.state_in ? a.state_in[((size_t)h * D + d) * D + v0 + lr]
+                 : a.has_h0   ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr]
+                              : 0.f;
     }
 
   auto step = [&](int b, int c) {
@@ -279,6 +283,12 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
     step(b, c);
     store_chunk(b ^ 1, cn);
     __syncthreads();
+  }
+  if (a.state_out) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.state_out[((size_t)h * D + 16 * rt + 4 * lg + i) * D + v0 + lr] = S[rt][i];
   }
   if (WRITE_O && a.want_ht) {
 #pragma unroll

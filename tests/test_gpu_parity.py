@@ -154,6 +154,20 @@ def test_split_launch_light_full_recompute_bitwise():
         assert torch.equal(a[k], b[k]), k
 
 
+def test_split_walk_in_pieces():
+    """The longest document (770 chunks) is walked in two pieces that hand the f32 state over
+    through the workspace; with h0, ht and dht, against the oracle, and light == full bitwise
+    (the full forward's state tape comes from the pieced walk)."""
+    w = syn.custom("pieces", [3000, 49252, 700], 1, 2, 64, "bf16", has_h0=True, want_ht=True, has_dht=True,
+                   seed=14)
+    inp = _dev(syn.make_inputs(w))
+    a = _run(w, inp, save_mode=G.SAVE_LIGHT, det=True)
+    _check_all(w, inp, a)
+    b = _run(w, inp, save_mode=G.SAVE_FULL, det=True)
+    for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_recompute_saved_set_bitwise_and_ckpt():
     w = EDGE[0]
     inp = _dev(syn.make_inputs(w))
@@ -229,6 +243,26 @@ def test_pack262k_deterministic_repeat():
     b = _run(w, inp, det=True)
     assert torch.equal(dq, b["dq"]) and torch.equal(dk, b["dk"])
     _check_all(w, inp, b, docs=[3], heads=[5])
+
+
+def test_pack262k_longest_document_alone_bitwise():
+    """The pack's longest document (98,304 tokens) runs apart from the others and its walk in
+    pieces; run alone (one document: one launch, one walk) it gives the same bits."""
+    w, inp = _big("pack262k")
+    a = _run(w, inp, det=True)
+    L0 = w.lengths[0]
+    w1 = syn.custom("pack_doc0", [L0], w.H, w.HV, w.d, w.dtype, has_h0=w.has_h0, want_ht=True)
+    one = {k: (v[:L0].contiguous() if v is not None and k not in ("cu_seqlens", "h0", "dht") else v)
+           for k, v in inp.items()}
+    one["cu_seqlens"] = torch.tensor([0, L0], dtype=torch.int32, device=DEV)
+    a_o = a["o"][:L0].clone()
+    grads = {k: a[k][:L0].clone() for k in ("dq", "dk", "dv", "dg", "dbeta")}
+    del a
+    torch.cuda.empty_cache()
+    b = _run(w1, one, det=True)
+    assert torch.equal(a_o, b["o"])
+    for k, v in grads.items():
+        assert torch.equal(v, b[k]), k
 
 
 def test_cp4share_h0_ht_dh0():
