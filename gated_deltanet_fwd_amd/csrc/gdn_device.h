@@ -183,6 +183,22 @@ __device__ __forceinline__ void lds_store4_t(bf16* base, int stride, int col, in
   *reinterpret_cast<bf16x4*>(base + col * stride + row) = v;
 }
 
+// Raw buffer resource over [base, base + bytes) (gfx9 word 3). A buffer store whose offset lies
+// past the end is dropped by the hardware, so lanes past a chunk's end store without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte buffer load at a byte offset; bytes past the resource's end read as zero.
+__device__ __forceinline__ i32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, int off_bytes) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off_bytes, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(const bf16x8& v, __amdgpu_buffer_rsrc_t r, int off_bytes) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off_bytes, 0, 0);
+}
+
 // ---------------------------------------------------------------------------------------
 // io dtype access (bf16 or f32)
 
@@ -197,6 +213,17 @@ struct IO<bf16> {
     for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
   }
   static __device__ __forceinline__ bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  // 8 consecutive values through a buffer resource (zeros past its end); off in elements
+  static __device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(bf16x8, buf_load16(r, off * 2));
+  }
+  // 4 consecutive values through a buffer resource (dropped past its end); off in elements
+  static __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, int off, const float x[4]) {
+    i32x2_t v;
+    v[0] = (int)pack_bf16x2(x[0], x[1]);
+    v[1] = (int)pack_bf16x2(x[2], x[3]);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off * 2, 0, 0);
+  }
   static __device__ __forceinline__ float load1(const bf16* p) { return (float)*p; }
   static __device__ __forceinline__ void store1(bf16* p, float x) { *p = (bf16)x; }
   // 4 consecutive values (8-byte aligned)
@@ -222,22 +249,24 @@ struct IO<float> {
     return r;
   }
   static __device__ __forceinline__ float load1(const float* p) { return *p; }
+  static __device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int off) {
+    const float4 a = __builtin_bit_cast(float4, buf_load16(r, off * 4));
+    const float4 b = __builtin_bit_cast(float4, buf_load16(r, off * 4 + 16));
+    bf16x8 v;
+    v[0] = (bf16)a.x; v[1] = (bf16)a.y; v[2] = (bf16)a.z; v[3] = (bf16)a.w;
+    v[4] = (bf16)b.x; v[5] = (bf16)b.y; v[6] = (bf16)b.z; v[7] = (bf16)b.w;
+    return v;
+  }
+  static __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, int off, const float x[4]) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, make_float4(x[0], x[1], x[2], x[3])), r,
+                                           off * 4, 0, 0);
+  }
   static __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
   // 4 consecutive values (16-byte aligned)
   static __device__ __forceinline__ void store4(float* p, const float x[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
   }
 };
-
-// Raw buffer resource over [base, base + bytes) (gfx9 word 3). A buffer store whose offset lies
-// past the end is dropped by the hardware, so lanes past a chunk's end store without a branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ void buf_store16(const bf16x8& v, __amdgpu_buffer_rsrc_t r, int off_bytes) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off_bytes, 0, 0);
-}
 
 // Sum over the 16 lanes that share l / 16 (the lanes of one MFMA output row group).
 __device__ __forceinline__ float sum16(float x) {

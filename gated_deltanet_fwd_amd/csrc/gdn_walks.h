@@ -52,11 +52,14 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
   if (a.status[0]) return;
   const ChainMap cm = decode_chain(blk, a, 1);
   if (!cm.valid) return;
-  const int n = a.seq_order[cm.rank];
+  // chain constants are uniform: held in scalar registers (the chunk's buffer resources below
+  // are built from them)
+  const int n = __builtin_amdgcn_readfirstlane(a.seq_order[cm.rank]);
   const int j = cm.j, h = j * a.G + cm.gi;
   // this launch's piece of the document: chunks [piece_lo, piece_hi) from its first
-  const int c_begin = a.seq_c0[n] + a.piece_lo;
-  const int c_end = a.seq_c0[n] + min(a.seq_c0[n + 1] - a.seq_c0[n], a.piece_hi);
+  const int c_doc = __builtin_amdgcn_readfirstlane(a.seq_c0[n]);
+  const int c_begin = c_doc + a.piece_lo;
+  const int c_end = c_doc + min(__builtin_amdgcn_readfirstlane(a.seq_c0[n + 1]) - c_doc, a.piece_hi);
   constexpr int NT = walk_threads<D>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -74,33 +77,47 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
   const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
   const int v0 = 16 * w;
   // chunk c of the piece starts at token doc_t0 + 64 (c - c_begin)
-  const int doc_t0 = a.cu[n] + a.piece_lo * CH, doc_t1 = a.cu[n + 1];
+  const int doc_t0 = __builtin_amdgcn_readfirstlane(a.cu[n]) + a.piece_lo * CH;
+  const int doc_t1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
 
   // ---- staging: global -> registers (issued before a chunk's compute) -> LDS (after it).
-  // Rows past the chunk's end re-read its last row: finite values whose contributions vanish
-  // because beta and the row factors are zero there and P is masked.
+  // The token tiles are read through buffer resources bounded at the chunk's last row, at
+  // per-lane offsets fixed for the whole walk: rows past the chunk's end read as zeros, whose
+  // contributions vanish (beta and the row factors are zero there and P is masked).
+  int oK[PPT], oV[PPT], oA[APT], oP[APT]; // element offsets of this thread's pieces
+#pragma unroll
+  for (int it = 0; it < PPT; ++it) {
+    const int p = tid + NT * it, row = p / RP, pc = p % RP;
+    oK[it] = row * a.H * D + pc * 8;
+    oV[it] = row * a.HV * D + pc * 8;
+  }
+#pragma unroll
+  for (int it = 0; it < APT; ++it) {
+    const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+    oA[it] = row * a.HV * CH + pc * 8;
+    oP[it] = row * CH + pc * 8;
+  }
   bf16x8 rK[PPT], rV[PPT], rQ[PPT], rA[APT], rP[APT];
   float sg = 0.f, sglast = 0.f, sbeta = 0.f, srk = 0.f, srq = 0.f;
   auto load_chunk = [&](int c) {
     const int t0 = doc_t0 + (c - c_begin) * CH;
     const int last = min(CH, doc_t1 - t0) - 1;
-    const TI* kc = kp + ((size_t)t0 * a.H + j) * D;
-    const TI* qc = qp + ((size_t)t0 * a.H + j) * D;
-    const TI* vc = vp + ((size_t)t0 * a.HV + h) * D;
+    const int kq_bytes = (last * a.H * D + D) * (int)sizeof(TI), v_bytes = (last * a.HV * D + D) * (int)sizeof(TI);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + ((size_t)t0 * a.H + j) * D, kq_bytes);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp + ((size_t)t0 * a.H + j) * D, kq_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp + ((size_t)t0 * a.HV + h) * D, v_bytes);
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
-      const int p = tid + NT * it, row = min(p / RP, last), pc = p % RP;
-      rK[it] = IO<TI>::load8(kc + row * a.H * D + pc * 8);
-      rV[it] = IO<TI>::load8(vc + row * a.HV * D + pc * 8);
-      if (WRITE_O) rQ[it] = IO<TI>::load8(qc + row * a.H * D + pc * 8);
+      rK[it] = IO<TI>::bload8(kr, oK[it]);
+      rV[it] = IO<TI>::bload8(vr, oV[it]);
+      if (WRITE_O) rQ[it] = IO<TI>::bload8(qr, oK[it]);
     }
-    const bf16* ac = akk + ((size_t)t0 * a.HV + h) * CH;
-    const bf16* pc_ = pm + ((size_t)c * a.HV + h) * CH * CH;
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(akk + ((size_t)t0 * a.HV + h) * CH, (last * a.HV * CH + CH) * 2);
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(pm + ((size_t)c * a.HV + h) * CH * CH, CH * CH * 2);
 #pragma unroll
     for (int it = 0; it < APT; ++it) {
-      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
-      rA[it] = *reinterpret_cast<const bf16x8*>(ac + min(row, last) * a.HV * CH + pc * 8);
-      if (WRITE_O) rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
+      rA[it] = IO<bf16>::bload8(ar, oA[it]);
+      if (WRITE_O) rP[it] = IO<bf16>::bload8(pr, oP[it]);
     }
     {
       // per-token scalars of row `lane`, staged by wave 0; the other waves load one row (the
@@ -242,7 +259,9 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
     }
     // O^T = diag-column(b rq) (Q S)^T + (P R)^T; lane holds O[t][v0 + 4 lg .. +3], t = 16 mt + lr
     if (WRITE_O) {
-      TI* op = (TI*)a.o + ((size_t)t0 * a.HV + h) * D + v0 + 4 * lg;
+      // rows of the chunk only: stores past the resource's end (tokens >= len) are dropped
+      const __amdgpu_buffer_rsrc_t orr = make_rsrc((TI*)a.o + ((size_t)t0 * a.HV + h) * D,
+                                                   ((len - 1) * a.HV * D + D) * (int)sizeof(TI));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc = zero4();
@@ -253,9 +272,7 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
         float ov[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = __builtin_fmaf(sq, qsT[mt][i], acc[i]);
-        // tokens past the chunk's end go to the discard area: every lane stores, so no branch
-        // hides the number of outstanding stores from the wait counts
-        IO<TI>::store4(t < len ? op + (size_t)t * a.HV * D : reinterpret_cast<TI*>(a.discard) + 4 * lane, ov);
+        IO<TI>::bstore4(orr, t * a.HV * D + v0 + 4 * lg, ov);
       }
     }
     // S <- gamma S + K^T diag(exp(G_last - G) rk) R
