@@ -189,9 +189,9 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
     for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(S[2 * kd], S[2 * kd + 1]);
     if (WRITE_TAPE) {
       // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
-      bf16* tp = reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D + (size_t)(v0 + lr) * D + 8 * lg;
+      const __amdgpu_buffer_rsrc_t tr = make_rsrc(reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D, D * D * 2);
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) *reinterpret_cast<bf16x8*>(tp + 32 * kd) = sb[kd];
+      for (int kd = 0; kd < KD; ++kd) buf_store16(sb[kd], tr, ((v0 + lr) * D + 8 * lg + 32 * kd) * 2);
     }
     // K S (64 tokens x 16 columns) and (Q S)^T (16 columns x 64 tokens)
     f32x4 ks[4], qsT[4];
@@ -349,9 +349,10 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
   if (a.status[0]) return;
   const ChainMap cm = decode_chain(blk, a, 1);
   if (!cm.valid) return;
-  const int n = a.seq_order[cm.rank];
+  const int n = __builtin_amdgcn_readfirstlane(a.seq_order[cm.rank]); // uniform (scalar registers)
   const int j = cm.j, h = j * a.G + cm.gi;
-  const int c_begin = a.seq_c0[n], c_end = a.seq_c0[n + 1];
+  const int c_begin = __builtin_amdgcn_readfirstlane(a.seq_c0[n]);
+  const int c_end = __builtin_amdgcn_readfirstlane(a.seq_c0[n + 1]);
   constexpr int NT = bwalk_threads<D>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -365,37 +366,53 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
   const int v0 = 16 * w;
-  const int doc_t0 = a.cu[n], doc_t1 = a.cu[n + 1];
+  const int doc_t0 = __builtin_amdgcn_readfirstlane(a.cu[n]), doc_t1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
 
-  // staging (rows past the chunk's end re-read its last row; the row factors and the q scale are
-  // zero there and P^T is masked, so they contribute nothing)
+  // staging through buffer resources bounded at the chunk's last row, at per-lane offsets fixed
+  // for the whole walk (rows past the chunk's end read as zeros; the row factors and the q scale
+  // are zero there and P^T is masked, so they contribute nothing)
+  int oK[PPT], oV[PPT], oR[PPT], oA[APT], oP[APT]; // element offsets of this thread's pieces
+#pragma unroll
+  for (int it = 0; it < PPT; ++it) {
+    const int p = tid + NT * it, row = p / RP, pc = p % RP;
+    oK[it] = row * a.H * D + pc * 8;
+    oV[it] = row * a.HV * D + pc * 8;
+    oR[it] = row;
+  }
+#pragma unroll
+  for (int it = 0; it < APT; ++it) {
+    const int p = tid + NT * it, row = p >> 3, pc = p & 7;
+    oA[it] = row * a.HV * CH + pc * 8;
+    oP[it] = row * CH + pc * 8;
+  }
   bf16x8 rK[PPT], rQ[PPT], rD[PPT], rA[APT], rP[APT];
   float rgq[PPT], rrq[PPT];
   float sg = 0.f, sglast = 0.f, sbeta = 0.f, srk = 0.f;
   auto load_chunk = [&](int c) {
     const int t0 = doc_t0 + (c - c_begin) * CH;
     const int last = min(CH, doc_t1 - t0) - 1;
-    const TI* kc = kp + ((size_t)t0 * a.H + j) * D;
-    const TI* qc = qp + ((size_t)t0 * a.H + j) * D;
-    const TI* dc = dop + ((size_t)t0 * a.HV + h) * D;
+    const int kq_bytes = (last * a.H * D + D) * (int)sizeof(TI), v_bytes = (last * a.HV * D + D) * (int)sizeof(TI);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp + ((size_t)t0 * a.H + j) * D, kq_bytes);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp + ((size_t)t0 * a.H + j) * D, kq_bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dop + ((size_t)t0 * a.HV + h) * D, v_bytes);
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gcum + (size_t)h * a.T + t0, (last + 1) * 4);
+    const __amdgpu_buffer_rsrc_t rqr = make_rsrc(a.rq + (size_t)j * a.T + t0, (last + 1) * 4);
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
-      const int p = tid + NT * it, row = p / RP, pc = p % RP, rr = min(row, last);
-      rK[it] = IO<TI>::load8(kc + rr * a.H * D + pc * 8);
-      rQ[it] = IO<TI>::load8(qc + rr * a.H * D + pc * 8);
-      rD[it] = IO<TI>::load8(dc + rr * a.HV * D + pc * 8);
+      rK[it] = IO<TI>::bload8(kr, oK[it]);
+      rQ[it] = IO<TI>::bload8(qr, oK[it]);
+      rD[it] = IO<TI>::bload8(dr, oV[it]);
       // Q rows are staged scaled by exp(G) rq (zero past the end; formed in store_chunk, so no
       // load result is used before the chunk's compute)
-      rgq[it] = a.gcum[(size_t)h * a.T + t0 + rr];
-      rrq[it] = a.rq[(size_t)j * a.T + t0 + rr];
+      rgq[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, oR[it] * 4, 0, 0));
+      rrq[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rqr, oR[it] * 4, 0, 0));
     }
-    const bf16* ac = akk + ((size_t)t0 * a.HV + h) * CH;
-    const bf16* pc_ = pm + ((size_t)c * a.HV + h) * CH * CH;
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(akk + ((size_t)t0 * a.HV + h) * CH, (last * a.HV * CH + CH) * 2);
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(pm + ((size_t)c * a.HV + h) * CH * CH, CH * CH * 2);
 #pragma unroll
     for (int it = 0; it < APT; ++it) {
-      const int p = tid + NT * it, row = p >> 3, pc = p & 7;
-      rA[it] = *reinterpret_cast<const bf16x8*>(ac + min(row, last) * a.HV * CH + pc * 8);
-      rP[it] = *reinterpret_cast<const bf16x8*>(pc_ + row * CH + pc * 8);
+      rA[it] = IO<bf16>::bload8(ar, oA[it]);
+      rP[it] = IO<bf16>::bload8(pr, oP[it]);
     }
     {
       // per-token scalars of row `lane`, staged by wave 0; the other waves load one row (the
@@ -455,9 +472,9 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
     for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(dS[2 * kd], dS[2 * kd + 1]);
     {
       // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
-      bf16* tp = reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D + (size_t)(v0 + lr) * D + 8 * lg;
+      const __amdgpu_buffer_rsrc_t tr = make_rsrc(reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D, D * D * 2);
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) *reinterpret_cast<bf16x8*>(tp + 32 * kd) = sb[kd];
+      for (int kd = 0; kd < KD; ++kd) buf_store16(sb[kd], tr, ((v0 + lr) * D + 8 * lg + 32 * kd) * 2);
     }
     // dO as operands (k = tokens), shared by P^T dO and (Q')^T dO
     bf16x8 db[2];
