@@ -168,6 +168,43 @@ def test_split_walk_in_pieces():
         assert torch.equal(a[k], b[k]), k
 
 
+def test_concurrent_calls_on_two_streams_bitwise():
+    """Two host threads run fwd + bwd at once, each on its own stream, on a problem whose longest
+    document runs apart on the library's second stream (shared by both calls): each result equals
+    the sequential one bitwise."""
+    import threading
+
+    w = [x for x in EDGE if x.name == "split_mid"][0]
+    inp = _dev(syn.make_inputs(w))
+    ref = _run(w, inp, det=True)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    errs = []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                p = G.problem_for(w, deterministic=True)
+                a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
+                o, ht, saved = G.gdn_fwd(p, *a, h0=inp["h0"], stream=streams[i])
+                gr = G.gdn_bwd(p, *a, saved, inp["dO"], h0=inp["h0"], dht=inp["dht"], stream=streams[i])
+                streams[i].synchronize()
+                outs[i] = dict(o=o, ht=ht, **gr)
+        except Exception as e:  # reported below
+            errs.append(e)
+
+    torch.cuda.synchronize()
+    th = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errs, errs
+    for out in outs:
+        for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+            assert torch.equal(out[k], ref[k]), k
+
+
 def test_recompute_saved_set_bitwise_and_ckpt():
     w = EDGE[0]
     inp = _dev(syn.make_inputs(w))
