@@ -269,7 +269,8 @@ def test_pack262k_fwd_bwd_atomic():
     out = _run(w, inp, det=False)
     for k in ("o", "dq", "dk", "dv", "dg", "dbeta"):
         assert torch.isfinite(out[k]).all(), k
-    _check_all(w, inp, out, docs=[3], heads=[2, 7, 13])
+    # the longest document (its own stream, walked in pieces) and the shortest
+    _check_all(w, inp, out, docs=[0, 3], heads=[2, 13])
 
 
 def test_pack262k_deterministic_repeat():
@@ -279,7 +280,7 @@ def test_pack262k_deterministic_repeat():
     del a
     b = _run(w, inp, det=True)
     assert torch.equal(dq, b["dq"]) and torch.equal(dk, b["dk"])
-    _check_all(w, inp, b, docs=[3], heads=[5])
+    _check_all(w, inp, b, docs=[0, 3], heads=[5])
 
 
 def test_pack262k_longest_document_alone_bitwise():
