@@ -423,15 +423,21 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
     gdn::Args aa = a, ab = a;
     range_a(aa, sp);
     range_b(ab, sp);
-    // The longest document in pieces of at least 384 chunks (at most 4): each piece's walk needs
-    // only that piece's intra launch, and starts from the state the previous piece left in the
-    // workspace (f32, so the result is the same as one walk over the document).
+    // The longest document in up to 4 pieces when it has at least 768 chunks: each piece's walk
+    // needs only that piece's intra launch, and starts from the state the previous piece left in
+    // the workspace (f32, so the result is the same as one walk over the document). The first
+    // piece is short (96 chunks), so that the walk starts after a small intra launch; the next
+    // piece's intra launch (a tenth of a walk step per chunk) is done before its walk is due.
     const int pieces = std::max(1, std::min(4, sp.cA / 384));
+    const int first = pieces > 1 ? std::min(96, sp.cA / pieces) : sp.cA;
     float* st = piece_state(W, workspace);
     gdn::Args ap[4];
     for (int i = 0; i < pieces; ++i) {
       ap[i] = aa;
-      const int lo = (int)((long)sp.cA * i / pieces), hi = (int)((long)sp.cA * (i + 1) / pieces);
+      auto bound = [&](int k) {
+        return k == 0 ? 0 : first + (int)((long)(sp.cA - first) * (k - 1) / (pieces - 1));
+      };
+      const int lo = bound(i), hi = i + 1 < pieces ? bound(i + 1) : sp.cA;
       ap[i].c_base = sp.cA0 + lo;
       ap[i].c_count = hi - lo;
       ap[i].piece_lo = lo;

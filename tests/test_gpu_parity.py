@@ -284,23 +284,26 @@ def test_pack262k_deterministic_repeat():
 
 
 def test_pack262k_longest_document_alone_bitwise():
-    """The pack's longest document (98,304 tokens) runs apart from the others and its walk in
-    pieces; run alone (one document: one launch, one walk) it gives the same bits."""
+    """The pack's longest document (98,304 tokens) runs apart from the others, its walk in pieces
+    that hand the f32 state over; packed twice (two equal documents: no part is the longest, one
+    launch per kernel, one walk per chain) it gives the same bits."""
     w, inp = _big("pack262k")
+    assert not w.has_h0
     a = _run(w, inp, det=True)
     L0 = w.lengths[0]
-    w1 = syn.custom("pack_doc0", [L0], w.H, w.HV, w.d, w.dtype, has_h0=w.has_h0, want_ht=True)
-    one = {k: (v[:L0].contiguous() if v is not None and k not in ("cu_seqlens", "h0", "dht") else v)
-           for k, v in inp.items()}
-    one["cu_seqlens"] = torch.tensor([0, L0], dtype=torch.int32, device=DEV)
+    w2 = syn.custom("pack_doc0_twice", [L0, L0], w.H, w.HV, w.d, w.dtype, want_ht=True)
+    two = {k: (torch.cat([v[:L0], v[:L0]]).contiguous() if v is not None and k not in ("cu_seqlens", "h0", "dht")
+               else v) for k, v in inp.items()}
+    two["cu_seqlens"] = torch.tensor([0, L0, 2 * L0], dtype=torch.int32, device=DEV)
     a_o = a["o"][:L0].clone()
     grads = {k: a[k][:L0].clone() for k in ("dq", "dk", "dv", "dg", "dbeta")}
     del a
     torch.cuda.empty_cache()
-    b = _run(w1, one, det=True)
-    assert torch.equal(a_o, b["o"])
-    for k, v in grads.items():
-        assert torch.equal(v, b[k]), k
+    b = _run(w2, two, det=True)
+    for half in (slice(0, L0), slice(L0, 2 * L0)):
+        assert torch.equal(a_o, b["o"][half])
+        for k, v in grads.items():
+            assert torch.equal(v, b[k][half]), k
 
 
 def test_cp4share_h0_ht_dh0():
