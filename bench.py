@@ -73,8 +73,9 @@ def kernel_models(T, NT, N, H, HV, D, io, has_h0=False, det=False):
     return m
 
 
-def step_roofline(T, HV, D, io_bytes):
-    """Op-level algorithmic work (inputs, outputs and the light saved set; tapes excluded) per token."""
+def step_roofline(T, HV, D, io_bytes, full=False):
+    """Op-level algorithmic work (inputs, outputs and the saved set; tapes excluded) per token. The
+    full saved set adds a bf16 state per chunk and v_new, w, u and the q.k tiles per token."""
     C = CHUNK
     G = 3
     fl_f = 6 * D * D + 6 * C * D + 4 * C * D / G + 2 * C * C / 3
@@ -82,6 +83,8 @@ def step_roofline(T, HV, D, io_bytes):
     fl_r = 2 * C * D / G + 2 * C * C / 3
     inputs = 2 * 16 * D * io_bytes + HV * D * io_bytes + 2 * HV * 4
     saved = HV * C * 2 + HV * 4 + HV * 4 / C
+    if full:
+        saved += HV * D * D * 2 / C + 3 * HV * D * 2 + HV * C * 2
     b_f = inputs + HV * D * io_bytes + saved
     b_b = inputs + HV * D * io_bytes + saved + 2 * 16 * D * io_bytes + HV * D * io_bytes + 2 * HV * 4
     b_r = 16 * D * io_bytes + 2 * HV * 4 + saved
@@ -293,6 +296,9 @@ def main():
     ap.add_argument("--workload", default="pack262k")
     ap.add_argument("--atomic", action="store_true",
                     help="float-atomic dq/dk reduction (default: the deterministic fixed-order reduction)")
+    ap.add_argument("--full", action="store_true",
+                    help="full saved set: the forward also saves the states, v_new, w, u and the q.k tiles, "
+                         "and the backward does not replay the states (default: the light saved set)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fwd-only and ckpt timings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -332,7 +338,7 @@ def main():
     torch.cuda.set_device(dev)
     inp = syn.make_inputs(w, device=dev)
     det = not args.atomic
-    p = G.problem_for(w, save_mode=G.SAVE_LIGHT, deterministic=det)
+    p = G.problem_for(w, save_mode=G.SAVE_FULL if args.full else G.SAVE_LIGHT, deterministic=det)
     saved = torch.empty(G.gdn_saved_bytes(p), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(G.gdn_workspace_bytes(p, G.OP_FWD), dtype=torch.uint8, device=dev)
     ws_r = torch.empty(G.gdn_workspace_bytes(p, G.OP_RECOMPUTE), dtype=torch.uint8, device=dev)
@@ -420,7 +426,7 @@ def main():
     roof["avg_launch_ms"] = kernels[dom]["avg_ms"]
     roof["launches_per_step"] = per_step
 
-    sr = step_roofline(w.T, w.HV, w.d, io)
+    sr = step_roofline(w.T, w.HV, w.d, io, full=args.full)
     out = {
         "metric": METRIC,
         "value": value,
@@ -434,10 +440,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: %d docs %s, %d tokens, (H,HV)=(%d,%d), d=%d, l2norm=%d, light saved set, "
+        "config": {"workload": "%s: %d docs %s, %d tokens, (H,HV)=(%d,%d), d=%d, l2norm=%d, %s saved set, "
                                "%s dq/dk reduction" % (w.name, w.N, "/".join(str(x) for x in w.lengths[:4]) +
                                                        ("/..." if w.N > 4 else ""), w.T, w.H, w.HV, w.d,
-                                                       int(w.l2norm), "deterministic" if det else "atomic"),
+                                                       int(w.l2norm), "full" if args.full else "light",
+                                                       "deterministic" if det else "atomic"),
                    "global_batch": w.T, "seq_len": max(w.lengths), "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "step_roofline": {"op": "fwdbwd", "roofline_ms": 1e3 * sr["fwdbwd"]["roofline_s"],

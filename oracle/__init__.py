@@ -55,6 +55,8 @@ def load(path: Optional[str] = None):
     lib.gdn_oracle_bwd.restype = I
     lib.gdn_oracle_chunked_fwd.argtypes = common + [I, P, P, P, P, P, I]
     lib.gdn_oracle_chunked_fwd.restype = I
+    lib.gdn_oracle_chunked_fwd_full.argtypes = common + [I, P, P, P, P, P, P, P, P, P, P, I]
+    lib.gdn_oracle_chunked_fwd_full.restype = I
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -123,16 +125,26 @@ def bwd(cu_seqlens, q, k, v, g, beta, dO, h0=None, dht=None, l2norm=False, eps=1
 
 
 def chunked_fwd(cu_seqlens, q, k, v, g, beta, h0=None, l2norm=False, eps=1e-6, chunk=64, threads=None,
-                lib=None):
-    """Chunked FP64 forward. Returns dict o, ht, A [T,HV,chunk], gcum [T,HV], gamma [NT,HV]."""
+                lib=None, full=False):
+    """Chunked FP64 forward. Returns dict o, ht, A [T,HV,chunk], gcum [T,HV], gamma [NT,HV]; with
+    full=True also what the full saved set adds: W [T,HV,dk], U and R = v_new [T,HV,dv], the rows of
+    P [T,HV,chunk] and the state at the start of each chunk H [NT,HV,dk,dv]."""
     lib = lib or load()
     keep, args, (T, N, H, HV, dk, dv) = _common(cu_seqlens, q, k, v, g, beta, h0, l2norm, eps)
     cu = keep[0]
     NT = int(sum((int(cu[n + 1]) - int(cu[n]) + chunk - 1) // chunk for n in range(N)))
     out = dict(o=np.zeros((T, HV, dv)), ht=np.zeros((N, HV, dk, dv)), A=np.zeros((T, HV, chunk)),
                gcum=np.zeros((T, HV)), gamma=np.zeros((NT, HV)))
-    rc = lib.gdn_oracle_chunked_fwd(*args, int(chunk), _ptr(out["o"]), _ptr(out["ht"]), _ptr(out["A"]),
-                                    _ptr(out["gcum"]), _ptr(out["gamma"]), int(threads or default_threads()))
+    nth = int(threads or default_threads())
+    if full:
+        out.update(W=np.zeros((T, HV, dk)), U=np.zeros((T, HV, dv)), R=np.zeros((T, HV, dv)),
+                   P=np.zeros((T, HV, chunk)), H=np.zeros((NT, HV, dk, dv)))
+        rc = lib.gdn_oracle_chunked_fwd_full(*args, int(chunk), *(_ptr(out[x]) for x in
+                                                                 ("o", "ht", "A", "gcum", "gamma", "W", "U", "R",
+                                                                  "P", "H")), nth)
+    else:
+        rc = lib.gdn_oracle_chunked_fwd(*args, int(chunk), _ptr(out["o"]), _ptr(out["ht"]), _ptr(out["A"]),
+                                        _ptr(out["gcum"]), _ptr(out["gamma"]), nth)
     if rc != 0:
         raise RuntimeError("oracle chunked fwd failed (%d)" % rc)
     del keep

@@ -36,7 +36,8 @@
  *                           W and U, and the inter-chunk state walk. It also returns the
  *                           chunk intermediates the pages' saved set names (Akk = the
  *                           inverse, gcum = in-chunk cumulative log decay, gamma = the
- *                           chunk's total decay).
+ *                           chunk's total decay; gdn_oracle_chunked_fwd_full also the full
+ *                           set's W, U, v_new, P rows and chunk start states).
  *
  * Inputs are float32 arrays holding the exact values the GPU receives (bf16 values widen
  * to float32 exactly); every operation is in double. Work is split over threads by
@@ -67,6 +68,7 @@ typedef struct {
   /* chunked-form extras */
   int chunk;
   double *A, *gcum, *gamma;
+  double *Wo, *Uo, *Ro, *Po, *Hs; /* full saved set: W, U, R = v_new, P rows, chunk start states */
   int64_t* seq_chunk0; /* first global chunk index of each document */
   /* work queue */
   int n_items;
@@ -384,6 +386,7 @@ static void chunked_item(job_t* J, int n, int j) {
     int64_t cidx = J->seq_chunk0[n];
     for (int64_t cs = 0; cs < L; cs += C, ++cidx) {
       const int Ce = (int)((L - cs) < C ? (L - cs) : C);
+      if (J->Hs) memcpy(J->Hs + ((size_t)cidx * J->HV + h) * dd, S, dd * sizeof(double));
       double run = 0.0;
       for (int i = 0; i < Ce; ++i) {
         const int64_t tau = t0 + cs + i;
@@ -467,6 +470,13 @@ static void chunked_item(job_t* J, int n, int j) {
           for (int c = 0; c < C; ++c)
             J->A[((size_t)tau * J->HV + h) * C + c] = (c < Ce) ? Am[(size_t)i * C + c] : 0.0;
         if (J->gcum) J->gcum[(size_t)tau * J->HV + h] = Gc[i];
+        const size_t rk_ = ((size_t)tau * J->HV + h) * dk, rv_ = ((size_t)tau * J->HV + h) * dv;
+        if (J->Wo) memcpy(J->Wo + rk_, W + (size_t)i * dk, dk * sizeof(double));
+        if (J->Uo) memcpy(J->Uo + rv_, U + (size_t)i * dv, dv * sizeof(double));
+        if (J->Ro) memcpy(J->Ro + rv_, R + (size_t)i * dv, dv * sizeof(double));
+        if (J->Po)
+          for (int c = 0; c < C; ++c)
+            J->Po[((size_t)tau * J->HV + h) * C + c] = (c < Ce) ? Pm[(size_t)i * C + c] : 0.0;
       }
       if (J->gamma) J->gamma[(size_t)cidx * J->HV + h] = gam;
     }
@@ -587,6 +597,31 @@ int gdn_oracle_chunked_fwd(int64_t T, int N, const int32_t* cu, int H, int HV, i
   J.T = T; J.N = N; J.cu = cu; J.H = H; J.HV = HV; J.dk = dk; J.dv = dv;
   J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.h0 = h0; J.l2norm = l2norm; J.eps = eps;
   J.o = o; J.ht = ht; J.chunk = chunk; J.A = A; J.gcum = gcum; J.gamma = gamma;
+  if (chunk <= 0 || N < 0 || !cu) return -1;
+  J.seq_chunk0 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + 1));
+  if (!J.seq_chunk0) return -2;
+  J.seq_chunk0[0] = 0;
+  for (int n = 0; n < N; ++n)
+    J.seq_chunk0[n + 1] = J.seq_chunk0[n] + ((int64_t)cu[n + 1] - cu[n] + chunk - 1) / chunk;
+  const int rc = run(&J, OP_CHUNKED, nthreads);
+  free(J.seq_chunk0);
+  return rc;
+}
+
+/* The same, also returning what the full saved set holds besides the light one: W and U
+ * ([T,HV,dk], [T,HV,dv]), R = U - W S (v_new, [T,HV,dv]), the rows of P ([T,HV,chunk], zero past
+ * the chunk's valid length) and the state at the start of every chunk ([NT,HV,dk,dv]). */
+int gdn_oracle_chunked_fwd_full(int64_t T, int N, const int32_t* cu, int H, int HV, int dk, int dv,
+                                const float* q, const float* k, const float* v, const float* g, const float* beta,
+                                const float* h0, int l2norm, double eps, int chunk, double* o, double* ht,
+                                double* A, double* gcum, double* gamma, double* W, double* U, double* R,
+                                double* P, double* Hs, int nthreads) {
+  job_t J;
+  memset(&J, 0, sizeof J);
+  J.T = T; J.N = N; J.cu = cu; J.H = H; J.HV = HV; J.dk = dk; J.dv = dv;
+  J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.h0 = h0; J.l2norm = l2norm; J.eps = eps;
+  J.o = o; J.ht = ht; J.chunk = chunk; J.A = A; J.gcum = gcum; J.gamma = gamma;
+  J.Wo = W; J.Uo = U; J.Ro = R; J.Po = P; J.Hs = Hs;
   if (chunk <= 0 || N < 0 || !cu) return -1;
   J.seq_chunk0 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + 1));
   if (!J.seq_chunk0) return -2;

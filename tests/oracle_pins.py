@@ -349,6 +349,75 @@ def pin_chunked_equals_recurrent(lib, seed=14, tol=1e-11):
     assert abs(ch["gamma"][0, 0] - np.exp(G[-1])) < 1e-12
 
 
+def pin_chunked_full_set(lib, seed=15, tol=1e-11):
+    """What the full saved set adds, against the token recurrence:
+    - the state at the start of every chunk is h0 for a document's first chunk and, for chunk m,
+      the final state of the recurrence run over the document's first m C tokens;
+    - v_new = R, row t: beta_t (v_t - a_t S_{t-1}^T kh_t), the correction the delta rule adds at
+      token t (S_t = a_t S_{t-1} + kh_t r_t^T), with S_{t-1} from the recurrence over the tokens
+      before t;
+    - U = R wherever the chunk starts from a zero state, and U does not depend on the start state;
+    - W maps the start state to the change of R: U - R = W S_c on every chunk (dv >= dk here, so
+      the start states determine W);
+    - P: with g = 0 and q = k, P_ij = kh_i . kh_j for i >= j (1 on the diagonal), 0 above it and
+      past the chunk's valid length."""
+    rng = np.random.default_rng(seed)
+    lens, C = [21, 9], 8
+    dk, dv = 4, 6
+    p = rand_problem(rng, lens, H=1, HV=2, dk=dk, dv=dv)
+    kh = _unit_rows(p["k"])
+
+    def chunked(pp):
+        return oracle.chunked_fwd(pp["cu"], pp["q"], pp["k"], pp["v"], pp["g"], pp["beta"], pp["h0"], l2norm=True,
+                                  chunk=C, lib=lib, threads=1, full=True)
+
+    def state_after(n, m):  # recurrent state of document n after its first m tokens
+        t0 = int(p["cu"][n])
+        sub = dict(cu=np.array([0, m], np.int32), h0=p["h0"][n:n + 1],
+                   **{x: p[x][t0:t0 + m] for x in ("q", "k", "v", "g", "beta")})
+        return _fwd(lib, sub, True)[1][0]
+
+    ch = chunked(p)
+    z = dict(p, h0=None)
+    ch0 = chunked(z)
+    cidx = 0
+    for n, L in enumerate(lens):
+        t0 = int(p["cu"][n])
+        for cs in range(0, L, C):
+            S_c = state_after(n, cs) if cs > 0 else p["h0"][n].astype(np.float64)
+            if cs == 0:
+                assert np.array_equal(ch["H"][cidx], S_c)
+            assert np.max(np.abs(ch["H"][cidx] - S_c)) < tol
+            if cs == 0:
+                assert np.max(np.abs(ch0["U"][t0:t0 + C] - ch0["R"][t0:t0 + C])) < tol
+            rows = slice(t0 + cs, t0 + min(cs + C, L))
+            assert np.max(np.abs(ch["U"][rows] - ch0["U"][rows])) < tol
+            for h in range(2):
+                lhs = ch["U"][rows, h] - ch["R"][rows, h]
+                assert np.max(np.abs(lhs - ch["W"][rows, h] @ ch["H"][cidx, h])) < tol
+            cidx += 1
+        for m in range(L):
+            S_prev = state_after(n, m) if m > 0 else p["h0"][n].astype(np.float64)
+            t = t0 + m
+            for h in range(2):
+                a = np.exp(np.float64(p["g"][t, h]))
+                r = np.float64(p["beta"][t, h]) * (p["v"][t, h] - a * S_prev[h].T @ kh[t, 0])
+                assert np.max(np.abs(ch["R"][t, h] - r)) < tol
+    # P at g = 0 with q = k
+    pq = dict(p, q=p["k"].copy(), g=np.zeros_like(p["g"]))
+    P = chunked(pq)["P"]
+    for n, L in enumerate(lens):
+        t0 = int(p["cu"][n])
+        for cs in range(0, L, C):
+            Ce = min(C, L - cs)
+            Kc = kh[t0 + cs:t0 + cs + Ce, 0]
+            ref = np.zeros((Ce, C))
+            ref[:, :Ce] = np.tril(Kc @ Kc.T)
+            for h in range(2):
+                assert np.max(np.abs(P[t0 + cs:t0 + cs + Ce, h] - ref)) < tol
+                assert np.max(np.abs(np.diag(P[t0 + cs:t0 + cs + Ce, h, :Ce]) - 1.0)) < 1e-5
+
+
 ALL_PINS = [
     pin_finite_differences,
     pin_directional_derivative,
@@ -365,4 +434,5 @@ ALL_PINS = [
     pin_grouped_equals_repeated,
     pin_l2norm_scale_invariance,
     pin_chunked_equals_recurrent,
+    pin_chunked_full_set,
 ]
