@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import gated_deltanet_fwd_amd as G
+import oracle
 import synthetic as syn
 from parity_util import assert_close, host_inputs, oracle_bwd, oracle_fwd, to_np
 
@@ -122,6 +123,50 @@ def test_edge_cases(w, det):
     inp = _dev(syn.make_inputs(w))
     out = _run(w, inp, det=det)
     _check_all(w, inp, out)
+
+
+def _saved_regions(w, full):
+    """Byte offsets of the saved set's regions: a 256-byte tag, then each region aligned to 256."""
+    NT = sum((L + 63) // 64 for L in w.lengths)
+    T, HV, d = w.T, w.HV, w.d
+    sizes = [("A", T * HV * 64 * 2), ("gcum", T * HV * 4), ("gamma", NT * HV * 4)]
+    if full:
+        sizes += [("H", NT * HV * d * d * 2), ("R", T * HV * d * 2), ("W", T * HV * d * 2), ("U", T * HV * d * 2),
+                  ("P", T * HV * 64 * 2)]
+    off, out = 256, {}
+    for name, n in sizes:
+        out[name] = (off, n)
+        off = (off + n + 255) // 256 * 256
+    return out, NT
+
+
+@pytest.mark.parametrize("name", ["edge_tails", "edge_d64_f32"])
+def test_full_saved_set_against_oracle(name):
+    """Every region of the full saved set (A, gcum, gamma; the chunk start states, v_new, w, u and
+    the P rows) against the FP64 chunked oracle, with ragged chunks, empty documents and h0."""
+    w = [x for x in EDGE if x.name == name][0]
+    inp = _dev(syn.make_inputs(w))
+    out = _run(w, inp, save_mode=G.SAVE_FULL, bwd=False)
+    h, _, _ = host_inputs(inp, None, None, w.HV // w.H)
+    ref = oracle.chunked_fwd(h["cu"], h["q"], h["k"], h["v"], h["g"], h["beta"], h["h0"], l2norm=w.l2norm,
+                             chunk=64, full=True)
+    regions, NT = _saved_regions(w, True)
+    raw = out["saved"]
+
+    def view(key, dtype, shape):
+        off, n = regions[key]
+        return raw[off:off + n].view(dtype).reshape(shape)
+
+    T, HV, d = w.T, w.HV, w.d
+    assert_close("A", view("A", torch.bfloat16, (T, HV, 64)), ref["A"])
+    assert_close("gcum", view("gcum", torch.float32, (HV, T)).t(), ref["gcum"])
+    assert_close("gamma", view("gamma", torch.float32, (NT, HV)), ref["gamma"])
+    # the state tape is stored transposed: [chunk][v head][value][key]
+    assert_close("h tape", view("H", torch.bfloat16, (NT, HV, d, d)).transpose(2, 3), ref["H"])
+    assert_close("v_new", view("R", torch.bfloat16, (T, HV, d)), ref["R"])
+    assert_close("w", view("W", torch.bfloat16, (T, HV, d)), ref["W"])
+    assert_close("u", view("U", torch.bfloat16, (T, HV, d)), ref["U"])
+    assert_close("Aqk", view("P", torch.bfloat16, (T, HV, 64)), ref["P"])
 
 
 def test_all_documents_empty():
