@@ -55,6 +55,11 @@ int launch_fill_zero(float* p, size_t n, void* stream) {
 // ---------------------------------------------------------------------------------------
 // Full saved set extras, per (chunk, value head): w = A diag(beta b) Kh, u = A diag(beta) V,
 // Aqk = P (decayed, masked normalised q.k), all bf16 token rows.
+//
+// The row-scaled K and V rows are staged in LDS as they are stored (16-byte rows) and read back
+// transposed; the products are formed transposed (w^T = (diag(beta b) Kh)^T A^T, the A rows as the
+// B operand straight from memory), so each lane holds 4 consecutive d of one token and writes
+// them with one 8-byte store.
 template <int D, typename TI>
 __global__ __launch_bounds__(NTHREADS) void k_wy_full(Args a) {
   if (a.status[0]) return;
@@ -64,70 +69,81 @@ __global__ __launch_bounds__(NTHREADS) void k_wy_full(Args a) {
   const int t0 = a.c_t0[c];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  constexpr int STK = CH + PAD;
-  __shared__ __attribute__((aligned(16))) bf16 sKsT[D * STK];
-  __shared__ __attribute__((aligned(16))) bf16 sVsT[D * STK];
-  __shared__ float sG[CH], sB[CH], srk[CH];
+  constexpr int SK = D + 16; // rows of 32 mod 64 bytes
+  __shared__ __attribute__((aligned(16))) bf16 sKs[CH * SK];
+  __shared__ __attribute__((aligned(16))) bf16 sVs[CH * SK];
+  __shared__ float sSk[CH], sSv[CH];
   const TI* kp = (const TI*)a.k;
   const TI* vp = (const TI*)a.v;
-  if (tid < CH) {
-    const bool ok = tid < len;
-    sG[tid] = ok ? a.gcum[(size_t)h * a.T + t0 + tid] : 0.f;
-    sB[tid] = ok ? a.beta[(size_t)(t0 + tid) * a.HV + h] : 0.f;
-    srk[tid] = ok ? a.rk[(size_t)j * a.T + t0 + tid] : 0.f;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < CH * (D / 8); idx += NTHREADS) {
-    const int r = idx & 63, pc = idx >> 6;
-    float kf[8], vf[8];
-    if (r < len) {
-      IO<TI>::load8f(kp + ((size_t)(t0 + r) * a.H + j) * D + pc * 8, kf);
-      IO<TI>::load8f(vp + ((size_t)(t0 + r) * a.HV + h) * D + pc * 8, vf);
-    } else {
+  // every load first (rows past the chunk's end clamped, zeroed through the row factors or a
+  // mask), so that they are in flight together
+  constexpr int IT = CH * (D / 8) / NTHREADS;
+  float kf[IT][8], vf[IT][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = vf[e] = 0.f;
-    }
-    const float sk = sB[r] * __expf(sG[r]) * srk[r], sv = sB[r];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sKsT[(pc * 8 + e) * STK + r] = (bf16)(kf[e] * sk);
-      sVsT[(pc * 8 + e) * STK + r] = (bf16)(vf[e] * sv);
-    }
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + it * NTHREADS, rr = min(idx / (D / 8), len - 1), pc = idx % (D / 8);
+    IO<TI>::load8f(kp + ((size_t)(t0 + rr) * a.H + j) * D + pc * 8, kf[it]);
+    IO<TI>::load8f(vp + ((size_t)(t0 + rr) * a.HV + h) * D + pc * 8, vf[it]);
   }
+  // this wave's A rows (tokens 16 w + lr) as MFMA B operands: B[k = token'][n = token]
   const int ar = 16 * w + lr;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   bf16x8 fa[2];
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
-    fa[k2] = ar < len ? *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + ar) * a.HV + h) * CH + k2 * 32 + lg * 8)
-                      : zero8();
+    fa[k2] = *reinterpret_cast<const bf16x8*>(akk + ((size_t)(t0 + min(ar, len - 1)) * a.HV + h) * CH + k2 * 32 +
+                                              lg * 8);
+  // the P rows to copy: thread tid takes 16-byte pieces tid and tid + 256 of the 64 x 64 tile
+  const bf16* pp = reinterpret_cast<const bf16*>(a.qk) + ((size_t)c * a.HV + h) * CH * CH;
+  const bf16x8 pv0 = *reinterpret_cast<const bf16x8*>(pp + tid * 8);
+  const bf16x8 pv1 = *reinterpret_cast<const bf16x8*>(pp + (tid + NTHREADS) * 8);
+  if (tid < CH) {
+    // row factors: beta exp(G) rk for K, beta for V; zero past the chunk's end
+    const int r = min(tid, len - 1);
+    const float bt = a.beta[(size_t)(t0 + r) * a.HV + h];
+    const float sk = bt * __expf(a.gcum[(size_t)h * a.T + t0 + r]) * a.rk[(size_t)j * a.T + t0 + r];
+    sSk[tid] = keepf(sk, tid < len);
+    sSv[tid] = keepf(bt, tid < len);
+  }
   __syncthreads();
-  bf16* wo = reinterpret_cast<bf16*>(a.w);
-  bf16* uo = reinterpret_cast<bf16*>(a.u);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + it * NTHREADS, r = idx / (D / 8), pc = idx % (D / 8);
+    const float sk = sSk[r], sv = sSv[r];
+    bf16x8 kb, vb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kb[e] = (bf16)(kf[it][e] * sk);
+      vb[e] = (bf16)(vf[it][e] * sv);
+    }
+    *reinterpret_cast<bf16x8*>(sKs + r * SK + pc * 8) = kb;
+    *reinterpret_cast<bf16x8*>(sVs + r * SK + pc * 8) = vb;
+  }
+  fa[0] = keep8(fa[0], ar < len);
+  fa[1] = keep8(fa[1], ar < len);
+  __syncthreads();
+  bf16* wo = reinterpret_cast<bf16*>(a.w) + ((size_t)(t0 + ar) * a.HV + h) * D;
+  bf16* uo = reinterpret_cast<bf16*>(a.u) + ((size_t)(t0 + ar) * a.HV + h) * D;
 #pragma unroll
   for (int ct = 0; ct < D / 16; ++ct) {
     f32x4 accw = zero4(), accu = zero4();
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      accw = mfma(fa[k2], lds8(sKsT, STK, 16 * ct + lr, k2 * 32 + lg * 8), accw);
-      accu = mfma(fa[k2], lds8(sVsT, STK, 16 * ct + lr, k2 * 32 + lg * 8), accu);
+      accw = mfma(lds_tr8(sKs, SK, k2 * 32, 16 * ct), fa[k2], accw);
+      accu = mfma(lds_tr8(sVs, SK, k2 * 32, 16 * ct), fa[k2], accu);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + lg * 4 + i;
-      if (r < len) {
-        wo[((size_t)(t0 + r) * a.HV + h) * D + 16 * ct + lr] = (bf16)accw[i];
-        uo[((size_t)(t0 + r) * a.HV + h) * D + 16 * ct + lr] = (bf16)accu[i];
-      }
+    // lane: d = 16 ct + 4 lg + i of token ar
+    if (ar < len) {
+      const float xw[4] = {accw[0], accw[1], accw[2], accw[3]}, xu[4] = {accu[0], accu[1], accu[2], accu[3]};
+      IO<bf16>::store4(wo + 16 * ct + 4 * lg, xw);
+      IO<bf16>::store4(uo + 16 * ct + 4 * lg, xu);
     }
   }
-  const bf16* pp = reinterpret_cast<const bf16*>(a.qk) + ((size_t)c * a.HV + h) * CH * CH;
-  bf16* aq = reinterpret_cast<bf16*>(a.aqk);
-  for (int idx = tid; idx < len * (CH / 8); idx += NTHREADS) {
-    const int r = idx >> 3, pc = idx & 7;
-    *reinterpret_cast<bf16x8*>(aq + ((size_t)(t0 + r) * a.HV + h) * CH + pc * 8) =
-        *reinterpret_cast<const bf16x8*>(pp + r * CH + pc * 8);
-  }
+  // Aqk: the rows of P within the chunk
+  bf16* aq = reinterpret_cast<bf16*>(a.aqk) + ((size_t)t0 * a.HV + h) * CH;
+  if ((tid >> 3) < len) *reinterpret_cast<bf16x8*>(aq + (size_t)(tid >> 3) * a.HV * CH + (tid & 7) * 8) = pv0;
+  if (((tid + NTHREADS) >> 3) < len)
+    *reinterpret_cast<bf16x8*>(aq + (size_t)((tid + NTHREADS) >> 3) * a.HV * CH + (tid & 7) * 8) = pv1;
 }
 
 int launch_wy_full(const Args& a, void* stream) {
