@@ -221,25 +221,27 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
       }
       xb[kt] = pack_kp(X[0], X[1]);
     }
-    // R = A X
+    // R = A X. The full saved set's v_new = R is formed a second time transposed, R^T = X^T A^T
+    // (the same two fragments with their roles swapped), so that a lane holds 4 consecutive
+    // values of one token's row: one 8-byte store, dropped past the chunk's end
     f32x4 R[4];
+    __amdgpu_buffer_rsrc_t vr;
+    if (FULL)
+      vr = make_rsrc(reinterpret_cast<bf16*>(a.vnew) + ((size_t)t0 * a.HV + h) * D, ((len - 1) * a.HV * D + D) * 2);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       R[mt] = zero4();
+      f32x4 RT = zero4();
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) R[mt] = mfma(lds8(At, SA, 16 * mt + lr, 32 * kt + 8 * lg), xb[kt], R[mt]);
-    }
-    if (FULL) {
-      // rows past the chunk's end go to the discard area (no branch around the stores)
-      bf16* vn = reinterpret_cast<bf16*>(a.vnew) + ((size_t)t0 * a.HV + h) * D + v0 + lr;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * lg + i;
-          bf16* dst = r < len ? vn + (size_t)r * a.HV * D : reinterpret_cast<bf16*>(a.discard) + lane;
-          *dst = (bf16)R[mt][i];
-        }
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 af = lds8(At, SA, 16 * mt + lr, 32 * kt + 8 * lg);
+        R[mt] = mfma(af, xb[kt], R[mt]);
+        if (FULL) RT = mfma(xb[kt], af, RT);
+      }
+      if (FULL) {
+        const float x4[4] = {RT[0], RT[1], RT[2], RT[3]};
+        IO<bf16>::bstore4(vr, (16 * mt + lr) * a.HV * D + v0 + 4 * lg, x4);
+      }
     }
     // operands of R (for (P R)^T) and of diag(exp(G_last - G) rk) R (for the state update)
     bf16x8 rb[2], rdb[2];
