@@ -108,7 +108,7 @@ SavedLayout saved_layout(const Sizes& s, int full) {
 }
 
 struct WorkLayout {
-  size_t seq_c0, c_t0, c_len, seq_order, pair_order, status, discard, rk, rq, qk, htape, dstape, dqacc, dkacc, state,
+  size_t seq_c0, c_t0, c_len, seq_order, pair_order, status, rk, rq, qk, htape, dstape, dqacc, dkacc, state,
       total;
 };
 
@@ -126,7 +126,6 @@ WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
   L.seq_order = take((size_t)s.N * 4);
   L.pair_order = take(((size_t)(s.N * s.H + 7) / 8 + 1) * 2 * 4);
   L.status = take(4);
-  L.discard = take(gdn::kDiscardBytes);
   L.rk = take((size_t)s.T * s.H * 4);
   L.rq = take((size_t)s.T * s.H * 4);
   L.qk = take((size_t)s.NT * s.HV * kChunk * kChunk * 2);
@@ -331,7 +330,6 @@ void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
   a.seq_order = (int*)(b + W.seq_order);
   a.pair_order = (int*)(b + W.pair_order);
   a.status = (int*)(b + W.status);
-  a.discard = b + W.discard;
   a.rk = (float*)(b + W.rk);
   a.rq = (float*)(b + W.rq);
   a.qk = (uint16_t*)(b + W.qk);

@@ -47,7 +47,6 @@ struct Args {
   int* c_len;      // [NT] valid tokens of each chunk (1..64)
   int* seq_order;  // [N] documents, longest first
   int* status;     // [1] nonzero if the device tables disagree with the host's chunk count
-  void* discard;   // [kDiscardBytes] target of stores from lanes past a chunk's end (never read)
   float* rk;       // [H, T] inverse L2 norms of k rows (1 when the norm is off), head-major
   float* rq;       // [H, T] inverse L2 norms of q rows, head-major
   uint16_t* qk;    // bf16 [NT, HV, 64, 64] P = exp(G_q - G_k) qh.kh masked to q >= k, per value head
@@ -75,9 +74,6 @@ struct Args {
   const float* state_in;
   float* state_out;
 };
-
-// Bytes of the workspace area that takes the stores of lanes past a chunk's end.
-constexpr size_t kDiscardBytes = 4096;
 
 int chain_blocks(const Args& a, int ntile);
 
