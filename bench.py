@@ -34,7 +34,7 @@ CHUNK = 64
 METRIC = "tokens/s fwd+bwd (and fwd, ckpt) at (H,HV)=(16,48), d=128, 262144 tok"
 
 
-def kernel_models(T, NT, N, H, HV, D, io, has_h0=False, det=False):
+def kernel_models(T, NT, N, H, HV, D, io, has_h0=False, det=False, full=False):
     """Algorithmic (compulsory) bytes and MFMA flops of one launch of each kernel.
 
     Bytes: every operand of the kernel read once and every result written once (a q/k tile read by
@@ -64,6 +64,13 @@ def kernel_models(T, NT, N, H, HV, D, io, has_h0=False, det=False):
     m["gdn_walk_bwd"] = (2 * qkin + vin + akk + pv + 2 * scal_v + 2 * scal_q + tape + (2 * states if has_h0 else 0),
                          T * HV * (6 * D * D + 4 * C * D))
     m["gdn_walk_pair"] = tuple(x + y for x, y in zip(m["gdn_walk_tape"], m["gdn_walk_bwd"]))
+    if full:
+        # the full saved set: the forward walk also writes the state tape and v_new (bf16); w, u
+        # and the P rows are formed and copied by k_wy_full
+        fw = m["gdn_walk_fwd"]
+        m["gdn_walk_fwd"] = (fw[0] + tape + T * HV * D * 2, fw[1])
+        m["gdn_wy_full"] = (akk + qkin + vin + pv + 2 * scal_v + scal_q + 2 * T * HV * D * 2 + akk,
+                            T * HV * 2 * (2 * C * D))
     out_qk = 2 * qkin if det else 2 * acc
     m["gdn_chunk_grad"] = (2 * tape + 2 * qkin + 2 * vin + akk + pv + 2 * scal_v + 2 * scal_q + gam
                            + vin + 2 * scal_v + out_qk,
@@ -404,7 +411,7 @@ def main():
     value = w.T * args.steps / t_fb
     io = 2 if w.dtype == "bf16" else 4
     NT = int(sum((L + CHUNK - 1) // CHUNK for L in w.lengths))
-    models = kernel_models(w.T, NT, w.N, w.H, w.HV, w.d, io, has_h0=w.has_h0, det=det)
+    models = kernel_models(w.T, NT, w.N, w.H, w.HV, w.d, io, has_h0=w.has_h0, det=det, full=args.full)
     # dominant kernel = largest share of the timed step (summed launch time). A kernel may run as
     # several launches per step (the longest document's and the others'); its per-launch
     # algorithmic work is then the step's divided by the launches, so that achieved = the step's
@@ -419,7 +426,10 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": by / avg_s / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(dom, args.workload)
+    # the committed counters are of the default step (light saved set, deterministic reduction)
+    default_kernel = not args.full and not (args.atomic and dom in ("gdn_chunk_grad", "gdn_fill_zero",
+                                                                    "gdn_finalize_qk"))
+    roof["traffic"] = load_traffic(dom, args.workload) if default_kernel else None
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = by
     roof["algorithmic_flops"] = fl
