@@ -2,17 +2,31 @@
 """Benchmark of the MI355X gated-delta-rule training kernel (one GPU).
 
 One step = one pass of the whole hot path over one batch: gdn_fwd then gdn_bwd (light saved
-set) on the packed workload of 4 documents 98304/65536/57344/40960 = 262144 tokens,
-(H, HV) = (16, 48), d = 128, bf16 inputs with the in-kernel q/k L2 norm (the pages' "shape A").
-Inputs are drawn once on the GPU and are resident in HBM before timing starts.
+set, deterministic dq/dk reduction) on the packed workload of 4 documents
+98304/65536/57344/40960 = 262144 tokens, (H, HV) = (16, 48), d = 128, bf16 inputs with the
+in-kernel q/k L2 norm (the pages' "shape A"). Inputs are drawn once on the GPU and are resident
+in HBM before timing starts.
 
-Prints one JSON line: tokens/s of the fwd+bwd step (the headline), plus fwd-only and
-checkpointed (fwd + recompute + bwd) rates, the roofline of the dominant kernel with its
-per-launch duration measured by HIP events on the launch stream during the timed region, and
-the FP64 CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line:
+  value / ms_per_step   fwd+bwd tokens/s over exactly --steps back-to-back steps, bracketed by
+                        synchronisations (no per-kernel instrumentation in that loop)
+  protocol              fwd, fwd+bwd and checkpointed (fwd + recompute + bwd, also with the
+                        recompute's kept tape) under the pages' timing protocol: a >= 512 MiB
+                        buffer written before every timed call, 5 groups x 12 calls, median and
+                        per-group drift
+  configs               the other workloads (8,192-token document fwd, CP4 share fwd+bwd with h0,
+                        512 short documents checkpointed), same protocol, each with its op
+                        roofline fraction
+  roofline              the kernel with the longest span on the step's critical path: its
+                        algorithmic bytes (inputs, outputs, saved set) or flops per launch over
+                        its mean launch duration, HIP events recorded on the stream each launch
+                        goes to, in a separate pass; `traffic` is the committed HBM counter
+                        figure for that kernel when its source is unchanged
+  cpu_baseline          the FP64 oracle on the host cores on a bounded sample of the same workload
+                        (every document, a few q/k-head groups), fwd+bwd, fwd and checkpointed
 
-    python bench.py [--steps K] [--warmup W] [--workload pack262k] [--atomic]
-                    [--no-cpu-baseline] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload pack262k] [--atomic] [--full]
+                    [--no-cpu-baseline] [--no-extra] [--gpus 1]
 """
 from __future__ import annotations
 
@@ -20,7 +34,9 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -31,70 +47,92 @@ if ROOT not in sys.path:
 PEAK_HBM = 8.0e12           # bytes/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15          # flop/s, MI355X dense bf16 MFMA
 CHUNK = 64
+FLUSH_BYTES = 512 << 20     # written before every timed call of the protocol (L2 and MALL)
 METRIC = "tokens/s fwd+bwd (and fwd, ckpt) at (H,HV)=(16,48), d=128, 262144 tok"
 
 
-def kernel_models(T, NT, N, H, HV, D, io, has_h0=False, det=False, full=False):
-    """Algorithmic (compulsory) bytes and MFMA flops of one launch of each kernel.
+def kernel_models(T, NT, N, H, HV, D, io, has_h0=False, has_dht=False, want_ht=False, det=True, save_mode="light"):
+    """Per kernel, over one fwd + bwd step: (algorithmic bytes, MFMA flops, intermediate bytes).
 
-    Bytes: every operand of the kernel read once and every result written once (a q/k tile read by
-    the G value heads of its group counts once). Flops: the contractions of the chunked method the
-    kernel performs, 2 flops per multiply-add.
+    Algorithmic bytes are the op roofline's: the inputs, outputs, saved set and states that the
+    kernel reads or writes, each tensor counted once per kernel (a q/k tile read by the G value
+    heads of its group counts once). Intermediates the implementation moves (the replayed state
+    tape and the end-state-gradient tape, the per-value-head q.k tiles, the inverse norms, FP32
+    dq/dk accumulators) are not algorithmic and are reported apart. In the full and kept-tape forms
+    the state tape (and, full, v_new, w, u, the q.k rows) belong to the saved set, so their writes
+    and reads are algorithmic. Flops: the contractions of the chunked method the kernel performs,
+    2 flops per multiply-add.
     """
     C = CHUNK
     f4 = 4
+    full, kept = save_mode == "full", save_mode in ("full", "tape")
     pv = NT * HV * C * C * 2       # decayed masked q.k per value head (P or P^T), bf16
-    akk = T * HV * C * 2           # A rows, bf16
-    scal_v = T * HV * f4           # one f32 per token and value head
-    scal_q = T * H * f4            # one f32 per token and q/k head
-    gam = NT * HV * f4
+    akk = T * HV * C * 2           # A rows, bf16 (saved)
+    gb = T * HV * f4               # g or beta (input), gcum (saved), dg or dbeta (output)
+    gam = NT * HV * f4             # gamma (saved)
+    nrm = T * H * f4               # inverse norms of q or k rows (workspace)
     tape = NT * HV * D * D * 2     # one bf16 state per chunk and value head
-    qkin = T * H * D * io
-    vin = T * HV * D * io
-    states = N * HV * D * D * f4
+    qk = T * H * D * io            # q or k (input), dq or dk (output)
+    vv = T * HV * D * io           # v, dO (inputs), o, dv (outputs)
+    wuv = T * HV * D * 2           # w, u or v_new rows, bf16
+    st = N * HV * D * D * f4       # one state tensor
     acc = T * H * D * f4           # f32 dq or dk accumulator (atomic reduction)
+    h0 = st if has_h0 else 0
     m = {}
-    m["gdn_intra"] = (2 * qkin + 2 * scal_v + 2 * scal_q + pv + akk + scal_v + gam,
-                      NT * H * 2 * (2 * C * C * D) + NT * HV * (2 * C ** 3 // 3))
-    m["gdn_intra_bwd"] = (2 * qkin + scal_v + 2 * scal_q + pv, NT * H * 2 * (2 * C * C * D))
-    m["gdn_walk_fwd"] = (2 * qkin + vin + akk + pv + 2 * scal_v + 2 * scal_q + vin + (2 * states if has_h0 else 0),
-                         T * HV * (6 * D * D + 4 * C * D))
-    m["gdn_walk_tape"] = (qkin + vin + akk + 2 * scal_v + scal_q + tape + (states if has_h0 else 0),
-                          T * HV * (4 * D * D + 2 * C * D))
-    m["gdn_walk_bwd"] = (2 * qkin + vin + akk + pv + 2 * scal_v + 2 * scal_q + tape + (2 * states if has_h0 else 0),
-                         T * HV * (6 * D * D + 4 * C * D))
-    m["gdn_walk_pair"] = tuple(x + y for x, y in zip(m["gdn_walk_tape"], m["gdn_walk_bwd"]))
+    # name: (algorithmic bytes, flops, intermediate bytes)
+    m["gdn_intra"] = (2 * qk + 2 * gb + akk + gb + gam,
+                      NT * H * 2 * (2 * C * C * D) + NT * HV * (2 * C ** 3 // 3), pv + 2 * nrm)
+    m["gdn_walk_fwd"] = (2 * qk + vv + akk + 2 * gb + h0 + vv + (st if want_ht else 0)
+                         + (tape if kept else 0) + (wuv if full else 0),
+                         T * HV * (6 * D * D + 4 * C * D), pv + 2 * nrm)
     if full:
-        # the full saved set: the forward walk also writes the state tape and v_new (bf16); w, u
-        # and the P rows are formed and copied by k_wy_full
-        fw = m["gdn_walk_fwd"]
-        m["gdn_walk_fwd"] = (fw[0] + tape + T * HV * D * 2, fw[1])
-        m["gdn_wy_full"] = (akk + qkin + vin + pv + 2 * scal_v + scal_q + 2 * T * HV * D * 2 + akk,
-                            T * HV * 2 * (2 * C * D))
-    out_qk = 2 * qkin if det else 2 * acc
-    m["gdn_chunk_grad"] = (2 * tape + 2 * qkin + 2 * vin + akk + pv + 2 * scal_v + 2 * scal_q + gam
-                           + vin + 2 * scal_v + out_qk,
-                           T * HV * 2 * (5 * D * D + 8 * C * D + 2 * C * C) + NT * H * 2 * (2 * C * C * D))
-    m["gdn_finalize_qk"] = (2 * acc + 2 * qkin + 2 * scal_q + 2 * qkin, 0)
-    m["gdn_fill_zero"] = (acc, 0)
+        m["gdn_wy_full"] = (akk + qk + vv + 2 * gb + 2 * wuv + akk, T * HV * 2 * (2 * C * D), pv + nrm)
+    m["gdn_intra_bwd"] = (2 * qk + gb, NT * H * 2 * (2 * C * C * D), pv + 2 * nrm)
+    rev = (2 * qk + vv + akk + 2 * gb + (st if has_dht else 0) + h0, T * HV * (6 * D * D + 4 * C * D),
+           pv + 2 * nrm + tape)
+    if kept:
+        m["gdn_walk_bwd"] = rev
+    else:
+        tw = (qk + vv + akk + 2 * gb + h0, T * HV * (4 * D * D + 2 * C * D), nrm + tape)
+        m["gdn_walk_pair"] = tuple(x + y for x, y in zip(tw, rev))
+    grad_alg = 2 * qk + 2 * vv + akk + 2 * gb + vv + 2 * gb + (2 * qk if det else 0) + (tape if kept else 0)
+    grad_int = (tape if kept else 2 * tape) + pv + 2 * nrm + (0 if det else 2 * acc)
+    m["gdn_chunk_grad"] = (grad_alg, T * HV * 2 * (5 * D * D + 8 * C * D + 2 * C * C) + NT * H * 2 * (2 * C * C * D),
+                           grad_int)
+    if not det:
+        m["gdn_finalize_qk"] = (2 * qk + 2 * qk, 0, 2 * acc + 2 * nrm)
+        m["gdn_fill_zero"] = (0, 0, acc)
     return m
 
 
-def step_roofline(T, HV, D, io_bytes, full=False):
-    """Op-level algorithmic work (inputs, outputs and the saved set; tapes excluded) per token. The
-    full saved set adds a bf16 state per chunk and v_new, w, u and the q.k tiles per token."""
+def step_roofline(T, HV, D, io_bytes, H=16, NT=None, N=1, has_h0=False, want_ht=False, has_dht=False,
+                  save_mode="light"):
+    """Op-level algorithmic work per token: MFMA flops of the chunked method and HBM bytes of the
+    inputs, outputs and the saved set (written by fwd and recompute, read by bwd), plus the states
+    a workload passes (h0 and dht read, ht and dh0 written). Tapes and other intermediates are not
+    counted. The full saved set adds a bf16 state per chunk and v_new, w, u and the q.k rows per
+    token; the kept-tape form adds the state only. Returns fwd, fwdbwd and ckpt (fwd + recompute +
+    bwd) records with the roofline time max(flops / MFMA peak, bytes / HBM peak)."""
     C = CHUNK
-    G = 3
+    G = HV // H
+    NT = T / C if NT is None else NT
     fl_f = 6 * D * D + 6 * C * D + 4 * C * D / G + 2 * C * C / 3
     fl_b = 16 * D * D + (12 + 2 / G) * 2 * C * D + 4 * C * C / 3
     fl_r = 2 * C * D / G + 2 * C * C / 3
-    inputs = 2 * 16 * D * io_bytes + HV * D * io_bytes + 2 * HV * 4
-    saved = HV * C * 2 + HV * 4 + HV * 4 / C
-    if full:
-        saved += HV * D * D * 2 / C + 3 * HV * D * 2 + HV * C * 2
-    b_f = inputs + HV * D * io_bytes + saved
-    b_b = inputs + HV * D * io_bytes + saved + 2 * 16 * D * io_bytes + HV * D * io_bytes + 2 * HV * 4
-    b_r = 16 * D * io_bytes + 2 * HV * 4 + saved
+    inputs = 2 * H * D * io_bytes + HV * D * io_bytes + 2 * HV * 4
+    saved = HV * C * 2 + HV * 4 + HV * 4 * NT / T
+    if save_mode in ("full", "tape"):
+        saved += HV * D * D * 2 * NT / T
+    if save_mode == "full":
+        saved += 3 * HV * D * 2 + HV * C * 2
+    state = N * HV * D * D * 4 / T if T else 0.0
+    b_f = inputs + HV * D * io_bytes + saved + state * (has_h0 + want_ht)
+    b_b = (inputs + HV * D * io_bytes + saved + 2 * H * D * io_bytes + HV * D * io_bytes + 2 * HV * 4
+           + state * (has_h0 + has_dht + has_h0))
+    # the recompute reads k, g, beta; its state walk (kept-tape and full forms) also v, and the full
+    # form's q.k rows q
+    b_r = (H * D * io_bytes + 2 * HV * 4 + saved + (HV * D * io_bytes if save_mode != "light" else 0)
+           + (H * D * io_bytes if save_mode == "full" else 0))
     out = {}
     for name, fl, by in (("fwd", fl_f, b_f), ("fwdbwd", fl_f + fl_b, b_f + b_b),
                          ("ckpt", fl_f + fl_r + fl_b, b_f + b_r + b_b)):
@@ -114,7 +152,7 @@ def source_sha(path):
 
 
 def load_traffic(kernel, workload):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
     path = os.path.join(ROOT, "profiles", "pmc_%s_%s.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
@@ -127,30 +165,38 @@ def load_traffic(kernel, workload):
 
 
 def cpu_baseline(w, inputs_dev):
-    """Time the FP64 oracle (fwd + bwd, all heads) on the two shortest documents of the workload."""
+    """Time the FP64 oracle on a bounded sample of the workload: every document in full, for the
+    first few q/k heads (with their value heads), enough (document, head) items to occupy the host
+    cores. The oracle's cost per token and head is the same everywhere, so the whole workload's
+    rate is the sample's tokens x H / sampled heads over its time. Times fwd and bwd (the oracle's
+    reverse mode recomputes its forward) separately; fwd+bwd = both, ckpt = 2 fwd + bwd."""
     import numpy as np
+    import torch
     import oracle
 
-    cu = inputs_dev["cu_seqlens"].cpu().numpy()
-    lens = np.diff(cu)
-    docs = sorted(np.argsort(lens, kind="stable")[:2].tolist())
-    tok = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in docs])
-    ti = __import__("torch").from_numpy(tok).to(inputs_dev["q"].device)
-    f = lambda t: None if t is None else t.index_select(0, ti).float().cpu().numpy()
-    q, k, v, g, b, dO = (f(inputs_dev[x]) for x in ("q", "k", "v", "g", "beta", "dO"))
-    cu1 = np.zeros(len(docs) + 1, np.int32)
-    cu1[1:] = np.cumsum(lens[docs])
     threads = oracle.default_threads()
-    used = min(threads, len(docs) * w.H)  # the oracle splits work over (document, q/k head) items
+    heads = max(1, min(w.H, math.ceil(threads / max(1, w.N))))
+    Gg = w.HV // w.H
+    vh = [j * Gg + gi for j in range(heads) for gi in range(Gg)]
+    f = lambda name, idx: inputs_dev[name][:, idx].float().cpu().numpy()
+    q, k = f("q", list(range(heads))), f("k", list(range(heads)))
+    v, g, b, dO = (f(x, vh) for x in ("v", "g", "beta", "dO"))
+    h0 = inputs_dev["h0"][:, vh].float().cpu().numpy() if inputs_dev.get("h0") is not None else None
+    cu = inputs_dev["cu_seqlens"].cpu().numpy()
+    used = min(threads, w.N * heads)  # the oracle splits work over (document, q/k head) items
     t0 = time.time()
-    oracle.fwd(cu1, q, k, v, g, b, None, l2norm=w.l2norm, threads=threads)
-    oracle.bwd(cu1, q, k, v, g, b, dO, None, None, l2norm=w.l2norm, threads=threads)
-    dt = time.time() - t0
-    ntok = int(len(tok))
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": "fwd+bwd of documents %s (%d tokens, all %d q/k and %d v heads, d=%d) of the same pack, "
-                      "FP64 token recurrence, %.1f s" % ("/".join(str(int(lens[n])) for n in docs), ntok, w.H,
-                                                          w.HV, w.d, dt)}
+    oracle.fwd(cu, q, k, v, g, b, h0, l2norm=w.l2norm, threads=threads)
+    t_f = time.time() - t0
+    t0 = time.time()
+    oracle.bwd(cu, q, k, v, g, b, dO, h0, None, l2norm=w.l2norm, threads=threads)
+    t_b = time.time() - t0
+    scale = w.H / heads  # whole-workload time = sample time x this
+    rate = lambda t: w.T / (t * scale)
+    return {"value": rate(t_f + t_b), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "fwd+bwd of all %d documents (%d tokens) for q/k heads 0..%d of %d with their %d value heads, "
+                      "d=%d, FP64 token recurrence: fwd %.1f s + bwd %.1f s; tokens/s scaled by %d/%d heads"
+                      % (w.N, w.T, heads - 1, w.H, len(vh), w.d, t_f, t_b, w.H, heads),
+            "fwd_tokens_per_s": rate(t_f), "ckpt_tokens_per_s": rate(2 * t_f + t_b), "threads": threads}
 
 
 COPY_BYTES = 1 << 30  # bytes read (and written) by the calibration copy
@@ -161,11 +207,12 @@ COPY_BYTES = 1 << 30  # bytes read (and written) by the calibration copy
 KERNEL_ORDER = {"k_tables": ["gdn_tables"], "k_intra": ["gdn_intra", "gdn_intra_bwd"],
                 "k_walk_fwd": ["gdn_walk_fwd", "gdn_walk_tape"], "k_write_tag": ["gdn_write_tag"],
                 "k_walk_pair": ["gdn_walk_pair"], "k_walk_bwd": ["gdn_walk_bwd"], "k_fill_zero": ["gdn_fill_zero"],
-                "k_chunk_grad": ["gdn_chunk_grad"], "k_finalize_qk": ["gdn_finalize_qk"]}
+                "k_chunk_grad": ["gdn_chunk_grad"], "k_finalize_qk": ["gdn_finalize_qk"],
+                "k_poison": ["gdn_poison"]}
 KERNEL_SOURCE = {"gdn_tables": "gdn_fwd.hip", "gdn_intra": "gdn_fwd.hip", "gdn_intra_bwd": "gdn_fwd.hip",
                  "gdn_walk_fwd": "gdn_fwd.hip", "gdn_walk_tape": "gdn_fwd.hip", "gdn_write_tag": "gdn_bwd.hip",
                  "gdn_walk_bwd": "gdn_bwd.hip", "gdn_walk_pair": "gdn_bwd.hip", "gdn_fill_zero": "gdn_bwd.hip", "gdn_chunk_grad": "gdn_bwd.hip",
-                 "gdn_finalize_qk": "gdn_bwd.hip"}
+                 "gdn_finalize_qk": "gdn_bwd.hip", "gdn_poison": "gdn_bwd.hip"}
 
 
 def _csv_rows(d, suffix):
@@ -295,6 +342,154 @@ def summarize_trace(trace_dir, command):
     print("\n".join(lines))
 
 
+def _nt(w):
+    return int(sum((L + CHUNK - 1) // CHUNK for L in w.lengths))
+
+
+def _workload_desc(w, save_mode, det):
+    lens = "/".join(str(x) for x in w.lengths[:4]) + ("/..." if w.N > 4 else "")
+    return ("%s: %d docs %s, %d tokens, (H,HV)=(%d,%d), d=%d, l2norm=%d%s, %s saved set, %s dq/dk reduction"
+            % (w.name, w.N, lens, w.T, w.H, w.HV, w.d, int(w.l2norm), ", h0, ht, dht" if w.has_h0 else "",
+               save_mode, "deterministic" if det else "atomic"))
+
+
+class Runner:
+    """Buffers and calls of one workload on the GPU (inputs resident in HBM)."""
+
+    def __init__(self, G, syn, w, dev, save_mode="light", det=True):
+        import torch
+        self.G, self.w, self.dev = G, w, dev
+        modes = {"light": G.SAVE_LIGHT, "full": G.SAVE_FULL, "tape": G.SAVE_TAPE}
+        self.inp = syn.make_inputs(w, device=dev)
+        self.p = G.problem_for(w, save_mode=modes[save_mode], deterministic=det)
+        self.pt = G.problem_for(w, save_mode=G.SAVE_TAPE, deterministic=det)  # kept-tape checkpoint
+        e = lambda n: torch.empty(n, dtype=torch.uint8, device=dev)
+        self.saved = e(G.gdn_saved_bytes(self.p))
+        self.saved_t = e(G.gdn_saved_bytes(self.pt))
+        self.ws_f = e(G.gdn_workspace_bytes(self.p, G.OP_FWD))
+        self.ws_r = e(G.gdn_workspace_bytes(self.p, G.OP_RECOMPUTE))
+        self.ws_rt = e(G.gdn_workspace_bytes(self.pt, G.OP_RECOMPUTE))
+        self.ws_b = e(G.gdn_workspace_bytes(self.p, G.OP_BWD))
+        self.ws_bt = e(G.gdn_workspace_bytes(self.pt, G.OP_BWD))
+        inp = self.inp
+        self.o = torch.empty_like(inp["v"])
+        self.ht = torch.empty((w.N, w.HV, w.d, w.d), dtype=torch.float32, device=dev) if w.want_ht else None
+        self.grads = dict(dq=torch.empty_like(inp["q"]), dk=torch.empty_like(inp["k"]), dv=torch.empty_like(inp["v"]),
+                          dg=torch.empty_like(inp["g"]), dbeta=torch.empty_like(inp["beta"]),
+                          dh0=torch.empty_like(inp["h0"]) if inp["h0"] is not None else None)
+        self.stream = torch.cuda.current_stream()
+        self.a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
+
+    def fwd(self):
+        self.G.gdn_fwd(self.p, *self.a, h0=self.inp["h0"], o=self.o, ht=self.ht, saved=self.saved,
+                       workspace=self.ws_f, stream=self.stream)
+
+    def recompute(self, kept=False):
+        p, sv, ws = (self.pt, self.saved_t, self.ws_rt) if kept else (self.p, self.saved, self.ws_r)
+        self.G.gdn_fwd_recompute(p, *self.a, h0=self.inp["h0"], saved=sv, workspace=ws, stream=self.stream)
+
+    def bwd(self, kept=False):
+        p, sv, ws = (self.pt, self.saved_t, self.ws_bt) if kept else (self.p, self.saved, self.ws_b)
+        self.G.gdn_bwd(p, *self.a, sv, self.inp["dO"], h0=self.inp["h0"], dht=self.inp["dht"], grads=self.grads,
+                       workspace=ws, stream=self.stream)
+
+    def op(self, name):
+        return {"fwd": self.fwd,
+                "fwdbwd": lambda: (self.fwd(), self.bwd()),
+                "ckpt": lambda: (self.fwd(), self.recompute(), self.bwd()),
+                "ckpt_kept_tape": lambda: (self.fwd(), self.recompute(kept=True), self.bwd(kept=True))}[name]
+
+
+def protocol_time(fn, flush, stream, warmup=10, groups=5, per_group=12):
+    """The pages' timing protocol, adapted: `warmup` untimed calls, then `groups` x `per_group`
+    timed calls; before each, `flush` (>= 512 MiB) is written and the stream synchronised, and HIP
+    events bracket the call alone. Returns the median (ms), the per-group medians and their drift
+    (max / min - 1)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(groups):
+        evs = []
+        for _ in range(per_group):
+            flush.fill_(1.0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        per.append([a.elapsed_time(b) for a, b in evs])
+    allv = [x for g in per for x in g]
+    med_g = [statistics.median(g) for g in per]
+    drift = max(med_g) / min(med_g) - 1.0
+    return {"median_ms": statistics.median(allv), "group_medians_ms": med_g, "drift": drift,
+            "drift_flag": drift > 0.02, "calls": len(allv)}
+
+
+def kernel_pass(lib, fn, steps):
+    """Per-kernel launch times over `steps` calls of fn, each timed alone (every launch bracketed
+    by HIP events on its own stream; a synchronisation between calls). Per kernel: launches per
+    call, summed launch time per call, span per call (first start to last end of its launches)
+    and mean launch duration (ms)."""
+    import torch
+    names = (ctypes.c_char_p * 256)()
+    st = (ctypes.c_double * 256)()
+    en = (ctypes.c_double * 256)()
+    lib.gdn_timing_launches.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    agg = {}
+    wall = []
+    for _ in range(steps):
+        lib.gdn_timing_reset()
+        lib.gdn_timing_enable(1)
+        fn()
+        torch.cuda.synchronize()
+        lib.gdn_timing_enable(0)
+        n = min(256, lib.gdn_timing_launches(256, names, st, en))
+        per = {}
+        for i in range(n):
+            per.setdefault(names[i].decode(), []).append((st[i], en[i]))
+        wall.append(max(en[i] for i in range(n)) - min(st[i] for i in range(n)))
+        for k, iv in per.items():
+            a = agg.setdefault(k, {"launches": 0, "sum_ms": 0.0, "span_ms": 0.0})
+            a["launches"] += len(iv)
+            a["sum_ms"] += sum(e - s for s, e in iv)
+            a["span_ms"] += max(e for _, e in iv) - min(s for s, _ in iv)
+    lib.gdn_timing_reset()
+    out = {}
+    for k, a in agg.items():
+        out[k] = {"launches_per_step": a["launches"] / steps, "sum_ms_per_step": a["sum_ms"] / steps,
+                  "span_ms_per_step": a["span_ms"] / steps, "avg_launch_ms": a["sum_ms"] / a["launches"]}
+    return out, statistics.median(wall)
+
+
+def roofline_of(kernels, models, workload_name, default_step):
+    """The kernel with the longest span per step (the largest block of the step's critical path;
+    kernels of a split launch plan overlap, so their summed launch time overstates it): its
+    algorithmic bytes or flops per launch over its mean launch duration, against the MI355X peak
+    that bounds it (the larger of the HBM and MFMA times at peak)."""
+    dom = max((k for k in kernels if k in models), key=lambda k: kernels[k]["span_ms_per_step"])
+    kt = kernels[dom]
+    per = kt["launches_per_step"]
+    by, fl, inter = (x / per for x in models[dom])
+    avg_s = kt["avg_launch_ms"] / 1e3
+    t_hbm, t_mfma = by / PEAK_HBM, fl / PEAK_BF16
+    if t_mfma > t_hbm:
+        roof = {"bound": "mfma", "achieved": fl / avg_s / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": by / avg_s / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    traffic = load_traffic(dom, workload_name) if default_step else None
+    roof["traffic"] = traffic
+    roof.update({"kernel": dom, "algorithmic_bytes": by, "algorithmic_flops": fl, "intermediate_bytes": inter,
+                 "traffic_ratio": (traffic / by) if traffic else None, "avg_launch_ms": kt["avg_launch_ms"],
+                 "launches_per_step": per, "span_ms_per_step": kt["span_ms_per_step"],
+                 "mfma_frac": fl / avg_s / PEAK_BF16, "hbm_frac": by / avg_s / PEAK_HBM})
+    return roof
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,7 +502,8 @@ def main():
                     help="full saved set: the forward also saves the states, v_new, w, u and the q.k tiles, "
                          "and the backward does not replay the states (default: the light saved set)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the fwd-only and ckpt timings")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the headline loop and the kernel pass (no protocol timings, no other workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain device copy of %d MiB (counter calibration)" %
                     (COPY_BYTES >> 20))
@@ -343,100 +539,50 @@ def main():
     w = syn.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    inp = syn.make_inputs(w, device=dev)
     det = not args.atomic
-    p = G.problem_for(w, save_mode=G.SAVE_FULL if args.full else G.SAVE_LIGHT, deterministic=det)
-    saved = torch.empty(G.gdn_saved_bytes(p), dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(G.gdn_workspace_bytes(p, G.OP_FWD), dtype=torch.uint8, device=dev)
-    ws_r = torch.empty(G.gdn_workspace_bytes(p, G.OP_RECOMPUTE), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(G.gdn_workspace_bytes(p, G.OP_BWD), dtype=torch.uint8, device=dev)
-    o = torch.empty_like(inp["v"])
-    ht = torch.empty((w.N, w.HV, w.d, w.d), dtype=torch.float32, device=dev) if w.want_ht else None
-    grads = dict(dq=torch.empty_like(inp["q"]), dk=torch.empty_like(inp["k"]), dv=torch.empty_like(inp["v"]),
-                 dg=torch.empty_like(inp["g"]), dbeta=torch.empty_like(inp["beta"]),
-                 dh0=torch.empty_like(inp["h0"]) if inp["h0"] is not None else None)
-    stream = torch.cuda.current_stream()
-    a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
+    mode = "full" if args.full else "light"
+    r = Runner(G, syn, w, dev, save_mode=mode, det=det)
+    stream = r.stream
+    step = r.op("fwdbwd")
 
-    def fwd():
-        G.gdn_fwd(p, *a, h0=inp["h0"], o=o, ht=ht, saved=saved, workspace=ws_f, stream=stream)
-
-    def recompute():
-        G.gdn_fwd_recompute(p, *a, h0=inp["h0"], saved=saved, workspace=ws_r, stream=stream)
-
-    def bwd():
-        G.gdn_bwd(p, *a, saved, inp["dO"], h0=inp["h0"], dht=inp["dht"], grads=grads, workspace=ws_b,
-                  stream=stream)
-
-    def timed(fn, steps, warmup, kernel_timing=False):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        if kernel_timing:
-            lib.gdn_timing_reset()
-            lib.gdn_timing_enable(1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.time()
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.time() - t0
-        if kernel_timing:
-            lib.gdn_timing_enable(0)
-        return e0.elapsed_time(e1) / 1e3, wall
-
-    step = lambda: (fwd(), bwd())
-    t_fb, wall_fb = timed(step, args.steps, args.warmup, kernel_timing=True)
-    # per-kernel totals over the timed region
-    names = (ctypes.c_char_p * 32)()
-    tot = (ctypes.c_double * 32)()
-    cnt = (ctypes.c_int * 32)()
-    lib.gdn_timing_collect.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    nk = lib.gdn_timing_collect(32, names, tot, cnt)
-    kernels = {names[i].decode(): {"total_ms": tot[i], "launches": cnt[i], "avg_ms": tot[i] / max(1, cnt[i])}
-               for i in range(min(nk, 32))}
-    lib.gdn_timing_reset()
-
-    extra = {}
-    if not args.no_extra:
-        ksteps = max(3, args.steps // 2)
-        t_f, _ = timed(fwd, ksteps, 1)
-        t_c, _ = timed(lambda: (fwd(), recompute(), bwd()), ksteps, 1)
-        extra["fwd"] = {"tokens_per_s": w.T * ksteps / t_f, "ms": 1e3 * t_f / ksteps}
-        extra["ckpt"] = {"tokens_per_s": w.T * ksteps / t_c, "ms": 1e3 * t_c / ksteps}
-
+    # ---- headline: exactly --steps steps back to back, synchronised on both sides
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    t_fb = e0.elapsed_time(e1) / 1e3
     ms = 1e3 * t_fb / args.steps
     value = w.T * args.steps / t_fb
-    io = 2 if w.dtype == "bf16" else 4
-    NT = int(sum((L + CHUNK - 1) // CHUNK for L in w.lengths))
-    models = kernel_models(w.T, NT, w.N, w.H, w.HV, w.d, io, has_h0=w.has_h0, det=det, full=args.full)
-    # dominant kernel = largest share of the timed step (summed launch time). A kernel may run as
-    # several launches per step (the longest document's and the others'); its per-launch
-    # algorithmic work is then the step's divided by the launches, so that achieved = the step's
-    # work / the step's summed launch time (a lower bound when the launches overlap in time).
-    dom = max((k for k in kernels if k in models), key=lambda k: kernels[k]["total_ms"])
-    per_step = kernels[dom]["launches"] / args.steps
-    by, fl = (x / per_step for x in models[dom])
-    avg_s = kernels[dom]["avg_ms"] / 1e3
-    t_hbm, t_mfma = by / PEAK_HBM, fl / PEAK_BF16
-    if t_mfma > t_hbm:
-        roof = {"bound": "mfma", "achieved": fl / avg_s / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": by / avg_s / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    # the committed counters are of the default step (light saved set, deterministic reduction)
-    default_kernel = not args.full and not (args.atomic and dom in ("gdn_chunk_grad", "gdn_fill_zero",
-                                                                    "gdn_finalize_qk"))
-    roof["traffic"] = load_traffic(dom, args.workload) if default_kernel else None
-    roof["kernel"] = dom
-    roof["algorithmic_bytes"] = by
-    roof["algorithmic_flops"] = fl
-    roof["avg_launch_ms"] = kernels[dom]["avg_ms"]
-    roof["launches_per_step"] = per_step
 
-    sr = step_roofline(w.T, w.HV, w.d, io, full=args.full)
+    # ---- per-kernel pass (separate from the headline loop)
+    kernels, step_wall_ms = kernel_pass(lib, step, max(3, min(args.steps, 10)))
+    io = 2 if w.dtype == "bf16" else 4
+    NT = _nt(w)
+    models = kernel_models(w.T, NT, w.N, w.H, w.HV, w.d, io, has_h0=w.has_h0, has_dht=w.has_dht,
+                           want_ht=w.want_ht, det=det, save_mode=mode)
+    default_step = mode == "light" and det
+    roof = roofline_of(kernels, models, args.workload, default_step)
+    kern_out = {}
+    for k, v in sorted(kernels.items()):
+        d = dict(v)
+        if k in models:
+            per = v["launches_per_step"]
+            d.update(algorithmic_bytes_per_launch=models[k][0] / per, flops_per_launch=models[k][1] / per,
+                     intermediate_bytes_per_launch=models[k][2] / per)
+            tr = load_traffic(k, args.workload) if default_step else None
+            if tr:
+                d.update(traffic_bytes_per_launch=tr, traffic_ratio=tr / (models[k][0] / per))
+        kern_out[k] = d
+
+    sr = step_roofline(w.T, w.HV, w.d, io, H=w.H, NT=NT, N=w.N, has_h0=w.has_h0, want_ht=w.want_ht,
+                       has_dht=w.has_dht, save_mode=mode)
     out = {
         "metric": METRIC,
         "value": value,
@@ -450,22 +596,54 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: %d docs %s, %d tokens, (H,HV)=(%d,%d), d=%d, l2norm=%d, %s saved set, "
-                               "%s dq/dk reduction" % (w.name, w.N, "/".join(str(x) for x in w.lengths[:4]) +
-                                                       ("/..." if w.N > 4 else ""), w.T, w.H, w.HV, w.d,
-                                                       int(w.l2norm), "full" if args.full else "light",
-                                                       "deterministic" if det else "atomic"),
-                   "global_batch": w.T, "seq_len": max(w.lengths), "parallelism": "none (1 GPU)"},
+        "config": {"workload": _workload_desc(w, mode, det), "global_batch": w.T, "seq_len": max(w.lengths),
+                   "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "step_roofline": {"op": "fwdbwd", "roofline_ms": 1e3 * sr["fwdbwd"]["roofline_s"],
-                          "frac": sr["fwdbwd"]["roofline_s"] / (ms / 1e3)},
-        "kernels_ms_per_step": {k: v["total_ms"] / args.steps for k, v in sorted(kernels.items())},
-        "wall_s": wall_fb,
+                          "frac": sr["fwdbwd"]["roofline_s"] / (ms / 1e3),
+                          "bytes_per_token": sr["fwdbwd"]["bytes_per_token"],
+                          "flops_per_token": sr["fwdbwd"]["flops_per_token"]},
+        "kernels": kern_out,
+        "kernel_pass_step_ms": step_wall_ms,
+        "wall_s": wall,
     }
-    for k, v in extra.items():
-        out[k] = dict(v, roofline_frac=sr[k]["roofline_s"] / (v["ms"] / 1e3))
+
+    if not args.no_extra:
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        prot = {}
+        for op in ("fwd", "fwdbwd", "ckpt", "ckpt_kept_tape"):
+            t = protocol_time(r.op(op), flush, stream)
+            sr_op = sr["ckpt" if op.startswith("ckpt") else op]
+            if op == "ckpt_kept_tape":
+                sr_op = step_roofline(w.T, w.HV, w.d, io, H=w.H, NT=NT, N=w.N, has_h0=w.has_h0, want_ht=w.want_ht,
+                                      has_dht=w.has_dht, save_mode="tape")["ckpt"]
+            t.update(tokens_per_s=w.T / (t["median_ms"] / 1e3), roofline_ms=1e3 * sr_op["roofline_s"],
+                     roofline_frac=sr_op["roofline_s"] / (t["median_ms"] / 1e3))
+            prot[op] = t
+        out["protocol"] = prot
+        del r
+        torch.cuda.empty_cache()
+        cfgs = {}
+        for name, op in (("single8k", "fwd"), ("cp4share", "fwdbwd"), ("short512", "ckpt")):
+            wc = syn.WORKLOADS[name]
+            rc = Runner(G, syn, wc, dev, save_mode="light", det=wc.deterministic or det)
+            t = protocol_time(rc.op(op), flush, stream)
+            ioc = 2 if wc.dtype == "bf16" else 4
+            src = step_roofline(wc.T, wc.HV, wc.d, ioc, H=wc.H, NT=_nt(wc), N=wc.N, has_h0=wc.has_h0,
+                                want_ht=wc.want_ht, has_dht=wc.has_dht)[op]
+            t.update(op=op, workload=_workload_desc(wc, "light", wc.deterministic or det),
+                     tokens_per_s=wc.T / (t["median_ms"] / 1e3), roofline_ms=1e3 * src["roofline_s"],
+                     roofline_frac=src["roofline_s"] / (t["median_ms"] / 1e3))
+            cfgs[name] = t
+            del rc
+            torch.cuda.empty_cache()
+        out["configs"] = cfgs
+        del flush
+        r = None
     if not args.no_cpu_baseline:
+        inp = syn.make_inputs(w, device=dev)
         out["cpu_baseline"] = cpu_baseline(w, inp)
+        del inp
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

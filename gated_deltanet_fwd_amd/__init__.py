@@ -1,13 +1,17 @@
 """Python binding of the MI355X gated-delta-rule training kernel (libgdn.so, include/gdn.h).
 
 Argument marshalling only: every step of the computation runs in the HIP kernels behind the C
-ABI. PyTorch supplies device memory and the current stream. The functions carry the C names:
+ABI. PyTorch supplies device memory and streams: the launch stream (torch's current stream unless
+one is given) and, for problems whose longest document runs apart from the others, an auxiliary
+stream that this module keeps per device and names in the problem descriptor. Buffers that a call
+allocates are allocated on its launch stream. The functions carry the C names:
 
     gdn_saved_bytes(problem)                      -> int
     gdn_workspace_bytes(problem, op)              -> int
     gdn_fwd(problem, q, k, v, g, beta, cu, ...)   -> (o, ht, saved)
     gdn_fwd_recompute(problem, q, k, v, g, beta, cu, ...) -> saved
     gdn_bwd(problem, q, k, v, g, beta, cu, saved, dO, ...) -> dict of gradients
+    gdn_status(problem, op, workspace)            -> int (synchronises the stream)
 
 A missing or unloadable library raises ImportError-like errors at first use; there is no other
 code path.
@@ -26,11 +30,12 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ESAVED, GDN_EWORKSPACE, GDN_EHIP = range(6)
 DTYPE_BF16, DTYPE_F32 = 0, 1
-SAVE_LIGHT, SAVE_FULL = 0, 1
+SAVE_LIGHT, SAVE_FULL, SAVE_TAPE = 0, 1, 2
 OP_FWD, OP_RECOMPUTE, OP_BWD = 0, 1, 2
+ABI_VERSION = 2
 
-EXPORTS = ("gdn_saved_bytes", "gdn_workspace_bytes", "gdn_fwd", "gdn_fwd_recompute", "gdn_bwd", "gdn_last_error",
-           "gdn_abi_version")
+EXPORTS = ("gdn_saved_bytes", "gdn_workspace_bytes", "gdn_fwd", "gdn_fwd_recompute", "gdn_bwd", "gdn_status",
+           "gdn_last_error", "gdn_abi_version")
 
 
 class GdnError(RuntimeError):
@@ -53,6 +58,9 @@ class _Problem(ctypes.Structure):
         ("save_mode", ctypes.c_int32),
         ("deterministic", ctypes.c_int32),
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("aux_stream", ctypes.c_void_p),
+        ("segments", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
     ]
 
 
@@ -79,10 +87,15 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_fwd_recompute.restype = I
     lib.gdn_bwd.argtypes = [pp] + [P] * 17 + [Z, P]
     lib.gdn_bwd.restype = I
+    lib.gdn_status.argtypes = [pp, I, P, P]
+    lib.gdn_status.restype = I
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_abi_version.argtypes = []
     lib.gdn_abi_version.restype = I
+    if lib.gdn_abi_version() != ABI_VERSION:
+        raise OSError("libgdn.so has ABI version %d, this binding expects %d: rebuild it" %
+                      (lib.gdn_abi_version(), ABI_VERSION))
     _lib = lib
     return lib
 
@@ -92,9 +105,11 @@ class Problem:
 
     def __init__(self, cu_seqlens_host, h_qk: int, h_v: int, d: int, dtype=torch.bfloat16, l2norm: bool = True,
                  has_h0: bool = False, want_ht: bool = False, save_mode: int = SAVE_LIGHT,
-                 deterministic: bool = True):
+                 deterministic: bool = True, use_aux_stream=True, segments: int = 0):
         self.cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
         self.dtype = dtype
+        # True: the module's auxiliary stream of the device; False: one stream; or a stream object
+        self.use_aux_stream = use_aux_stream
         self.st = _Problem(
             n_seqs=int(self.cu.shape[0] - 1),
             h_qk=int(h_qk),
@@ -108,6 +123,9 @@ class Problem:
             save_mode=int(save_mode),
             deterministic=int(bool(deterministic)),
             cu_seqlens_host=self.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            aux_stream=None,
+            segments=int(segments),
+            reserved0=0,
         )
 
     @property
@@ -126,10 +144,49 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _torch_stream(stream, device) -> torch.cuda.Stream:
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+_aux_streams: Dict[int, torch.cuda.Stream] = {}
+
+
+def aux_stream(device) -> torch.cuda.Stream:
+    """The auxiliary stream this module names in problems on `device` (created on first use, kept
+    for the life of the process, default priority)."""
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    if idx not in _aux_streams:
+        _aux_streams[idx] = torch.cuda.Stream(device=idx)
+    return _aux_streams[idx]
+
+
+class _Call:
+    """Launch context of one call: the launch stream, allocations on it, and the problem's auxiliary
+    stream set for the call."""
+
+    def __init__(self, p: "Problem", device, stream):
+        self.p = p
+        self.device = device
+        self.stream = _torch_stream(stream, device)
+        u = p.use_aux_stream
+        aux = u if isinstance(u, torch.cuda.Stream) else aux_stream(device) if u else None
+        p.st.aux_stream = None if aux is None or aux.cuda_stream == self.stream.cuda_stream else aux.cuda_stream
+
+    def empty(self, *shape, dtype):
+        with torch.cuda.stream(self.stream):
+            return torch.empty(*shape, dtype=dtype, device=self.device)
+
+    def empty_like(self, t):
+        with torch.cuda.stream(self.stream):
+            return torch.empty_like(t)
+
+    def handle(self) -> ctypes.c_void_p:
+        return ctypes.c_void_p(self.stream.cuda_stream)
 
 
 def _check(rc: int):
@@ -151,39 +208,35 @@ def gdn_workspace_bytes(p: Problem, op: int) -> int:
     return int(n)
 
 
-def _empty_bytes(n: int, device) -> torch.Tensor:
-    return torch.empty(n, dtype=torch.uint8, device=device)
-
-
 def gdn_fwd(p: Problem, q, k, v, g, beta, cu_seqlens, h0=None, o=None, ht=None, saved=None, workspace=None,
             stream=None):
     """Forward: returns (o, ht or None, saved)."""
     lib = load_library()
-    dev = q.device
+    c = _Call(p, q.device, stream)
     T, HV, d = p.T, p.st.h_v, p.st.d
     if o is None:
-        o = torch.empty((T, HV, d), dtype=q.dtype, device=dev)
+        o = c.empty((T, HV, d), dtype=q.dtype)
     if p.st.want_ht and ht is None:
-        ht = torch.empty((p.N, HV, d, d), dtype=torch.float32, device=dev)
+        ht = c.empty((p.N, HV, d, d), dtype=torch.float32)
     if saved is None:
-        saved = _empty_bytes(gdn_saved_bytes(p), dev)
+        saved = c.empty(gdn_saved_bytes(p), dtype=torch.uint8)
     if workspace is None:
-        workspace = _empty_bytes(gdn_workspace_bytes(p, OP_FWD), dev)
+        workspace = c.empty(gdn_workspace_bytes(p, OP_FWD), dtype=torch.uint8)
     _check(lib.gdn_fwd(p.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o),
-                       _ptr(ht), _ptr(saved), _ptr(workspace), workspace.numel(), _stream(stream)))
+                       _ptr(ht), _ptr(saved), _ptr(workspace), workspace.numel(), c.handle()))
     return o, ht, saved
 
 
 def gdn_fwd_recompute(p: Problem, q, k, v, g, beta, cu_seqlens, h0=None, saved=None, workspace=None, stream=None):
     """Checkpoint re-run of the forward: returns the saved set only."""
     lib = load_library()
-    dev = q.device
+    c = _Call(p, q.device, stream)
     if saved is None:
-        saved = _empty_bytes(gdn_saved_bytes(p), dev)
+        saved = c.empty(gdn_saved_bytes(p), dtype=torch.uint8)
     if workspace is None:
-        workspace = _empty_bytes(gdn_workspace_bytes(p, OP_RECOMPUTE), dev)
+        workspace = c.empty(gdn_workspace_bytes(p, OP_RECOMPUTE), dtype=torch.uint8)
     _check(lib.gdn_fwd_recompute(p.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                 _ptr(h0), _ptr(saved), _ptr(workspace), workspace.numel(), _stream(stream)))
+                                 _ptr(h0), _ptr(saved), _ptr(workspace), workspace.numel(), c.handle()))
     return saved
 
 
@@ -191,25 +244,33 @@ def gdn_bwd(p: Problem, q, k, v, g, beta, cu_seqlens, saved, dO, h0=None, dht=No
             stream=None) -> Dict[str, torch.Tensor]:
     """Backward: returns dict dq, dk, dv, dg, dbeta, dh0 (dh0 None without h0)."""
     lib = load_library()
-    dev = q.device
+    c = _Call(p, q.device, stream)
     if grads is None:
-        grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-                     dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
-                     dh0=torch.empty_like(h0) if (p.st.has_h0 and h0 is not None) else None)
+        grads = dict(dq=c.empty_like(q), dk=c.empty_like(k), dv=c.empty_like(v), dg=c.empty_like(g),
+                     dbeta=c.empty_like(beta),
+                     dh0=c.empty_like(h0) if (p.st.has_h0 and h0 is not None) else None)
     if workspace is None:
-        workspace = _empty_bytes(gdn_workspace_bytes(p, OP_BWD), dev)
+        workspace = c.empty(gdn_workspace_bytes(p, OP_BWD), dtype=torch.uint8)
     _check(lib.gdn_bwd(p.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(h0),
                        _ptr(saved), _ptr(dO), _ptr(dht), _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]),
                        _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads.get("dh0")), _ptr(workspace),
-                       workspace.numel(), _stream(stream)))
+                       workspace.numel(), c.handle()))
     return grads
 
 
+def gdn_status(p: Problem, op: int, workspace, stream=None) -> int:
+    """Device-side status of the last call of `op` on this workspace: GDN_OK, GDN_EINVAL or
+    GDN_ESAVED (synchronises the launch stream)."""
+    c = _Call(p, workspace.device, stream)
+    return int(load_library().gdn_status(p.ref(), int(op), _ptr(workspace), c.handle()))
+
+
 def problem_for(w, save_mode: int = SAVE_LIGHT, deterministic: Optional[bool] = None, l2norm: Optional[bool] = None,
-                want_ht: Optional[bool] = None) -> Problem:
+                want_ht: Optional[bool] = None, use_aux_stream=True, segments: int = 0) -> Problem:
     """Problem descriptor for a synthetic workload description (see synthetic.Workload)."""
     cu = np.zeros(w.N + 1, dtype=np.int32)
     cu[1:] = np.cumsum(np.asarray(w.lengths, dtype=np.int64))
     return Problem(cu, w.H, w.HV, w.d, dtype=w.torch_dtype, l2norm=w.l2norm if l2norm is None else l2norm,
                    has_h0=w.has_h0, want_ht=w.want_ht if want_ht is None else want_ht, save_mode=save_mode,
-                   deterministic=w.deterministic if deterministic is None else deterministic)
+                   deterministic=w.deterministic if deterministic is None else deterministic,
+                   use_aux_stream=use_aux_stream, segments=segments)

@@ -1,15 +1,16 @@
 // Host side of the C ABI in include/gdn.h: validation, buffer layouts, saved-set tagging and the
-// launch sequence of each call. No device memory is allocated or freed here and nothing
-// synchronises. Launches go to the caller's stream; when one document's chain work dominates,
-// the other documents' intra and walk launches go to a second stream of the library's own
-// (one per device, default priority), forked from and joined back into the caller's stream.
+// launch sequence of each call. No device memory is allocated or freed here, no stream is
+// created and nothing synchronises (except the gdn_status query). Launches go to the caller's
+// stream; when one document's chain work dominates and the caller names an auxiliary stream,
+// the other documents' intra and walk launches go to that stream, forked from and joined back
+// into the caller's stream with events from a per-thread pool.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -18,10 +19,6 @@
 
 #include "gdn.h"
 #include "gdn_internal.h"
-
-namespace gdn {
-int launch_write_tag(void* dst, const uint64_t* words, void* stream);
-}
 
 namespace {
 
@@ -40,7 +37,7 @@ int fail(int code, const char* fmt, ...) {
 constexpr int kChunk = 64;
 constexpr size_t kAlign = 256;
 constexpr size_t kTagBytes = 256;
-constexpr uint64_t kMagic = 0x31564153'4e4447ULL; // "GDNSAV1"
+constexpr uint64_t kMagic = 0x32564153'4e4447ULL; // "GDNSAV2"
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -58,8 +55,11 @@ int check_problem(const gdn_problem* p, Sizes* s) {
   if (p->d != 64 && p->d != 128) return fail(GDN_EUNSUPPORTED, "d must be 64 or 128 (got %d)", p->d);
   if (p->dtype != GDN_DTYPE_BF16 && p->dtype != GDN_DTYPE_F32)
     return fail(GDN_EUNSUPPORTED, "unsupported dtype %d", p->dtype);
-  if (p->save_mode != GDN_SAVE_LIGHT && p->save_mode != GDN_SAVE_FULL)
-    return fail(GDN_EINVAL, "save_mode must be light (0) or full (1)");
+  if (p->save_mode != GDN_SAVE_LIGHT && p->save_mode != GDN_SAVE_FULL && p->save_mode != GDN_SAVE_TAPE)
+    return fail(GDN_EINVAL, "save_mode must be light (0), full (1) or tape (2)");
+  if (p->segments < 0) return fail(GDN_EINVAL, "segments must be >= 0 (got %d)", p->segments);
+  if (p->segments > 1) return fail(GDN_EUNSUPPORTED, "segmented walks are not available in this build");
+  if (p->reserved0 != 0) return fail(GDN_EINVAL, "reserved0 must be 0");
   if (!p->cu_seqlens_host) return fail(GDN_EINVAL, "cu_seqlens_host is NULL");
   const int32_t* cu = p->cu_seqlens_host;
   if (cu[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0] must be 0");
@@ -81,11 +81,15 @@ int check_problem(const gdn_problem* p, Sizes* s) {
   return GDN_OK;
 }
 
+// The saved set keeps the state tape in the full and the kept-tape forms; the full form also
+// keeps v_new, w, u and the q.k rows.
+bool keeps_tape(int save_mode) { return save_mode == GDN_SAVE_FULL || save_mode == GDN_SAVE_TAPE; }
+
 struct SavedLayout {
   size_t akk, gcum, gamma, htape, vnew, w, u, aqk, total;
 };
 
-SavedLayout saved_layout(const Sizes& s, int full) {
+SavedLayout saved_layout(const Sizes& s, int save_mode) {
   SavedLayout L{};
   size_t off = kTagBytes;
   auto take = [&](size_t bytes) {
@@ -96,8 +100,8 @@ SavedLayout saved_layout(const Sizes& s, int full) {
   L.akk = take((size_t)s.T * s.HV * kChunk * 2);
   L.gcum = take((size_t)s.T * s.HV * 4);
   L.gamma = take((size_t)s.NT * s.HV * 4);
-  if (full) {
-    L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
+  if (keeps_tape(save_mode)) L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
+  if (save_mode == GDN_SAVE_FULL) {
     L.vnew = take((size_t)s.T * s.HV * s.D * 2);
     L.w = take((size_t)s.T * s.HV * s.D * 2);
     L.u = take((size_t)s.T * s.HV * s.D * 2);
@@ -112,7 +116,7 @@ struct WorkLayout {
       total;
 };
 
-WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
+WorkLayout work_layout(const Sizes& s, int op, int save_mode, int deterministic) {
   WorkLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -132,7 +136,7 @@ WorkLayout work_layout(const Sizes& s, int op, int full, int deterministic) {
   // the state handed from one piece of the longest document's walk to the next
   if (op != GDN_OP_BWD) L.state = take((size_t)s.HV * s.D * s.D * 4);
   if (op == GDN_OP_BWD) {
-    if (!full) L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
+    if (!keeps_tape(save_mode)) L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
     L.dstape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
     if (!deterministic) {
       L.dqacc = take((size_t)s.T * s.H * s.D * 4);
@@ -161,11 +165,15 @@ uint64_t problem_hash(const gdn_problem* p) {
   return h;
 }
 
-// Saved buffers written by gdn_fwd / gdn_fwd_recompute in this process, with the hash of the
-// problem they were written for. gdn_bwd refuses a buffer that is not listed under the hash of
-// its own problem.
-std::mutex g_reg_mu;
-std::unordered_map<const void*, uint64_t> g_registry;
+// The four words of the saved set's tag for this problem: magic, ABI version, save mode and
+// the hash of the problem (sizes, flags, cu_seqlens). gdn_fwd / gdn_fwd_recompute write them,
+// the first kernel of gdn_bwd compares them.
+void tag_words(const gdn_problem* p, uint64_t w[4]) {
+  w[0] = kMagic;
+  w[1] = (uint64_t)GDN_ABI_VERSION;
+  w[2] = (uint64_t)p->save_mode;
+  w[3] = problem_hash(p);
+}
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -182,8 +190,8 @@ int check_ptr(const void* ptr, const char* name) {
   } while (0)
 
 // Optional kernel timing for benchmarks: while enabled, each launch is bracketed by two
-// hipEvents recorded on the call's stream; gdn_timing_collect waits for them and sums the
-// elapsed time per kernel name.
+// hipEvents recorded on the stream it goes to; gdn_timing_collect waits for them and sums the
+// elapsed time per kernel name, gdn_timing_launches returns each launch's start and end.
 std::atomic<int> g_timing_on{0};
 std::mutex g_timing_mu;
 struct PendingEvent {
@@ -222,6 +230,45 @@ void timing_end(const char* name, hipEvent_t start, void* stream) {
   } while (0)
 #define LAUNCH(name, x) LAUNCH_ON(stream, name, x)
 
+// Events for ordering the caller's two streams: a pool per thread and device, reused by every
+// call of the thread (a wait enqueued with hipStreamWaitEvent refers to the record made before
+// it, so recording the same event again in a later call is safe). The events live until the
+// process ends.
+struct EventPool {
+  std::vector<hipEvent_t> ev;
+  size_t next = 0;
+};
+thread_local std::unordered_map<int, EventPool> t_pools;
+
+struct CallEvents {
+  EventPool* pool = nullptr;
+  int take(hipEvent_t* out) {
+    if (!pool) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_EHIP, "hipGetDevice failed");
+      pool = &t_pools[dev];
+      pool->next = 0;
+    }
+    if (pool->next == pool->ev.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+        return fail(GDN_EHIP, "hipEventCreate failed");
+      pool->ev.push_back(e);
+    }
+    *out = pool->ev[pool->next++];
+    return GDN_OK;
+  }
+  // Orders `to` after the work enqueued so far on `from`.
+  int order(hipStream_t from, hipStream_t to) {
+    hipEvent_t e = nullptr;
+    CHECK(take(&e));
+    hipError_t r = hipEventRecord(e, from);
+    if (r == hipSuccess) r = hipStreamWaitEvent(to, e, 0);
+    if (r != hipSuccess) return fail(GDN_EHIP, "stream fork/join: %s", hipGetErrorString(r));
+    return GDN_OK;
+  }
+};
+
 void fill_common(gdn::Args& a, const Sizes& s, const gdn_problem* p) {
   std::memset(&a, 0, sizeof a);
   a.N = s.N;
@@ -241,10 +288,10 @@ void fill_common(gdn::Args& a, const Sizes& s, const gdn_problem* p) {
 
 // Two-part launch plan. The walks are serial over a document's chunks, so the longest document
 // sets their run time while the others' chains finish early and leave CUs idle. When it is
-// clearly the longest (at least 5/4 of the next one, and at least 64 chunks), its intra and walk
-// launches (part A) run on the caller's stream and the other documents' (part B) on a second
-// stream: its walk then starts after its own intra launch rather than after everyone's, and
-// part B fills the CUs that part A leaves free.
+// clearly the longest (at least 5/4 of the next one, and at least 64 chunks) and the caller gave
+// an auxiliary stream, its intra and walk launches (part A) run on the caller's stream and the
+// other documents' (part B) on the auxiliary stream: its walk then starts after its own intra
+// launch rather than after everyone's, and part B fills the CUs that part A leaves free.
 struct Split {
   bool on = false;
   int n0 = 0;          // the longest document (ties: the lowest index), rank 0 of the tables
@@ -273,6 +320,12 @@ Split plan_split(const gdn_problem* p, const Sizes& s) {
   return sp;
 }
 
+// The caller's auxiliary stream, or NULL if there is none (or it is `stream` itself).
+hipStream_t aux_of(const gdn_problem* p, void* stream) {
+  if (!p->aux_stream || p->aux_stream == stream) return nullptr;
+  return (hipStream_t)p->aux_stream;
+}
+
 void range_a(gdn::Args& a, const Split& sp) {
   a.grp_off = 0;
   a.grp_end = a.H;
@@ -291,35 +344,6 @@ void range_b(gdn::Args& a, const Split& sp) {
   a.c_skip_at = sp.cA0;
   a.c_skip = sp.cA;
   a.c_count = a.NT - sp.cA;
-}
-
-// The library's second stream on the current device, created on first use and kept for the
-// life of the process; NULL if it cannot be created (the calls then use one stream).
-hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t streams[64];
-  static bool tried[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lk(mu);
-  if (!tried[dev]) {
-    tried[dev] = true;
-    hipStream_t st = nullptr;
-    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess) streams[dev] = st;
-  }
-  return streams[dev];
-}
-
-// Orders `to` after the work enqueued so far on `from` (an event of its own per call, so that
-// concurrent calls never share one).
-int stream_wait(hipStream_t from, hipStream_t to) {
-  hipEvent_t e = nullptr;
-  if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return fail(GDN_EHIP, "hipEventCreate failed");
-  hipError_t r = hipEventRecord(e, from);
-  if (r == hipSuccess) r = hipStreamWaitEvent(to, e, 0);
-  hipEventDestroy(e);
-  if (r != hipSuccess) return fail(GDN_EHIP, "stream fork/join: %s", hipGetErrorString(r));
-  return GDN_OK;
 }
 
 void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
@@ -347,8 +371,8 @@ void bind_saved(gdn::Args& a, const SavedLayout& L, void* saved) {
   a.akk = (uint16_t*)(b + L.akk);
   a.gcum = (float*)(b + L.gcum);
   a.gamma = (float*)(b + L.gamma);
-  if (L.htape) {
-    a.htape = (uint16_t*)(b + L.htape);
+  if (L.htape) a.htape = (uint16_t*)(b + L.htape);
+  if (L.vnew) {
     a.vnew = (uint16_t*)(b + L.vnew);
     a.w = (uint16_t*)(b + L.w);
     a.u = (uint16_t*)(b + L.u);
@@ -389,10 +413,11 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
   CHECK(check_ptr(saved, "saved"));
   CHECK(check_ptr(workspace, "workspace"));
   const int full = p->save_mode == GDN_SAVE_FULL;
-  const WorkLayout W = work_layout(s, write_o ? GDN_OP_FWD : GDN_OP_RECOMPUTE, full, p->deterministic);
+  const bool tape = keeps_tape(p->save_mode);
+  const WorkLayout W = work_layout(s, write_o ? GDN_OP_FWD : GDN_OP_RECOMPUTE, p->save_mode, p->deterministic);
   if (workspace_bytes < W.total)
     return fail(GDN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
-  const SavedLayout L = saved_layout(s, full);
+  const SavedLayout L = saved_layout(s, p->save_mode);
   gdn::Args a;
   fill_common(a, s, p);
   a.q = q;
@@ -408,15 +433,17 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
   bind_workspace(a, W, workspace);
   bind_saved(a, L, saved);
 
-  const bool walk = write_o || full;
+  // the light recompute runs no walk: the saved set needs only the chunk tables and the intra pass
+  const bool walk = write_o || tape;
   const Split sp = walk ? plan_split(p, s) : Split{};
-  hipStream_t side = sp.on ? side_stream() : nullptr;
+  hipStream_t side = sp.on ? aux_of(p, stream) : nullptr;
+  CallEvents ev;
   if (side) a.grp_split = a.H;
-  LAUNCH("gdn_tables", gdn::launch_tables(a, stream));
+  LAUNCH("gdn_tables", gdn::launch_tables(a, nullptr, nullptr, stream));
   const char* walk_name = write_o ? "gdn_walk_fwd" : "gdn_walk_tape";
   if (!side) {
     LAUNCH("gdn_intra", gdn::launch_intra(a, 0, stream));
-    if (walk) LAUNCH(walk_name, gdn::launch_walk_fwd(a, write_o, full, stream));
+    if (walk) LAUNCH(walk_name, gdn::launch_walk_fwd(a, write_o, tape, full, stream));
   } else {
     gdn::Args aa = a, ab = a;
     range_a(aa, sp);
@@ -445,43 +472,27 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
       if (i + 1 < pieces) ap[i].want_ht = 0;
     }
     LAUNCH("gdn_intra", gdn::launch_intra(ap[0], 0, stream));
-    CHECK(stream_wait((hipStream_t)stream, side));
+    CHECK(ev.order((hipStream_t)stream, side));
     hipEvent_t ready[4] = {nullptr, nullptr, nullptr, nullptr};
     for (int i = 1; i < pieces; ++i) {
       LAUNCH_ON(side, "gdn_intra", gdn::launch_intra(ap[i], 0, side));
-      if (hipEventCreateWithFlags(&ready[i], hipEventDisableTiming) != hipSuccess ||
-          hipEventRecord(ready[i], side) != hipSuccess) {
-        for (hipEvent_t e : ready)
-          if (e) hipEventDestroy(e);
-        return fail(GDN_EHIP, "piece event failed");
-      }
+      CHECK(ev.take(&ready[i]));
+      if (hipEventRecord(ready[i], side) != hipSuccess) return fail(GDN_EHIP, "piece event record failed");
     }
     LAUNCH_ON(side, "gdn_intra", gdn::launch_intra(ab, 0, side));
-    LAUNCH_ON(side, walk_name, gdn::launch_walk_fwd(ab, write_o, full, side));
-    int rc = GDN_OK;
-    for (int i = 0; i < pieces && rc == GDN_OK; ++i) {
+    LAUNCH_ON(side, walk_name, gdn::launch_walk_fwd(ab, write_o, tape, full, side));
+    for (int i = 0; i < pieces; ++i) {
       if (i > 0 && hipStreamWaitEvent((hipStream_t)stream, ready[i], 0) != hipSuccess)
-        rc = fail(GDN_EHIP, "piece event wait failed");
-      else {
-        hipEvent_t t0_ = timing_begin(stream);
-        const int e_ = gdn::launch_walk_fwd(ap[i], write_o, full, stream);
-        timing_end(walk_name, t0_, stream);
-        if (e_ != 0) rc = fail(GDN_EHIP, "%s: %s", walk_name, hipGetErrorString((hipError_t)e_));
-      }
+        return fail(GDN_EHIP, "piece event wait failed");
+      LAUNCH(walk_name, gdn::launch_walk_fwd(ap[i], write_o, tape, full, stream));
     }
-    for (hipEvent_t e : ready)
-      if (e) hipEventDestroy(e);
-    if (rc != GDN_OK) return rc;
-    CHECK(stream_wait(side, (hipStream_t)stream));
+    CHECK(ev.order(side, (hipStream_t)stream));
   }
   if (full) LAUNCH("gdn_wy_full", gdn::launch_wy_full(a, stream));
-  const uint64_t h = problem_hash(p);
-  const uint64_t words[4] = {kMagic, (uint64_t)GDN_ABI_VERSION, (uint64_t)p->save_mode, h};
-  LAUNCH("gdn_write_tag", gdn::launch_write_tag(saved, words, stream));
-  {
-    std::lock_guard<std::mutex> lk(g_reg_mu);
-    g_registry[saved] = h;
-  }
+  uint64_t words[4];
+  tag_words(p, words);
+  LAUNCH("gdn_write_tag", gdn::launch_write_tag(saved, words, a.status, stream));
+  if (write_o) LAUNCH("gdn_poison", gdn::launch_poison(a, GDN_OP_FWD, stream));
   g_err.clear();
   return GDN_OK;
 }
@@ -493,7 +504,7 @@ extern "C" {
 size_t gdn_saved_bytes(const gdn_problem* p) {
   Sizes s;
   if (check_problem(p, &s) != GDN_OK) return 0;
-  return saved_layout(s, p->save_mode == GDN_SAVE_FULL).total;
+  return saved_layout(s, p->save_mode).total;
 }
 
 size_t gdn_workspace_bytes(const gdn_problem* p, int op) {
@@ -503,7 +514,7 @@ size_t gdn_workspace_bytes(const gdn_problem* p, int op) {
     fail(GDN_EINVAL, "unknown op %d", op);
     return 0;
   }
-  return work_layout(s, op, p->save_mode == GDN_SAVE_FULL, p->deterministic).total;
+  return work_layout(s, op, p->save_mode, p->deterministic).total;
 }
 
 int gdn_fwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -537,19 +548,11 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   CHECK(check_tok(dbeta, "dbeta", s.T));
   if (p->has_h0) CHECK(check_ptr(dh0, "dh0"));
   CHECK(check_ptr(workspace, "workspace"));
-  {
-    std::lock_guard<std::mutex> lk(g_reg_mu);
-    auto it = g_registry.find(saved);
-    if (it == g_registry.end())
-      return fail(GDN_ESAVED, "saved buffer was not written by gdn_fwd/gdn_fwd_recompute in this process");
-    if (it->second != problem_hash(p))
-      return fail(GDN_ESAVED, "saved buffer was written for a different problem or save_mode");
-  }
-  const int full = p->save_mode == GDN_SAVE_FULL;
-  const WorkLayout W = work_layout(s, GDN_OP_BWD, full, p->deterministic);
+  const bool tape = keeps_tape(p->save_mode);
+  const WorkLayout W = work_layout(s, GDN_OP_BWD, p->save_mode, p->deterministic);
   if (workspace_bytes < W.total)
     return fail(GDN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
-  const SavedLayout L = saved_layout(s, full);
+  const SavedLayout L = saved_layout(s, p->save_mode);
   gdn::Args a;
   fill_common(a, s, p);
   a.q = q;
@@ -569,16 +572,20 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   a.dh0 = p->has_h0 ? dh0 : nullptr;
   bind_workspace(a, W, workspace);
   bind_saved(a, L, const_cast<void*>(saved));
-  if (!full) a.htape = (uint16_t*)((char*)workspace + W.htape);
 
   const Split sp = plan_split(p, s);
-  hipStream_t side = sp.on ? side_stream() : nullptr;
+  hipStream_t side = sp.on ? aux_of(p, stream) : nullptr;
+  CallEvents ev;
   if (side) a.grp_split = a.H;
-  LAUNCH("gdn_tables", gdn::launch_tables(a, stream));
+  // the first kernel compares the saved set's tag with this problem's; on a mismatch it sets the
+  // status word, every later kernel skips its work and the last one fills the gradients with NaN
+  uint64_t words[4];
+  tag_words(p, words);
+  LAUNCH("gdn_tables", gdn::launch_tables(a, (const uint64_t*)saved, words, stream));
   // light: the state tape is replayed; the tape walk and the reverse walk are independent and
-  // share one launch. full: the tape is in the saved set.
+  // share one launch. full / kept tape: the tape is in the saved set.
   auto walks = [&](const gdn::Args& x, hipStream_t st) -> int {
-    if (!full) LAUNCH_ON(st, "gdn_walk_pair", gdn::launch_walk_pair(x, st));
+    if (!tape) LAUNCH_ON(st, "gdn_walk_pair", gdn::launch_walk_pair(x, st));
     else LAUNCH_ON(st, "gdn_walk_bwd", gdn::launch_walk_bwd(x, st));
     return GDN_OK;
   };
@@ -590,11 +597,11 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
     range_a(aa, sp);
     range_b(ab, sp);
     LAUNCH("gdn_intra_bwd", gdn::launch_intra(aa, 1, stream));
-    CHECK(stream_wait((hipStream_t)stream, side));
+    CHECK(ev.order((hipStream_t)stream, side));
     CHECK(walks(aa, (hipStream_t)stream));
     LAUNCH_ON(side, "gdn_intra_bwd", gdn::launch_intra(ab, 1, side));
     CHECK(walks(ab, side));
-    CHECK(stream_wait(side, (hipStream_t)stream));
+    CHECK(ev.order(side, (hipStream_t)stream));
   }
   if (!p->deterministic) {
     LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
@@ -602,11 +609,54 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   }
   LAUNCH("gdn_chunk_grad", gdn::launch_chunk_grad(a, p->deterministic, stream));
   if (!p->deterministic) LAUNCH("gdn_finalize_qk", gdn::launch_finalize_qk(a, stream));
+  LAUNCH("gdn_poison", gdn::launch_poison(a, GDN_OP_BWD, stream));
   g_err.clear();
   return GDN_OK;
 }
 
+int gdn_status(const gdn_problem* p, int op, const void* workspace, void* stream) {
+  Sizes s;
+  CHECK(check_problem(p, &s));
+  if (op != GDN_OP_FWD && op != GDN_OP_RECOMPUTE && op != GDN_OP_BWD) return fail(GDN_EINVAL, "unknown op %d", op);
+  CHECK(check_ptr(workspace, "workspace"));
+  const WorkLayout W = work_layout(s, op, p->save_mode, p->deterministic);
+  int32_t st = 0;
+  hipError_t r = hipMemcpyAsync(&st, (const char*)workspace + W.status, sizeof st, hipMemcpyDeviceToHost,
+                                (hipStream_t)stream);
+  if (r == hipSuccess) r = hipStreamSynchronize((hipStream_t)stream);
+  if (r != hipSuccess) return fail(GDN_EHIP, "status copy: %s", hipGetErrorString(r));
+  if (st == 0) {
+    g_err.clear();
+    return GDN_OK;
+  }
+  if (st == 2) return fail(GDN_ESAVED, "the saved buffer's tag does not name this problem, save mode and ABI version");
+  return fail(GDN_EINVAL, "the device cu_seqlens disagree with the host copy in the problem");
+}
+
 void gdn_timing_enable(int on) { g_timing_on.store(on ? 1 : 0); }
+
+int gdn_timing_launches(int max, const char** names, double* start_ms, double* end_ms) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  const int n = (int)g_pending.size();
+  if (n == 0) return 0;
+  std::vector<double> st(n, 0.0), en(n, 0.0);
+  double lo = 0.0;
+  for (int i = 0; i < n; ++i) {
+    float a = 0.f, b = 0.f;
+    hipEventSynchronize(g_pending[i].stop);
+    hipEventElapsedTime(&a, g_pending[0].start, g_pending[i].start);
+    hipEventElapsedTime(&b, g_pending[0].start, g_pending[i].stop);
+    st[i] = a;
+    en[i] = b;
+    lo = std::min(lo, st[i]);
+  }
+  for (int i = 0; i < n && i < max; ++i) {
+    if (names) names[i] = g_pending[i].name;
+    if (start_ms) start_ms[i] = st[i] - lo;
+    if (end_ms) end_ms[i] = en[i] - lo;
+  }
+  return n;
+}
 
 int gdn_timing_collect(int max, const char** names, double* total_ms, int* launches) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
@@ -650,3 +700,21 @@ const char* gdn_last_error(void) { return g_err.c_str(); }
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
 } // extern "C"
+
+namespace gdn {
+
+// Forward with a caller-chosen workspace and no auxiliary stream (the entry point that allocates
+// nothing runs every launch on the caller's stream, so it records no events).
+int gdn_fwd_single_stream(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
+                          void* saved, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p) return fail(GDN_EINVAL, "problem descriptor is NULL");
+  gdn_problem pc = *p;
+  pc.aux_stream = nullptr;
+  return forward_common(&pc, q, k, v, g, beta, cu_seqlens, h0, o, ht, saved, workspace, workspace_bytes, stream,
+                        true);
+}
+
+int gdn_set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+} // namespace gdn

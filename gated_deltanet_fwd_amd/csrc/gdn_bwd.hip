@@ -26,17 +26,55 @@ static inline hipStream_t S_(void* s) { return reinterpret_cast<hipStream_t>(s);
 // ---------------------------------------------------------------------------------------
 // utilities
 
-__global__ void k_write_tag(uint64_t* dst, uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3) {
+// The saved set's tag; zeros when the call failed on the device (status nonzero), so that a
+// backward refuses the buffer.
+__global__ void k_write_tag(uint64_t* dst, const int* status, uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3) {
   if (threadIdx.x == 0) {
-    dst[0] = w0;
-    dst[1] = w1;
-    dst[2] = w2;
-    dst[3] = w3;
+    const bool ok = status[0] == 0;
+    dst[0] = ok ? w0 : 0;
+    dst[1] = ok ? w1 : 0;
+    dst[2] = ok ? w2 : 0;
+    dst[3] = ok ? w3 : 0;
   }
 }
 
-int launch_write_tag(void* dst, const uint64_t* w, void* stream) {
-  hipLaunchKernelGGL(k_write_tag, dim3(1), dim3(64), 0, S_(stream), (uint64_t*)dst, w[0], w[1], w[2], w[3]);
+int launch_write_tag(void* dst, const uint64_t* w, const int* status, void* stream) {
+  hipLaunchKernelGGL(k_write_tag, dim3(1), dim3(64), 0, S_(stream), (uint64_t*)dst, status, w[0], w[1], w[2],
+                     w[3]);
+  return (int)hipGetLastError();
+}
+
+// After a call whose status is nonzero (every kernel skipped its work): its floating-point
+// outputs are filled with NaN, so that no stale buffer content passes for a result.
+template <typename TI>
+__device__ void nan_fill(void* p, size_t n) {
+  if (!p) return;
+  const TI nanv = (TI)__builtin_nanf("");
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    ((TI*)p)[i] = nanv;
+}
+
+template <typename TI>
+__global__ __launch_bounds__(NTHREADS) void k_poison(Args a, int bwd) {
+  if (a.status[0] == 0) return;
+  const size_t T = (size_t)a.T, d = (size_t)a.D, states = (size_t)a.N * a.HV * d * d;
+  if (!bwd) {
+    nan_fill<TI>(a.o, T * a.HV * d);
+    if (a.want_ht) nan_fill<float>(a.ht, states);
+    return;
+  }
+  nan_fill<TI>(a.dq, T * a.H * d);
+  nan_fill<TI>(a.dk, T * a.H * d);
+  nan_fill<TI>(a.dv, T * a.HV * d);
+  nan_fill<float>(a.dg, T * a.HV);
+  nan_fill<float>(a.dbeta, T * a.HV);
+  nan_fill<float>(a.dh0, states);
+}
+
+int launch_poison(const Args& a, int op, void* stream) {
+  const int bwd = op == 2; // GDN_OP_BWD
+  if (a.dtype == 0) hipLaunchKernelGGL(k_poison<bf16>, dim3(512), dim3(NTHREADS), 0, S_(stream), a, bwd);
+  else hipLaunchKernelGGL(k_poison<float>, dim3(512), dim3(NTHREADS), 0, S_(stream), a, bwd);
   return (int)hipGetLastError();
 }
 
@@ -811,19 +849,22 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
 template <int D, typename TI>
 static int chunk_grad_t(const Args& a, int det, hipStream_t s) {
   if (a.c_count == 0) return 0;
-  // one persistent workgroup per resident slot (CUs x workgroups per CU, found once per process)
-  static std::atomic<int> slots[2]{{0}, {0}};
-  int n = slots[det].load(std::memory_order_relaxed);
+  // One persistent workgroup per resident slot (CUs x workgroups per CU), found once per kernel
+  // instance (this template's D and io type, the reduction mode) and device.
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> slots[2][kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return (int)hipErrorInvalidDevice;
+  int n = dev < kMaxDev ? slots[det][dev].load(std::memory_order_relaxed) : 0;
   if (n == 0) {
-    int dev = 0, ncu = 0, per = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    int ncu = 0, per = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return (int)hipErrorInvalidDevice;
     const hipError_t e = det ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_chunk_grad<D, TI, true>, GRAD_THREADS, 0)
                              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_chunk_grad<D, TI, false>, GRAD_THREADS, 0);
     if (e != hipSuccess) return (int)e;
     n = ncu * (per > 0 ? per : 1);
-    slots[det].store(n, std::memory_order_relaxed);
+    if (dev < kMaxDev) slots[det][dev].store(n, std::memory_order_relaxed);
   }
   const long items = (long)a.c_count * (det ? a.H : a.HV);
   const dim3 grid((unsigned)(items < n ? items : n));

@@ -18,17 +18,21 @@ namespace gdn {
 
 // ---------------------------------------------------------------------------------------
 // Chunk tables from the device copy of cu_seqlens (one workgroup of 1024 threads).
+// A backward call also compares the saved set's tag (tag[0..3]) with the words of its own problem
+// (w0..w3); on a mismatch the status is 2 and every later kernel of the call skips its work.
 __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu, int N, int H, int NT, int64_t T,
                                                  int* __restrict__ seq_c0, int* __restrict__ c_t0,
                                                  int* __restrict__ c_len, int* __restrict__ seq_order,
                                                  int* __restrict__ pair_order, int* __restrict__ status,
-                                                 int grp_split) {
+                                                 int grp_split, const uint64_t* __restrict__ tag, uint64_t w0,
+                                                 uint64_t w1, uint64_t w2, uint64_t w3) {
   __shared__ int s_scan[1024];
-  __shared__ int s_carry, s_bad;
+  __shared__ int s_carry, s_bad, s_tag_bad;
   const int tid = threadIdx.x;
   if (tid == 0) {
     s_carry = 0;
     s_bad = 0;
+    s_tag_bad = tag && (tag[0] != w0 || tag[1] != w1 || tag[2] != w2 || tag[3] != w3);
   }
   __syncthreads();
   for (int base = 0; base < N; base += 1024) {
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(1024) void k_tables(const int32_t* __restrict__ cu,
   if (tid == 0) {
     if (cu[0] != 0 || (int64_t)cu[N] != T || s_carry != NT) s_bad = 1;
     seq_c0[N] = s_carry;
-    status[0] = s_bad;
+    status[0] = s_bad ? 1 : s_tag_bad ? 2 : 0;
   }
   __syncthreads();
   const int bad = s_bad;
@@ -417,9 +421,11 @@ __global__ __launch_bounds__(walk_threads<D>(), 1) void k_walk_fwd(Args a) {
 
 static inline hipStream_t S_(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-int launch_tables(const Args& a, void* stream) {
+int launch_tables(const Args& a, const uint64_t* tag, const uint64_t* w, void* stream) {
+  const uint64_t z[4] = {0, 0, 0, 0};
+  if (!w) w = z;
   hipLaunchKernelGGL(k_tables, dim3(1), dim3(1024), 0, S_(stream), a.cu, a.N, a.H, a.NT, a.T, a.seq_c0, a.c_t0,
-                     a.c_len, a.seq_order, a.pair_order, a.status, a.grp_split);
+                     a.c_len, a.seq_order, a.pair_order, a.status, a.grp_split, tag, w[0], w[1], w[2], w[3]);
   return (int)hipGetLastError();
 }
 
@@ -458,20 +464,25 @@ void whole_range(Args& a) {
 }
 
 template <int D, typename TI>
-static int walk_t(const Args& a, int write_o, int write_tape, hipStream_t s) {
+static int walk_t(const Args& a, int write_o, int write_tape, int write_vnew, hipStream_t s) {
   const dim3 grid(chain_blocks(a, 1)), blk(walk_threads<D>());
+  if (!write_tape) write_vnew = 0;
   if (write_o && !write_tape) hipLaunchKernelGGL((k_walk_fwd<D, TI, true, false, false>), grid, blk, 0, s, a);
-  else if (write_o) hipLaunchKernelGGL((k_walk_fwd<D, TI, true, true, true>), grid, blk, 0, s, a);
-  else if (a.full) hipLaunchKernelGGL((k_walk_fwd<D, TI, false, true, true>), grid, blk, 0, s, a);
-  else hipLaunchKernelGGL((k_walk_fwd<D, TI, false, true, false>), grid, blk, 0, s, a);
+  else if (write_o && write_vnew) hipLaunchKernelGGL((k_walk_fwd<D, TI, true, true, true>), grid, blk, 0, s, a);
+  else if (write_o) hipLaunchKernelGGL((k_walk_fwd<D, TI, true, true, false>), grid, blk, 0, s, a);
+  else if (write_vnew) hipLaunchKernelGGL((k_walk_fwd<D, TI, false, true, true>), grid, blk, 0, s, a);
+  else if (write_tape) hipLaunchKernelGGL((k_walk_fwd<D, TI, false, true, false>), grid, blk, 0, s, a);
+  else return (int)hipErrorInvalidValue; // a walk that writes nothing
   return (int)hipGetLastError();
 }
 
-int launch_walk_fwd(const Args& a, int write_o, int write_tape, void* stream) {
+int launch_walk_fwd(const Args& a, int write_o, int write_tape, int write_vnew, void* stream) {
   const hipStream_t s = S_(stream);
   if (a.D == 128)
-    return a.dtype == 0 ? walk_t<128, bf16>(a, write_o, write_tape, s) : walk_t<128, float>(a, write_o, write_tape, s);
-  return a.dtype == 0 ? walk_t<64, bf16>(a, write_o, write_tape, s) : walk_t<64, float>(a, write_o, write_tape, s);
+    return a.dtype == 0 ? walk_t<128, bf16>(a, write_o, write_tape, write_vnew, s)
+                        : walk_t<128, float>(a, write_o, write_tape, write_vnew, s);
+  return a.dtype == 0 ? walk_t<64, bf16>(a, write_o, write_tape, write_vnew, s)
+                      : walk_t<64, float>(a, write_o, write_tape, write_vnew, s);
 }
 
 } // namespace gdn

@@ -46,7 +46,8 @@ struct Args {
   int* c_t0;       // [NT] first token of each chunk
   int* c_len;      // [NT] valid tokens of each chunk (1..64)
   int* seq_order;  // [N] documents, longest first
-  int* status;     // [1] nonzero if the device tables disagree with the host's chunk count
+  int* status;     // [1] 0 ok; 1 the device tables disagree with the host's chunk count;
+                   // 2 (backward) the saved set's tag does not name this problem
   float* rk;       // [H, T] inverse L2 norms of k rows (1 when the norm is off), head-major
   float* rq;       // [H, T] inverse L2 norms of q rows, head-major
   uint16_t* qk;    // bf16 [NT, HV, 64, 64] P = exp(G_q - G_k) qh.kh masked to q >= k, per value head
@@ -81,14 +82,22 @@ int chain_blocks(const Args& a, int ntile);
 void whole_range(Args& a);
 
 // Launchers (defined in the .hip translation units). Each returns a hipError_t as int.
-int launch_tables(const Args& a, void* stream);
+// tag / tag_words: the saved set's 256-byte tag and the four words it must hold (backward calls
+// only; NULL otherwise). A mismatch sets status 2, a cu_seqlens disagreement status 1.
+int launch_tables(const Args& a, const uint64_t* tag, const uint64_t* tag_words, void* stream);
 int launch_intra(const Args& a, int bwd_prep, void* stream);
-int launch_walk_fwd(const Args& a, int write_o, int write_tape, void* stream);
+// write_tape: the chunk-start state tape; write_vnew: v_new (the full saved set)
+int launch_walk_fwd(const Args& a, int write_o, int write_tape, int write_vnew, void* stream);
 int launch_walk_pair(const Args& a, void* stream); // tape walk and reverse walk in one launch
 int launch_wy_full(const Args& a, void* stream);
 int launch_walk_bwd(const Args& a, void* stream);
 int launch_chunk_grad(const Args& a, int deterministic, void* stream);
 int launch_fill_zero(float* p, size_t n, void* stream);
 int launch_finalize_qk(const Args& a, void* stream);
+// The saved set's tag (zeros when the call's status is nonzero, so that it is refused later).
+int launch_write_tag(void* dst, const uint64_t* words, const int* status, void* stream);
+// When the call's status is nonzero: its floating-point outputs (op GDN_OP_FWD: o, ht;
+// GDN_OP_BWD: dq, dk, dv, dg, dbeta, dh0) are filled with NaN. Otherwise it does nothing.
+int launch_poison(const Args& a, int op, void* stream);
 
 } // namespace gdn

@@ -25,23 +25,27 @@
  *   h0, ht      [N, HV, d, d] f32 (key index, value index); dht, dh0 the same
  *   cu_seqlens  [N + 1]      int32, cu_seqlens[0] = 0, nondecreasing, cu_seqlens[N] = T
  *
- * Ownership: the caller allocates every buffer (outputs, the saved set, the workspace). The
- * library never allocates or frees device memory and never synchronises the host. Work is
- * enqueued on the stream it is given (a hipStream_t; NULL = the default stream): all of it runs
- * after the work enqueued there before the call and before the work enqueued there after it.
- * When one document is much longer than the others, gdn_fwd, gdn_fwd_recompute (full mode) and
- * gdn_bwd fork part of their launches onto a second stream the library creates once per device
- * (default priority, kept until the process ends) and join it back with events, so this
- * ordering holds as for one stream. Inputs are not modified. Calls are reentrant; calls that
- * share a workspace or saved buffer must not overlap.
+ * Ownership: the caller allocates every buffer (outputs, the saved set, the workspace) and
+ * owns every stream. The library never allocates or frees device memory, never creates a
+ * stream and never synchronises the host (gdn_status, a query, is the one call that waits).
+ * Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and, when the
+ * problem names one, on the caller's auxiliary stream problem->aux_stream: all of it runs
+ * after the work enqueued on `stream` before the call and before the work enqueued there
+ * after it (the auxiliary stream is forked from and joined back into `stream` with events).
+ * With aux_stream = NULL every launch goes to `stream`. Inputs are not modified. Calls are
+ * reentrant; calls that share a workspace or a saved buffer must not overlap. Concurrent calls
+ * may name the same auxiliary stream: their auxiliary work then runs there one call after the
+ * other.
  *
  * Errors: every entry returns GDN_OK or an error code; gdn_last_error() gives a message for
- * the calling thread. All validation (shapes, cu_seqlens, sizes, pointers, alignment, the
- * saved-set tag) happens on the host before the first launch, so a rejected call writes
- * nothing. A launch failure returns GDN_EHIP. Faults inside kernels surface at the caller's
- * next synchronisation. The device copy of cu_seqlens must equal the host copy given in the
- * problem; if the device tables built from it disagree with the host's chunk count, every
- * kernel of the call skips all work (outputs are left unwritten) rather than read out of range.
+ * the calling thread. Host validation (shapes, cu_seqlens, sizes, pointers, alignment) runs
+ * before the first launch, so a call it rejects writes nothing. A launch failure returns
+ * GDN_EHIP. Two conditions can only be seen on the device, by the first kernel of a call:
+ * a device cu_seqlens that disagrees with the host copy in the problem, and (gdn_bwd) a saved
+ * buffer whose 256-byte tag does not name this problem, save mode and ABI version. Then every
+ * kernel of the call skips its work, the call's floating-point outputs are filled with NaN,
+ * and gdn_status() reports GDN_EINVAL or GDN_ESAVED. Faults inside kernels surface at the
+ * caller's next synchronisation.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -53,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 /* return codes */
 #define GDN_OK 0
@@ -67,16 +71,21 @@ extern "C" {
 #define GDN_DTYPE_BF16 0
 #define GDN_DTYPE_F32 1
 
-/* saved-set forms (README saved-set table quoted in flashinfer PR #8542):
+/* Saved-set forms (README saved-set table quoted in the review of flashinfer PR #8542; the
+ * kept-tape form follows the `reuse_recompute_tapes` row of the option table quoted in the
+ * review of flashinfer PR #8172).
  * LIGHT keeps Akk (the inverse of I + L per chunk, bf16 [T, HV, 64]), gcum (f32 [HV, T]) and
  * gamma (f32 [NT, HV]); the backward replays the state tape. FULL also keeps the state tape
  * (bf16 [NT, HV, d, d]), v_new (bf16 [T, HV, d]), w and u (bf16 [T, HV, d]) and Aqk
- * (bf16 [T, HV, 64]); the backward then skips the replay walk. Both forms give bitwise
- * identical gradients. */
+ * (bf16 [T, HV, 64]). TAPE keeps LIGHT plus the state tape only: a checkpointed step runs
+ * gdn_fwd in LIGHT form, then gdn_fwd_recompute and gdn_bwd in TAPE form, so the backward binds
+ * the tape that the recompute's walk wrote instead of replaying it. FULL and TAPE backwards
+ * skip the replay walk. All forms give bitwise identical outputs and gradients. */
 #define GDN_SAVE_LIGHT 0
 #define GDN_SAVE_FULL 1
+#define GDN_SAVE_TAPE 2
 
-/* operations, for gdn_workspace_bytes */
+/* operations, for gdn_workspace_bytes and gdn_status */
 #define GDN_OP_FWD 0
 #define GDN_OP_RECOMPUTE 1
 #define GDN_OP_BWD 2
@@ -91,40 +100,67 @@ typedef struct gdn_problem {
   int32_t l2norm_qk;              /* 1: L2-normalise q and k rows inside the kernel */
   int32_t has_h0;                 /* 1: h0 is given (and gdn_bwd writes dh0) */
   int32_t want_ht;                /* 1: gdn_fwd writes ht */
-  int32_t save_mode;              /* GDN_SAVE_LIGHT or GDN_SAVE_FULL */
+  int32_t save_mode;              /* GDN_SAVE_LIGHT, GDN_SAVE_FULL or GDN_SAVE_TAPE */
   int32_t deterministic;          /* 1: fixed-order dq/dk reduction over the HV/H value heads
                                      of each q/k head (bitwise reproducible); 0: FP32 atomics */
   const int32_t* cu_seqlens_host; /* host copy of cu_seqlens, read during each call only */
+  void* aux_stream;               /* optional second stream (hipStream_t) of the caller on the
+                                     device of `stream`; NULL: every launch on `stream` */
+  int32_t segments;               /* walk segments per document (the PR #8172 README option
+                                     table's `segments` / `walk_seg`): 0 or 1 = each document's
+                                     state walk is one serial chain; P >= 2 = documents long
+                                     enough are walked as up to P segments (transfer walks,
+                                     a carry merge, then the segments' walks side by side) */
+  int32_t reserved0;              /* must be 0 */
 } gdn_problem;
 
-/* Bytes of the saved buffer for this problem and save_mode (a 256-byte tag plus the saved
- * tensors, each 256-byte aligned). 0 if the problem is invalid (see gdn_last_error). */
+/* Bytes of the saved buffer for this problem and save_mode: a 256-byte tag plus the saved
+ * tensors, each 256-byte aligned (per-token figures of the README saved-set table quoted in
+ * the review of flashinfer PR #8542: light 6,339 B/token and full +67,584 B/token at
+ * HV = 48, d = 128, all chunks full). 0 if the problem is invalid (see gdn_last_error). */
 size_t gdn_saved_bytes(const gdn_problem* p);
 
-/* Bytes of device workspace one call of `op` needs (chunk tables, norms, q.k products, tapes,
- * FP32 accumulators). 0 if the problem is invalid. */
+/* Bytes of device workspace one call of `op` needs: chunk tables, inverse q/k norms, the
+ * per-value-head decayed q.k tiles, the replayed state tape and the end-state-gradient tape
+ * (backward), FP32 dq/dk accumulators (atomic reduction), the segment carry states. The
+ * pages' byte queries (flashinfer PR #8172 description: saved, workspace and communication
+ * byte-accounting APIs) are the model. 0 if the problem is invalid. */
 size_t gdn_workspace_bytes(const gdn_problem* p, int op);
 
-/* Forward. Writes o, ht (if want_ht) and the saved set. h0 may be NULL iff has_h0 = 0; ht may
- * be NULL iff want_ht = 0. */
+/* Forward (flashinfer PR #8172 description: the chunked training kernel's forward call; the
+ * chunk programs it runs are those the commit messages of flashinfer PR #7097 name: prep,
+ * intra, WY and the state walk). Writes o [T, HV, d], ht [N, HV, d, d] (if want_ht) and the
+ * saved set. h0 may be NULL iff has_h0 = 0; ht may be NULL iff want_ht = 0. */
 int gdn_fwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
             const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
             void* saved, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Checkpoint re-run of the forward: writes the saved set only (no o, no ht), bitwise equal to
- * the saved set gdn_fwd writes for the same inputs (activation checkpointing = forward,
- * recompute, backward). */
+/* Checkpoint re-run of the forward (flashinfer PR #8172 description: the checkpointed call;
+ * README option table: `recompute_output`, the re-run that launches no output program).
+ * Writes the saved set only (no o, no ht), bitwise equal to the saved set gdn_fwd writes for
+ * the same inputs and save_mode. */
 int gdn_fwd_recompute(const gdn_problem* p, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const int32_t* cu_seqlens,
                       const float* h0, void* saved, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* Backward. Reads the saved set of the matching forward, dO and optional dht (NULL = 0), and
- * writes dq, dk, dv, dg, dbeta and (if has_h0) dh0. */
+/* Backward (flashinfer PR #8172 description: the backward call, with its gradient-state
+ * traversal and gradient programs; the deterministic and float-atomic dq/dk reductions are
+ * the pages' deterministic and non-deterministic packages). Reads the saved set of the
+ * matching forward or recompute (same problem and save_mode), dO and optional dht (NULL = 0),
+ * and writes dq, dk, dv, dg, dbeta and (if has_h0) dh0. */
 int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
             const float* beta, const int32_t* cu_seqlens, const float* h0, const void* saved,
             const void* dO, const float* dht, void* dq, void* dk, void* dv, float* dg,
             float* dbeta, float* dh0, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device-side status of the last call of `op` that used this workspace (the refusals of
+ * flashinfer PR #8542's description: a saved set that does not match is refused). Enqueues a
+ * copy of the status word on `stream` and waits for `stream`: this query synchronises the
+ * host. Returns GDN_OK, GDN_EINVAL (the device cu_seqlens disagreed with the host copy) or
+ * GDN_ESAVED (gdn_bwd was given a saved buffer whose tag does not name this problem, save
+ * mode and ABI version); a copy failure returns GDN_EHIP. */
+int gdn_status(const gdn_problem* p, int op, const void* workspace, void* stream);
 
 /* Message of the calling thread's last error ("" if none). */
 const char* gdn_last_error(void);
@@ -133,13 +169,17 @@ const char* gdn_last_error(void);
 int gdn_abi_version(void);
 
 /* Kernel timing, for benchmarks. While enabled (on = 1), every kernel launch of the library is
- * bracketed by two hipEvents recorded on the call's stream (no synchronisation at launch).
- * gdn_timing_collect waits for all recorded events, adds their elapsed times to per-kernel
- * totals and returns the number of distinct kernels; for the first `max` (in name order) it
- * fills names (valid until the next collect on this thread), total_ms and launch counts (any
- * array may be NULL). gdn_timing_reset drops totals and pending events. */
+ * bracketed by two hipEvents recorded on the stream it is launched on (no synchronisation at
+ * launch). gdn_timing_collect waits for all recorded events, adds their elapsed times to
+ * per-kernel totals and returns the number of distinct kernels; for the first `max` (in name
+ * order) it fills names (valid until the next collect on this thread), total_ms and launch
+ * counts (any array may be NULL). gdn_timing_launches (call it before gdn_timing_collect, which
+ * drops the pending events) waits for them as well and fills, for up to `max` launches in
+ * launch order, the kernel name and the start and end times in ms after the earliest start;
+ * it returns the number of pending launches. gdn_timing_reset drops totals and pending events. */
 void gdn_timing_enable(int on);
 int gdn_timing_collect(int max, const char** names, double* total_ms, int* launches);
+int gdn_timing_launches(int max, const char** names, double* start_ms, double* end_ms);
 void gdn_timing_reset(void);
 
 #ifdef __cplusplus

@@ -18,12 +18,15 @@ def test_step_roofline_bytes_and_flops():
     fwd = inputs + HV * d * io + light                          # + o, saved set written
     bwd = inputs + HV * d * io + light + 2 * H * d * io + HV * d * io + 2 * HV * 4  # dO, saved read; dq, dk, dv, dg, dbeta
     rec = H * d * io + 2 * HV * 4 + light                       # k, g, beta read; saved written
-    for full, extra in ((False, 0), (True, full_extra)):
-        m = bench.step_roofline(T, HV, d, io, full=full)
+    tape_extra = HV * d * d * 2 // C                            # the kept-tape form's state per chunk
+    # the full and kept-tape recomputes walk the states (v read); the full one also forms the q.k rows (q read)
+    for mode, extra, rec_extra in (("light", 0, 0), ("full", full_extra, HV * d * io + H * d * io),
+                                   ("tape", tape_extra, HV * d * io)):
+        m = bench.step_roofline(T, HV, d, io, H=H, save_mode=mode)
         assert abs(m["fwd"]["bytes_per_token"] - (fwd + extra)) < 1e-6
         assert abs(m["fwdbwd"]["bytes_per_token"] - (fwd + bwd + 2 * extra)) < 1e-6
-        assert abs(m["ckpt"]["bytes_per_token"] - (fwd + rec + bwd + 3 * extra)) < 1e-6
-    m = bench.step_roofline(T, HV, d, io)
+        assert abs(m["ckpt"]["bytes_per_token"] - (fwd + rec + rec_extra + bwd + 3 * extra)) < 1e-6
+    m = bench.step_roofline(T, HV, d, io, H=H)
     assert round(m["fwd"]["bytes_per_token"]) == 39491
     assert round(m["fwdbwd"]["bytes_per_token"]) == 99846
     # MFMA work per v head and token: fwd 6d^2 + 6Cd + 4Cd/G + 2C^2/3, bwd 16d^2 + (12 + 2/G) 2Cd + 4C^2/3
@@ -35,3 +38,25 @@ def test_step_roofline_bytes_and_flops():
     assert round(f_fwd) == 161109 and round(f_bwd) == 475136
     # fwd + bwd at the packed workload: HBM and MFMA terms within a few percent, 3.27 ms
     assert abs(m["fwdbwd"]["roofline_s"] - 3.2718e-3) < 2e-6
+
+
+def test_kernel_models_count_no_intermediates_as_algorithmic():
+    """Per-kernel algorithmic bytes of the default step (light, deterministic) add up to the op's
+    compulsory tensors as each kernel reads or writes them, and contain no tape or q.k-tile bytes:
+    those are reported as intermediates."""
+    T, NT, N, H, HV, d, io = 262144, 4096, 4, 16, 48, 128, 2
+    m = bench.kernel_models(T, NT, N, H, HV, d, io)
+    tape = NT * HV * d * d * 2
+    pv = NT * HV * 64 * 64 * 2
+    qk, vv, akk, gb = T * H * d * io, T * HV * d * io, T * HV * 64 * 2, T * HV * 4
+    # the chunk-gradient kernel: reads q, k, v, dO, A, gcum, beta; writes dq, dk, dv, dg, dbeta
+    assert m["gdn_chunk_grad"][0] == 2 * qk + 2 * vv + akk + 2 * gb + 2 * qk + vv + 2 * gb
+    assert m["gdn_chunk_grad"][2] >= 2 * tape + pv
+    # the paired walks: q, k, v, dO, A, gcum, beta (k, v, A, gcum, beta once per walk kind)
+    assert m["gdn_walk_pair"][0] == (qk + vv + akk + 2 * gb) + (2 * qk + vv + akk + 2 * gb)
+    assert m["gdn_walk_pair"][2] >= 2 * tape + pv
+    # the forward walk: q, k, v, A, gcum, beta read and o written; the q.k tiles and norms are not algorithmic
+    assert m["gdn_walk_fwd"][0] == 2 * qk + vv + akk + 2 * gb + vv
+    # in the kept-tape form the chunk-gradient kernel's read of the state tape is a saved-set read
+    mt = bench.kernel_models(T, NT, N, H, HV, d, io, save_mode="tape")
+    assert mt["gdn_chunk_grad"][0] == m["gdn_chunk_grad"][0] + tape

@@ -23,8 +23,13 @@ def _dev(inp):
     return {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
 
 
-def _run(w, inp, save_mode=G.SAVE_LIGHT, det=None, bwd=True, recompute=False, poison=False, l2norm=None):
-    p = G.problem_for(w, save_mode=save_mode, deterministic=det, l2norm=l2norm)
+def _run(w, inp, save_mode=G.SAVE_LIGHT, det=None, bwd=True, recompute=False, poison=False, l2norm=None,
+         aux=True, recompute_mode=None, dht=True):
+    """fwd (save_mode), optionally recompute (recompute_mode, default save_mode) into a fresh saved
+    buffer, then bwd with the problem of the saved set it reads."""
+    p = G.problem_for(w, save_mode=save_mode, deterministic=det, l2norm=l2norm, use_aux_stream=aux)
+    pr = p if recompute_mode is None else G.problem_for(w, save_mode=recompute_mode, deterministic=det,
+                                                         l2norm=l2norm, use_aux_stream=aux)
     a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
     fill = float("nan") if poison else 0.0
     o = torch.full_like(inp["v"], fill)
@@ -33,30 +38,38 @@ def _run(w, inp, save_mode=G.SAVE_LIGHT, det=None, bwd=True, recompute=False, po
     ws = torch.full((G.gdn_workspace_bytes(p, G.OP_FWD),), 255 if poison else 0, dtype=torch.uint8, device=DEV)
     o, ht, saved = G.gdn_fwd(p, *a, h0=inp["h0"], o=o, ht=ht, saved=saved, workspace=ws)
     out = dict(o=o, ht=ht, saved=saved, p=p)
+    pb = p
     if recompute:
-        saved2 = torch.full_like(saved, 255 if poison else 0)
-        ws2 = torch.full((G.gdn_workspace_bytes(p, G.OP_RECOMPUTE),), 255 if poison else 0, dtype=torch.uint8,
+        saved2 = torch.full((G.gdn_saved_bytes(pr),), 255 if poison else 0, dtype=torch.uint8, device=DEV)
+        ws2 = torch.full((G.gdn_workspace_bytes(pr, G.OP_RECOMPUTE),), 255 if poison else 0, dtype=torch.uint8,
                          device=DEV)
-        G.gdn_fwd_recompute(p, *a, h0=inp["h0"], saved=saved2, workspace=ws2)
+        G.gdn_fwd_recompute(pr, *a, h0=inp["h0"], saved=saved2, workspace=ws2)
         out["saved_recompute"] = saved2
+        pb = pr
     if bwd:
         grads = dict(dq=torch.full_like(inp["q"], fill), dk=torch.full_like(inp["k"], fill),
                      dv=torch.full_like(inp["v"], fill), dg=torch.full_like(inp["g"], fill),
                      dbeta=torch.full_like(inp["beta"], fill),
                      dh0=torch.full_like(inp["h0"], fill) if inp["h0"] is not None else None)
-        wsb = torch.full((G.gdn_workspace_bytes(p, G.OP_BWD),), 255 if poison else 0, dtype=torch.uint8, device=DEV)
-        G.gdn_bwd(p, *a, out.get("saved_recompute", saved), inp["dO"], h0=inp["h0"], dht=inp["dht"], grads=grads,
-                  workspace=wsb)
+        wsb = torch.full((G.gdn_workspace_bytes(pb, G.OP_BWD),), 255 if poison else 0, dtype=torch.uint8,
+                         device=DEV)
+        G.gdn_bwd(pb, *a, out.get("saved_recompute", saved), inp["dO"], h0=inp["h0"],
+                  dht=inp["dht"] if dht else None, grads=grads, workspace=wsb)
         out.update(grads)
+        out["status"] = G.gdn_status(pb, G.OP_BWD, wsb)
     torch.cuda.synchronize()
     return out
 
 
-def _check_all(w, inp, out, docs=None, heads=None, bwd=True, l2norm=None):
+def _check_all(w, inp, out, docs=None, heads=None, bwd=True, l2norm=None, dht=True):
     """Compare o, ht and the gradients on the sampled documents x q/k heads."""
     l2 = w.l2norm if l2norm is None else l2norm
     Gg = w.HV // w.H
     h, ti, vh = host_inputs(inp, docs, heads, Gg)
+    if not dht:
+        h["dht"] = None
+    if bwd:
+        assert out.get("status", G.GDN_OK) == G.GDN_OK
     hq = list(range(w.H)) if heads is None else list(heads)
     dsel = list(range(w.N)) if docs is None else list(docs)
     o_ref, ht_ref = oracle_fwd(h, l2)
@@ -214,22 +227,23 @@ def test_split_walk_in_pieces():
 
 
 def test_concurrent_calls_on_two_streams_bitwise():
-    """Two host threads run fwd + bwd at once, each on its own stream, on a problem whose longest
-    document runs apart on the library's second stream (shared by both calls): each result equals
-    the sequential one bitwise."""
+    """Two host threads run fwd + bwd at once, each on its own stream and auxiliary stream, on a
+    problem whose longest document runs apart on the auxiliary stream: each result equals the
+    sequential one bitwise."""
     import threading
 
     w = [x for x in EDGE if x.name == "split_mid"][0]
     inp = _dev(syn.make_inputs(w))
     ref = _run(w, inp, det=True)
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    aux_streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = [None, None]
     errs = []
 
     def work(i):
         try:
             with torch.cuda.stream(streams[i]):
-                p = G.problem_for(w, deterministic=True)
+                p = G.problem_for(w, deterministic=True, use_aux_stream=aux_streams[i])
                 a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
                 o, ht, saved = G.gdn_fwd(p, *a, h0=inp["h0"], stream=streams[i])
                 gr = G.gdn_bwd(p, *a, saved, inp["dO"], h0=inp["h0"], dht=inp["dht"], stream=streams[i])
@@ -282,15 +296,108 @@ def test_atomic_close_to_deterministic():
         assert_close(k, b[k], a[k])
 
 
-def test_saved_set_refused_for_other_problem():
+def _bwd_with(p, inp, saved):
+    a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
+    ws = torch.zeros((G.gdn_workspace_bytes(p, G.OP_BWD),), dtype=torch.uint8, device=DEV)
+    gr = G.gdn_bwd(p, *a, saved, inp["dO"], h0=inp["h0"], dht=inp["dht"], workspace=ws)
+    st = G.gdn_status(p, G.OP_BWD, ws)
+    return gr, st
+
+
+def test_saved_tag_checked_on_device():
+    """The backward's first kernel compares the saved set's tag with its own problem: a saved set
+    written for another save mode, or a buffer whose address now holds other data, yields
+    GDN_ESAVED from gdn_status and all-NaN gradients; a copy of a valid saved set at another
+    address is accepted and gives the same bits."""
     w = EDGE[0]
     inp = _dev(syn.make_inputs(w))
-    a = _run(w, inp, bwd=False)
-    p2 = G.problem_for(w, save_mode=G.SAVE_FULL)
-    with pytest.raises(G.GdnError) as e:
-        G.gdn_bwd(p2, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"], a["saved"], inp["dO"],
-                  h0=inp["h0"], dht=inp["dht"])
-    assert e.value.code == G.GDN_ESAVED
+    ref = _run(w, inp, det=True)
+    assert ref["status"] == G.GDN_OK
+    # written for the light form, read as the full form
+    p_full = G.problem_for(w, save_mode=G.SAVE_FULL, deterministic=True)
+    gr, st = _bwd_with(p_full, inp, torch.zeros(G.gdn_saved_bytes(p_full), dtype=torch.uint8, device=DEV))
+    assert st == G.GDN_ESAVED
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.isnan(gr[k]).all(), k
+    # a valid saved set copied elsewhere (moved, offloaded and brought back) is accepted
+    p = G.problem_for(w, deterministic=True)
+    moved = ref["saved"].clone()
+    gr, st = _bwd_with(p, inp, moved)
+    assert st == G.GDN_OK
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(gr[k], ref[k]), k
+    # the original address now holds other data (as after the buffer was freed and reused)
+    ref["saved"].copy_(torch.randint(0, 256, ref["saved"].shape, dtype=torch.uint8, device=DEV))
+    gr, st = _bwd_with(p, inp, ref["saved"])
+    assert st == G.GDN_ESAVED
+    assert all(torch.isnan(gr[k]).all() for k in ("dq", "dk", "dv", "dg", "dbeta", "dh0"))
+    # a saved set of another problem (one token fewer in the last document)
+    w2 = syn.custom("edge_tails_short", list(w.lengths[:-1]) + [w.lengths[-1] - 1], w.H, w.HV, w.d, w.dtype,
+                    has_h0=True, want_ht=True, has_dht=True)
+    inp2 = _dev(syn.make_inputs(w2))
+    other = _run(w2, inp2, det=True, bwd=False)
+    gr, st = _bwd_with(p, inp, torch.cat([other["saved"], torch.zeros(ref["saved"].numel() - other["saved"].numel(),
+                                                                      dtype=torch.uint8, device=DEV)]))
+    assert st == G.GDN_ESAVED
+
+
+def test_device_cu_seqlens_mismatch_poisons_outputs():
+    """A device cu_seqlens that disagrees with the host copy: the tables kernel sees a different
+    chunk count, every kernel skips its work, the outputs are NaN and gdn_status reports it."""
+    w = EDGE[0]
+    inp = _dev(syn.make_inputs(w))
+    p = G.problem_for(w, deterministic=True)
+    bad_cu = inp["cu_seqlens"].clone()
+    bad_cu[1] = bad_cu[1] + 64  # one chunk more in the first document, one fewer later
+    a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], bad_cu)
+    ws = torch.zeros((G.gdn_workspace_bytes(p, G.OP_FWD),), dtype=torch.uint8, device=DEV)
+    o, ht, saved = G.gdn_fwd(p, *a, h0=inp["h0"], workspace=ws)
+    assert G.gdn_status(p, G.OP_FWD, ws) == G.GDN_EINVAL
+    assert torch.isnan(o).all() and torch.isnan(ht).all()
+    gr, st = _bwd_with(p, inp, saved)  # the failed forward wrote a zero tag
+    assert st == G.GDN_ESAVED
+
+
+@pytest.mark.parametrize("name", ["split_mid", "pieces"])
+def test_single_stream_bitwise(name):
+    """Without an auxiliary stream every launch goes to the caller's stream (no split of the launch
+    plan): outputs and gradients equal the two-stream run bitwise, in every saved-set form."""
+    if name == "pieces":
+        w = syn.custom("pieces", [3000, 49252, 700], 1, 2, 64, "bf16", has_h0=True, want_ht=True, has_dht=True,
+                       seed=14)
+    else:
+        w = [x for x in EDGE if x.name == name][0]
+    inp = _dev(syn.make_inputs(w))
+    for mode in (G.SAVE_LIGHT, G.SAVE_FULL):
+        a = _run(w, inp, save_mode=mode, det=True, aux=True)
+        b = _run(w, inp, save_mode=mode, det=True, aux=False)
+        assert torch.equal(a["saved"], b["saved"])
+        for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+            assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name", ["edge_tails", "split_mid"])
+def test_kept_tape_checkpoint_bitwise(name):
+    """Checkpointed step with kept tapes: fwd (light), recompute (kept-tape form) and bwd (kept-tape
+    form, no replay walk) give the gradients of the light fwd + bwd bitwise; fwd and bwd in the
+    kept-tape form as well."""
+    w = [x for x in EDGE if x.name == name][0]
+    inp = _dev(syn.make_inputs(w))
+    ref = _run(w, inp, det=True)
+    ck = _run(w, inp, det=True, recompute=True, recompute_mode=G.SAVE_TAPE)
+    kt = _run(w, inp, save_mode=G.SAVE_TAPE, det=True)
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(ck[k], ref[k]), k
+        assert torch.equal(kt[k], ref[k]), k
+    assert torch.equal(kt["o"], ref["o"]) and torch.equal(kt["ht"], ref["ht"])
+    # the kept-tape recompute writes the light set bitwise and the tape as the full forward does
+    full = _run(w, inp, save_mode=G.SAVE_FULL, det=True, bwd=False)
+    regions, _ = _saved_regions(w, True)
+    off, n = regions["H"]
+    end_light = regions["gamma"][0] + regions["gamma"][1]
+    sv = ck["saved_recompute"]
+    assert torch.equal(sv[256:end_light], ref["saved"][256:end_light])
+    assert torch.equal(sv[off:off + n], full["saved"][off:off + n])
 
 
 # ------------------------------------------------------------------------------------------
@@ -306,7 +413,7 @@ def _big(name):
 def test_single8k_fwd():
     w, inp = _big("single8k")
     out = _run(w, inp, bwd=False)
-    _check_all(w, inp, out, heads=[0, 15], bwd=False)
+    _check_all(w, inp, out, bwd=False)  # every head
 
 
 def test_pack262k_fwd_bwd_atomic():
@@ -351,10 +458,48 @@ def test_pack262k_longest_document_alone_bitwise():
             assert torch.equal(v, b[k][half]), k
 
 
-def test_cp4share_h0_ht_dh0():
+@pytest.mark.parametrize("dht", [True, False], ids=["dht", "no_dht"])
+def test_cp4share_h0_ht_dh0(dht):
+    """Both fragments of the share (the 40,960-token first one runs apart from the second, with h0),
+    with the final-state gradient given and absent."""
     w, inp = _big("cp4share")
-    out = _run(w, inp)
-    _check_all(w, inp, out, docs=[1], heads=[0, 9])
+    out = _run(w, inp, dht=dht)
+    _check_all(w, inp, out, docs=[0, 1], heads=[0, 9], dht=dht)
+
+
+def test_pack262k_ckpt_and_full_saved_set():
+    """The packed workload's checkpointed op (fwd, recompute, bwd) against the oracle on sampled
+    documents and heads, and its full saved set region by region against the chunked oracle on the
+    shortest document for one q/k head group."""
+    w, inp = _big("pack262k")
+    out = _run(w, inp, det=True, recompute=True)
+    assert torch.equal(out["saved"], out["saved_recompute"])
+    _check_all(w, inp, out, docs=[0, 3], heads=[7])
+    del out
+    torch.cuda.empty_cache()
+    full = _run(w, inp, save_mode=G.SAVE_FULL, det=True, bwd=False)
+    n, j = 3, 11
+    Gg = w.HV // w.H
+    h, ti, vh = host_inputs(inp, [n], [j], Gg)
+    ref = oracle.chunked_fwd(h["cu"], h["q"], h["k"], h["v"], h["g"], h["beta"], None, l2norm=True, chunk=64,
+                             full=True)
+    regions, NT = _saved_regions(w, True)
+    raw = full["saved"]
+    T, HV, d = w.T, w.HV, w.d
+    c0 = sum(L // 64 for L in w.lengths[:n])
+    nc = w.lengths[n] // 64
+
+    def view(key, dtype, shape):
+        off, nb = regions[key]
+        return raw[off:off + nb].view(dtype).reshape(shape)
+
+    assert_close("A", view("A", torch.bfloat16, (T, HV, 64)).index_select(0, ti)[:, vh], ref["A"])
+    assert_close("gcum", view("gcum", torch.float32, (HV, T)).t().index_select(0, ti)[:, vh], ref["gcum"])
+    assert_close("gamma", view("gamma", torch.float32, (NT, HV))[c0:c0 + nc][:, vh], ref["gamma"])
+    assert_close("h tape", view("H", torch.bfloat16, (NT, HV, d, d))[c0:c0 + nc][:, vh].transpose(2, 3), ref["H"])
+    for key, name in (("R", "v_new"), ("W", "w"), ("U", "u")):
+        assert_close(name, view(key, torch.bfloat16, (T, HV, d)).index_select(0, ti)[:, vh], ref[key])
+    assert_close("Aqk", view("P", torch.bfloat16, (T, HV, 64)).index_select(0, ti)[:, vh], ref["P"])
 
 
 def test_short512_ckpt_deterministic():

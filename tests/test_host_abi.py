@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     lib = _lib()
     for name in sorted(declared):
         assert hasattr(lib, name), "libgdn.so does not export %s" % name
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == G.ABI_VERSION == 2
 
 
 def _prob(lengths, H=16, HV=48, d=128, save_mode=G.SAVE_LIGHT, **kw):
@@ -59,14 +59,19 @@ def test_saved_and_workspace_formula(lengths, H, HV, d):
     NT = sum((L + 63) // 64 for L in lengths)
     light = 256 + _align(T * HV * 64 * 2) + _align(T * HV * 4) + _align(NT * HV * 4)
     assert G.gdn_saved_bytes(_prob(lengths, H, HV, d)) == light
-    full = light + _align(NT * HV * d * d * 2) + 3 * _align(T * HV * d * 2) + _align(T * HV * 64 * 2)
+    tape = _align(NT * HV * d * d * 2)
+    full = light + tape + 3 * _align(T * HV * d * 2) + _align(T * HV * 64 * 2)
     assert G.gdn_saved_bytes(_prob(lengths, H, HV, d, save_mode=G.SAVE_FULL)) == full
+    assert G.gdn_saved_bytes(_prob(lengths, H, HV, d, save_mode=G.SAVE_TAPE)) == light + tape
     wf = G.gdn_workspace_bytes(_prob(lengths, H, HV, d), G.OP_FWD)
     wb = G.gdn_workspace_bytes(_prob(lengths, H, HV, d), G.OP_BWD)
     wb_atomic = G.gdn_workspace_bytes(_prob(lengths, H, HV, d, deterministic=False), G.OP_BWD)
     assert wf >= NT * H * 64 * 64 * 2 + HV * d * d * 4  # tables, q.k, norms; the state between walk pieces
     assert wb >= wf - HV * d * d * 4 + 2 * NT * HV * d * d * 2  # the same but that state, plus two tapes
     assert wb_atomic >= wb + 2 * T * H * d * 4
+    # the kept-tape and full backwards read the state tape from the saved set: one tape fewer
+    for mode in (G.SAVE_FULL, G.SAVE_TAPE):
+        assert G.gdn_workspace_bytes(_prob(lengths, H, HV, d, save_mode=mode), G.OP_BWD) == wb - tape
 
 
 @pytest.mark.parametrize("bad,fragment", [
@@ -147,13 +152,22 @@ def test_fwd_rejects_small_workspace():
     assert _call_fwd(p, workspace_bytes=need - 1) == G.GDN_EWORKSPACE
 
 
-def test_bwd_rejects_unknown_saved_buffer():
+def test_reserved_and_segment_fields_validated():
     p = _prob([100, 28])
-    lib = _lib()
-    f = [ctypes.c_void_p(_fake(i).data_ptr()) for i in range(1, 20)]
-    rc = lib.gdn_bwd(p.ref(), f[0], f[1], f[2], f[3], f[4], f[5], None, f[6], f[7], None, f[8], f[9], f[10], f[11],
-                     f[12], None, f[13], G.gdn_workspace_bytes(p, G.OP_BWD), None)
-    assert rc == G.GDN_ESAVED
+    p.st.reserved0 = 1
+    assert _lib().gdn_saved_bytes(p.ref()) == 0 and "reserved0" in _lib().gdn_last_error().decode()
+    p = _prob([100, 28])
+    p.st.segments = -1
+    assert _lib().gdn_saved_bytes(p.ref()) == 0 and "segments" in _lib().gdn_last_error().decode()
+    p = _prob([100, 28])
+    p.st.save_mode = 3
+    assert _lib().gdn_saved_bytes(p.ref()) == 0 and "save_mode" in _lib().gdn_last_error().decode()
+
+
+def test_status_rejects_unknown_op():
+    p = _prob([100, 28])
+    assert _lib().gdn_status(p.ref(), 7, ctypes.c_void_p(_fake(1).data_ptr()), None) == G.GDN_EINVAL
+    assert "unknown op" in _lib().gdn_last_error().decode()
 
 
 def test_binding_refuses_without_library(tmp_path):
