@@ -35,7 +35,7 @@ OP_FWD, OP_RECOMPUTE, OP_BWD = 0, 1, 2
 ABI_VERSION = 2
 
 EXPORTS = ("gdn_saved_bytes", "gdn_workspace_bytes", "gdn_fwd", "gdn_fwd_recompute", "gdn_bwd", "gdn_status",
-           "gdn_last_error", "gdn_abi_version")
+           "gdn_fwd_noalloc", "gdn_last_error", "gdn_abi_version")
 
 
 class GdnError(RuntimeError):
@@ -89,6 +89,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_bwd.restype = I
     lib.gdn_status.argtypes = [pp, I, P, P]
     lib.gdn_status.restype = I
+    lib.gdn_fwd_noalloc.argtypes = [pp] + [P] * 10 + [P]
+    lib.gdn_fwd_noalloc.restype = I
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_abi_version.argtypes = []
@@ -256,6 +258,24 @@ def gdn_bwd(p: Problem, q, k, v, g, beta, cu_seqlens, saved, dO, h0=None, dht=No
                        _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads.get("dh0")), _ptr(workspace),
                        workspace.numel(), c.handle()))
     return grads
+
+
+def gdn_fwd_noalloc(p: Problem, q, k, v, g, beta, cu_seqlens, h0=None, o=None, ht=None, saved=None, stream=None):
+    """Forward whose workspace is the library's fixed device scratch array (no workspace
+    argument; the library allocates nothing). Returns (o, ht or None, saved); o, ht and saved are
+    allocated here when not given."""
+    lib = load_library()
+    c = _Call(p, q.device, stream)
+    T, HV, d = p.T, p.st.h_v, p.st.d
+    if o is None:
+        o = c.empty((T, HV, d), dtype=q.dtype)
+    if p.st.want_ht and ht is None:
+        ht = c.empty((p.N, HV, d, d), dtype=torch.float32)
+    if saved is None:
+        saved = c.empty(gdn_saved_bytes(p), dtype=torch.uint8)
+    _check(lib.gdn_fwd_noalloc(p.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(h0),
+                               _ptr(o), _ptr(ht), _ptr(saved), c.handle()))
+    return o, ht, saved
 
 
 def gdn_status(p: Problem, op: int, workspace, stream=None) -> int:

@@ -162,6 +162,21 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
  * mode and ABI version); a copy failure returns GDN_EHIP. */
 int gdn_status(const gdn_problem* p, int op, const void* workspace, void* stream);
 
+/* Size of the fixed device scratch array behind gdn_fwd_noalloc (64 MiB per device). */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* gdn_fwd for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same forward, with its workspace in a
+ * fixed device array of GDN_NOALLOC_SCRATCH_BYTES that the library holds on each device until
+ * the process ends, instead of a caller's buffer. Every launch goes to `stream` (aux_stream is
+ * ignored); no device memory is allocated or freed and no event is created. A problem whose
+ * forward workspace (gdn_workspace_bytes(p, GDN_OP_FWD)) exceeds the array is refused with
+ * GDN_EWORKSPACE. Calls on one device share the array: calls that overlap there (two streams,
+ * two threads) race and must not be issued. */
+int gdn_fwd_noalloc(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                    const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
+                    void* saved, void* stream);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* gdn_last_error(void);
 
