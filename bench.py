@@ -15,8 +15,9 @@ Prints one JSON line:
                         buffer written before every timed call, 5 groups x 12 calls, median and
                         per-group drift
   configs               the other workloads (8,192-token document fwd, CP4 share fwd+bwd with h0,
-                        512 short documents checkpointed), same protocol, each with its op
-                        roofline fraction
+                        512 short documents checkpointed, and the pages' shape B23: the causal
+                        conv1d + SiLU front-end over 10,240 packed q/k/v channels with the layer),
+                        same protocol, each with its op roofline fraction
   roofline              the kernel with the longest span on the step's critical path: its
                         algorithmic bytes (inputs, outputs, saved set) or flops per launch over
                         its mean launch duration, HIP events recorded on the stream each launch
@@ -400,6 +401,67 @@ class Runner:
                 "ckpt_kept_tape": lambda: (self.fwd(), self.recompute(kept=True), self.bwd(kept=True))}[name]
 
 
+class B23Runner:
+    """The pages' shape B23 layer: the causal conv1d + SiLU front-end over the 10,240 packed q/k/v
+    channels, writing q, k and v, then the gated delta rule on them (backward: the rule's backward,
+    then the front-end's with dq, dk, dv as its upstream gradients)."""
+
+    def __init__(self, G, syn, dev):
+        import torch
+        self.G = G
+        self.wc = syn.CONV_WORKLOADS["b23_conv"]
+        self.w = syn.WORKLOADS["b23"]
+        ci = syn.make_conv_inputs(self.wc, device=dev)
+        self.x, self.weight, self.bias = ci["x"], ci["weight"], ci["bias"]
+        self.cp = G.ConvProblem(ci["cu_seqlens"].cpu().numpy(), self.wc.groups, width=self.wc.width)
+        gi = syn.make_inputs(self.w, device=dev)
+        self.cu, self.g, self.beta, self.dO = gi["cu_seqlens"], gi["g"], gi["beta"], gi["dO"]
+        T, H, HV, d = self.w.T, self.w.H, self.w.HV, self.w.d
+        self.q = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+        self.k = torch.empty_like(self.q)
+        self.v = torch.empty((T, HV, d), dtype=torch.bfloat16, device=dev)
+        self.outs = [self.q.view(T, H * d), self.k.view(T, H * d), self.v.view(T, HV * d)]
+        self.p = G.problem_for(self.w)
+        e = lambda n: torch.empty(n, dtype=torch.uint8, device=dev)
+        self.saved = e(G.gdn_saved_bytes(self.p))
+        self.ws_f = e(G.gdn_workspace_bytes(self.p, G.OP_FWD))
+        self.ws_r = e(G.gdn_workspace_bytes(self.p, G.OP_RECOMPUTE))
+        self.ws_b = e(G.gdn_workspace_bytes(self.p, G.OP_BWD))
+        self.ws_c = e(G.gdn_conv_workspace_bytes(self.cp))
+        self.o = torch.empty_like(self.v)
+        self.grads = dict(dq=torch.empty_like(self.q), dk=torch.empty_like(self.k), dv=torch.empty_like(self.v),
+                          dg=torch.empty_like(self.g), dbeta=torch.empty_like(self.beta), dh0=None)
+        self.dys = [self.grads["dq"].view(T, H * d), self.grads["dk"].view(T, H * d), self.grads["dv"].view(T, HV * d)]
+        self.dx, self.dweight, self.dbias = torch.empty_like(self.x), torch.empty_like(self.weight), torch.empty_like(self.bias)
+        self.stream = torch.cuda.current_stream()
+
+    def conv_fwd(self):
+        self.G.gdn_conv_fwd(self.cp, self.x, self.weight, self.bias, self.cu, outs=self.outs, stream=self.stream)
+
+    def conv_bwd(self):
+        self.G.gdn_conv_bwd(self.cp, self.x, self.weight, self.bias, self.cu, self.dys, dx=self.dx,
+                            dweight=self.dweight, dbias=self.dbias, workspace=self.ws_c, stream=self.stream)
+
+    def gdn_fwd(self):
+        self.G.gdn_fwd(self.p, self.q, self.k, self.v, self.g, self.beta, self.cu, o=self.o, saved=self.saved,
+                       workspace=self.ws_f, stream=self.stream)
+
+    def gdn_recompute(self):
+        self.G.gdn_fwd_recompute(self.p, self.q, self.k, self.v, self.g, self.beta, self.cu, saved=self.saved,
+                                 workspace=self.ws_r, stream=self.stream)
+
+    def gdn_bwd(self):
+        self.G.gdn_bwd(self.p, self.q, self.k, self.v, self.g, self.beta, self.cu, self.saved, self.dO,
+                       grads=self.grads, workspace=self.ws_b, stream=self.stream)
+
+    def op(self, name):
+        return {"conv_fwd": self.conv_fwd, "conv_bwd": self.conv_bwd,
+                "fwd": lambda: (self.conv_fwd(), self.gdn_fwd()),
+                "fwdbwd": lambda: (self.conv_fwd(), self.gdn_fwd(), self.gdn_bwd(), self.conv_bwd()),
+                "ckpt": lambda: (self.conv_fwd(), self.gdn_fwd(), self.conv_fwd(), self.gdn_recompute(),
+                                 self.gdn_bwd(), self.conv_bwd())}[name]
+
+
 def protocol_time(fn, flush, stream, warmup=10, groups=5, per_group=12):
     """The pages' timing protocol, adapted: `warmup` untimed calls, then `groups` x `per_group`
     timed calls; before each, `flush` (>= 512 MiB) is written and the stream synchronised, and HIP
@@ -637,6 +699,31 @@ def main():
             cfgs[name] = t
             del rc
             torch.cuda.empty_cache()
+        # the pages' shape B23: conv front-end + gated delta rule layer
+        b23 = B23Runner(G, syn, dev)
+        wc, wb = b23.wc, b23.w
+        conv_bytes = {"conv_fwd": 2 * wc.T * wc.C * 2, "conv_bwd": 3 * wc.T * wc.C * 2}
+        rec = {"workload": "b23: 4 docs %s, %d tokens, conv over %d channels (%s), width %d, SiLU, then (H,HV)=(%d,%d), "
+                           "d=%d, l2norm=1, light saved set" % ("/".join(str(x) for x in wc.lengths), wc.T, wc.C,
+                                                               "+".join(str(c) for c in wc.groups), wc.width, wb.H,
+                                                               wb.HV, wb.d)}
+        srb = step_roofline(wb.T, wb.HV, wb.d, 2, H=wb.H, NT=_nt(wb), N=wb.N)
+        for op in ("conv_fwd", "conv_bwd", "fwd", "fwdbwd", "ckpt"):
+            t = protocol_time(b23.op(op), flush, stream)
+            if op.startswith("conv"):
+                t.update(gb_per_s=conv_bytes[op] / (t["median_ms"] / 1e3) / 1e9,
+                         roofline_ms=1e3 * conv_bytes[op] / PEAK_HBM,
+                         roofline_frac=conv_bytes[op] / PEAK_HBM / (t["median_ms"] / 1e3))
+            else:
+                extra_bytes = {"fwd": conv_bytes["conv_fwd"], "fwdbwd": sum(conv_bytes.values()),
+                               "ckpt": 2 * conv_bytes["conv_fwd"] + conv_bytes["conv_bwd"]}[op]
+                r_s = max(srb[op]["roofline_s"], (srb[op]["bytes_per_token"] * wb.T + extra_bytes) / PEAK_HBM)
+                t.update(tokens_per_s=wb.T / (t["median_ms"] / 1e3), roofline_ms=1e3 * r_s,
+                         roofline_frac=r_s / (t["median_ms"] / 1e3))
+            rec[op] = t
+        cfgs["b23"] = rec
+        del b23
+        torch.cuda.empty_cache()
         out["configs"] = cfgs
         del flush
         r = None

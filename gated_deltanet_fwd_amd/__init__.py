@@ -12,6 +12,8 @@ allocates are allocated on its launch stream. The functions carry the C names:
     gdn_fwd_recompute(problem, q, k, v, g, beta, cu, ...) -> saved
     gdn_bwd(problem, q, k, v, g, beta, cu, saved, dO, ...) -> dict of gradients
     gdn_status(problem, op, workspace)            -> int (synchronises the stream)
+    gdn_conv_fwd(conv_problem, x, weight, bias, cu, ...)      -> list of outputs (one per group)
+    gdn_conv_bwd(conv_problem, x, weight, bias, cu, dys, ...) -> dict dx, dweight, dbias
 
 A missing or unloadable library raises ImportError-like errors at first use; there is no other
 code path.
@@ -35,7 +37,8 @@ OP_FWD, OP_RECOMPUTE, OP_BWD = 0, 1, 2
 ABI_VERSION = 2
 
 EXPORTS = ("gdn_saved_bytes", "gdn_workspace_bytes", "gdn_fwd", "gdn_fwd_recompute", "gdn_bwd", "gdn_status",
-           "gdn_fwd_noalloc", "gdn_last_error", "gdn_abi_version")
+           "gdn_fwd_noalloc", "gdn_conv_workspace_bytes", "gdn_conv_fwd", "gdn_conv_bwd", "gdn_last_error",
+           "gdn_abi_version")
 
 
 class GdnError(RuntimeError):
@@ -61,6 +64,20 @@ class _Problem(ctypes.Structure):
         ("aux_stream", ctypes.c_void_p),
         ("segments", ctypes.c_int32),
         ("reserved0", ctypes.c_int32),
+    ]
+
+
+class _ConvProblem(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", ctypes.c_int32),
+        ("channels", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int64),
+        ("width", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("silu", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32),
+        ("group_channels", ctypes.c_int32 * 4),
+        ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -91,6 +108,13 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_status.restype = I
     lib.gdn_fwd_noalloc.argtypes = [pp] + [P] * 10 + [P]
     lib.gdn_fwd_noalloc.restype = I
+    cp = ctypes.POINTER(_ConvProblem)
+    lib.gdn_conv_workspace_bytes.argtypes = [cp]
+    lib.gdn_conv_workspace_bytes.restype = Z
+    lib.gdn_conv_fwd.argtypes = [cp, P, P, P, P, P, P]
+    lib.gdn_conv_fwd.restype = I
+    lib.gdn_conv_bwd.argtypes = [cp, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.gdn_conv_bwd.restype = I
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_abi_version.argtypes = []
@@ -294,3 +318,72 @@ def problem_for(w, save_mode: int = SAVE_LIGHT, deterministic: Optional[bool] = 
                    has_h0=w.has_h0, want_ht=w.want_ht if want_ht is None else want_ht, save_mode=save_mode,
                    deterministic=w.deterministic if deterministic is None else deterministic,
                    use_aux_stream=use_aux_stream, segments=segments)
+
+
+class ConvProblem:
+    """A gdn_conv_problem descriptor: the causal conv1d + SiLU front-end over [T, sum(groups)]
+    channels with a `width`-tap window, its output split into the groups' tensors."""
+
+    def __init__(self, cu_seqlens_host, group_channels, width: int = 4, dtype=torch.bfloat16, silu: bool = True):
+        self.cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+        self.groups = [int(c) for c in group_channels]
+        self.dtype = dtype
+        gc = (ctypes.c_int32 * 4)(*(self.groups + [0] * (4 - len(self.groups))))
+        self.st = _ConvProblem(n_seqs=int(self.cu.shape[0] - 1), channels=int(sum(self.groups)),
+                               n_tokens=int(self.cu[-1]), width=int(width),
+                               dtype=DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32, silu=int(bool(silu)),
+                               n_groups=len(self.groups), group_channels=gc,
+                               cu_seqlens_host=self.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+
+    @property
+    def T(self) -> int:
+        return int(self.st.n_tokens)
+
+    def ref(self):
+        return ctypes.byref(self.st)
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * 4)(*([t.data_ptr() for t in ts] + [0] * (4 - len(ts))))
+
+
+def gdn_conv_workspace_bytes(p: ConvProblem) -> int:
+    n = load_library().gdn_conv_workspace_bytes(p.ref())
+    if n == 0:
+        raise GdnError(GDN_EINVAL, load_library().gdn_last_error().decode())
+    return int(n)
+
+
+def gdn_conv_fwd(p: ConvProblem, x, weight, bias, cu_seqlens, outs=None, stream=None):
+    """Forward of the conv front-end: returns the list of output tensors, [T, group_channels[g]]."""
+    lib = load_library()
+    dev = x.device
+    s = _torch_stream(stream, dev)
+    if outs is None:
+        with torch.cuda.stream(s):
+            outs = [torch.empty((p.T, c), dtype=x.dtype, device=dev) for c in p.groups]
+    _check(lib.gdn_conv_fwd(p.ref(), _ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), _ptr_array(outs),
+                            ctypes.c_void_p(s.cuda_stream)))
+    return outs
+
+
+def gdn_conv_bwd(p: ConvProblem, x, weight, bias, cu_seqlens, dys, dx=None, dweight=None, dbias=None,
+                 workspace=None, stream=None) -> Dict[str, torch.Tensor]:
+    """Backward of the conv front-end: returns dict dx [T, C], dweight [C, W], dbias [C] (None when
+    bias is None)."""
+    lib = load_library()
+    dev = x.device
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        if dx is None:
+            dx = torch.empty_like(x)
+        if dweight is None:
+            dweight = torch.empty_like(weight)
+        if dbias is None and bias is not None:
+            dbias = torch.empty_like(bias)
+        if workspace is None:
+            workspace = torch.empty(gdn_conv_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    _check(lib.gdn_conv_bwd(p.ref(), _ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), _ptr_array(dys), _ptr(dx),
+                            _ptr(dweight), _ptr(dbias), _ptr(workspace), workspace.numel(),
+                            ctypes.c_void_p(s.cuda_stream)))
+    return dict(dx=dx, dweight=dweight, dbias=dbias)

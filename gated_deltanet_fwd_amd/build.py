@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgdn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_api.cpp", "gdn_static.hip"]
+SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_api.cpp", "gdn_static.hip", "gdn_conv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950",

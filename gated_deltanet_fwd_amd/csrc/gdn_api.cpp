@@ -718,3 +718,119 @@ int gdn_fwd_single_stream(const gdn_problem* p, const void* q, const void* k, co
 int gdn_set_error(int code, const char* msg) { return fail(code, "%s", msg); }
 
 } // namespace gdn
+
+// ---------------------------------------------------------------------------------------------
+// Short causal conv1d + SiLU front-end
+
+namespace {
+
+int check_conv(const gdn_conv_problem* p) {
+  if (!p) return fail(GDN_EINVAL, "conv problem descriptor is NULL");
+  if (p->n_seqs < 1) return fail(GDN_EINVAL, "n_seqs must be >= 1 (got %d)", p->n_seqs);
+  if (p->width < 1 || p->width > 4) return fail(GDN_EUNSUPPORTED, "conv width must be 1..4 (got %d)", p->width);
+  if (p->dtype != GDN_DTYPE_BF16 && p->dtype != GDN_DTYPE_F32)
+    return fail(GDN_EUNSUPPORTED, "unsupported dtype %d", p->dtype);
+  if (p->n_groups < 1 || p->n_groups > 4) return fail(GDN_EINVAL, "n_groups must be 1..4 (got %d)", p->n_groups);
+  int64_t c = 0;
+  for (int g = 0; g < p->n_groups; ++g) {
+    if (p->group_channels[g] < 8 || p->group_channels[g] % 8 != 0)
+      return fail(GDN_EINVAL, "group %d has %d channels: each group needs a positive multiple of 8", g,
+                  p->group_channels[g]);
+    c += p->group_channels[g];
+  }
+  if (c != p->channels) return fail(GDN_EINVAL, "channels (%d) must equal the sum of group_channels (%lld)",
+                                    p->channels, (long long)c);
+  if (!p->cu_seqlens_host) return fail(GDN_EINVAL, "cu_seqlens_host is NULL");
+  const int32_t* cu = p->cu_seqlens_host;
+  if (cu[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0] must be 0");
+  for (int n = 0; n < p->n_seqs; ++n)
+    if (cu[n + 1] < cu[n]) return fail(GDN_EINVAL, "cu_seqlens decreases at %d", n);
+  if ((int64_t)cu[p->n_seqs] != p->n_tokens)
+    return fail(GDN_EINVAL, "cu_seqlens[N] = %d but n_tokens = %lld", cu[p->n_seqs], (long long)p->n_tokens);
+  if ((int64_t)gdn::conv_blocks(p->n_tokens) > 65535) return fail(GDN_EINVAL, "too many tokens for one call");
+  return GDN_OK;
+}
+
+void conv_args(gdn::ConvArgs& a, const gdn_conv_problem* p, const void* x, const float* w, const float* b,
+               const int32_t* cu) {
+  std::memset(&a, 0, sizeof a);
+  a.T = p->n_tokens;
+  a.C = p->channels;
+  a.W = p->width;
+  a.N = p->n_seqs;
+  a.silu = p->silu ? 1 : 0;
+  a.n_groups = p->n_groups;
+  int off = 0;
+  for (int g = 0; g < p->n_groups; ++g) {
+    a.goff[g] = off;
+    off += p->group_channels[g];
+  }
+  for (int g = p->n_groups; g <= 4; ++g) a.goff[g] = off;
+  a.x = x;
+  a.w = w;
+  a.b = b;
+  a.cu = cu;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t gdn_conv_workspace_bytes(const gdn_conv_problem* p) {
+  if (check_conv(p) != GDN_OK) return 0;
+  const size_t n = (size_t)gdn::conv_blocks(p->n_tokens) * p->channels * (p->width + 1) * 4;
+  return align_up(n > 0 ? n : 1);
+}
+
+int gdn_conv_fwd(const gdn_conv_problem* p, const void* x, const float* weight, const float* bias,
+                 const int32_t* cu_seqlens, void* const* y, void* stream) {
+  CHECK(check_conv(p));
+  const int64_t T = p->n_tokens;
+  CHECK(check_tok(x, "x", T));
+  CHECK(check_ptr(weight, "weight"));
+  if (bias && !aligned16(bias)) return fail(GDN_EINVAL, "bias is not 16-byte aligned");
+  CHECK(check_ptr(cu_seqlens, "cu_seqlens"));
+  if (!y) return fail(GDN_EINVAL, "y (the array of output pointers) is NULL");
+  gdn::ConvArgs a;
+  conv_args(a, p, x, weight, bias, cu_seqlens);
+  for (int g = 0; g < p->n_groups; ++g) {
+    CHECK(check_tok(y[g], "y[g]", T));
+    a.y[g] = y[g];
+  }
+  LAUNCH("gdn_conv_fwd", gdn::launch_conv_fwd(a, p->dtype, stream));
+  g_err.clear();
+  return GDN_OK;
+}
+
+int gdn_conv_bwd(const gdn_conv_problem* p, const void* x, const float* weight, const float* bias,
+                 const int32_t* cu_seqlens, const void* const* dy, void* dx, float* dweight, float* dbias,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(check_conv(p));
+  const int64_t T = p->n_tokens;
+  CHECK(check_tok(x, "x", T));
+  CHECK(check_ptr(weight, "weight"));
+  if (bias && !aligned16(bias)) return fail(GDN_EINVAL, "bias is not 16-byte aligned");
+  CHECK(check_ptr(cu_seqlens, "cu_seqlens"));
+  CHECK(check_tok(dx, "dx", T));
+  CHECK(check_ptr(dweight, "dweight"));
+  if (dbias && !aligned16(dbias)) return fail(GDN_EINVAL, "dbias is not 16-byte aligned");
+  CHECK(check_ptr(workspace, "workspace"));
+  if (workspace_bytes < gdn_conv_workspace_bytes(p))
+    return fail(GDN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, gdn_conv_workspace_bytes(p));
+  if (!dy) return fail(GDN_EINVAL, "dy (the array of gradient pointers) is NULL");
+  gdn::ConvArgs a;
+  conv_args(a, p, x, weight, bias, cu_seqlens);
+  for (int g = 0; g < p->n_groups; ++g) {
+    CHECK(check_tok(dy[g], "dy[g]", T));
+    a.dy[g] = dy[g];
+  }
+  a.dx = dx;
+  a.dw = dweight;
+  a.db = dbias;
+  a.part = (float*)workspace;
+  LAUNCH("gdn_conv_bwd", gdn::launch_conv_bwd(a, p->dtype, stream));
+  g_err.clear();
+  return GDN_OK;
+}
+
+} // extern "C"

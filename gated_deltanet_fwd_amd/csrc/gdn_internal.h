@@ -100,4 +100,27 @@ int launch_write_tag(void* dst, const uint64_t* words, const int* status, void* 
 // GDN_OP_BWD: dq, dk, dv, dg, dbeta, dh0) are filled with NaN. Otherwise it does nothing.
 int launch_poison(const Args& a, int op, void* stream);
 
+// Short causal conv1d + SiLU front-end (gdn_conv.hip): sizes and pointers of one call.
+struct ConvArgs {
+  int64_t T;
+  int C, W, N, silu, n_groups;
+  int goff[5]; // channel offset of each output group (goff[n_groups] = C)
+  const void* x;
+  const float* w;
+  const float* b;
+  const int32_t* cu;
+  void* y[4];
+  const void* dy[4];
+  void* dx;
+  float* dw;
+  float* db;
+  float* part; // [blocks][C][W + 1] partial sums of dweight and dbias
+};
+
+// Workgroups along the tokens (each covers 1024 tokens); the backward's partial sums are
+// [conv_blocks(T)][C][W + 1] f32.
+int conv_blocks(int64_t T);
+int launch_conv_fwd(const ConvArgs& a, int dtype, void* stream);
+int launch_conv_bwd(const ConvArgs& a, int dtype, void* stream);
+
 } // namespace gdn

@@ -177,6 +177,49 @@ int gdn_fwd_noalloc(const gdn_problem* p, const void* q, const void* k, const vo
                     const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
                     void* saved, void* stream);
 
+/* ---- Short causal conv1d + SiLU front-end ------------------------------------------------
+ * The depthwise causal convolution that the pages run over the packed q/k/v channels together
+ * with the gated delta rule (flashinfer PR #8542 "Conventions": shape B23 runs the short causal
+ * convolution over the 10,240 packed q/k/v channels on every timed call; flashinfer PR #7117: the
+ * causal conv1d + SiLU training backend of the same kernel family; the README saved-set table
+ * keeps at most 3 history rows, a window of 4 taps). Per document (cu_seqlens as above), channel
+ * c and token t:
+ *
+ *     pre[t, c] = bias[c] + sum_{i<W} weight[c, i] x[t - (W-1) + i, c]   (x = 0 before the document)
+ *     y[t, c]   = SiLU(pre[t, c]) = pre / (1 + exp(-pre))                 (pre when silu = 0)
+ *
+ * x is [T, C] in the io dtype; weight f32 [C, W] (tap W-1 multiplies the current token); bias f32
+ * [C] or NULL. The output channels are written split into n_groups tensors y[g] of
+ * [T, group_channels[g]] (e.g. q, k, v: 2048, 2048, 6144 channels), so the gated delta rule reads
+ * them without a copy; the backward takes the upstream gradients split the same way and writes dx
+ * [T, C], dweight f32 [C, W] and dbias f32 [C] (if non-NULL). The weight and bias gradients are
+ * summed in a fixed order (bitwise reproducible). Ownership, streams and errors as above; these
+ * calls use `stream` only. */
+typedef struct gdn_conv_problem {
+  int32_t n_seqs;                 /* N >= 1 documents */
+  int32_t channels;               /* C = sum of group_channels, a multiple of 8 */
+  int64_t n_tokens;               /* T = cu_seqlens[N] */
+  int32_t width;                  /* W taps, 1..4 */
+  int32_t dtype;                  /* GDN_DTYPE_* of x, y, dy, dx */
+  int32_t silu;                   /* 1: y = SiLU(pre); 0: y = pre */
+  int32_t n_groups;               /* 1..4 output tensors */
+  int32_t group_channels[4];      /* channels of each output tensor, multiples of 8 */
+  const int32_t* cu_seqlens_host; /* host copy of cu_seqlens, read during each call only */
+} gdn_conv_problem;
+
+/* Bytes of device workspace gdn_conv_bwd needs (the per-workgroup partial sums of dweight and
+ * dbias). 0 if the problem is invalid. */
+size_t gdn_conv_workspace_bytes(const gdn_conv_problem* p);
+
+/* Forward: y[g] for every group. */
+int gdn_conv_fwd(const gdn_conv_problem* p, const void* x, const float* weight, const float* bias,
+                 const int32_t* cu_seqlens, void* const* y, void* stream);
+
+/* Backward: dx, dweight and (if non-NULL) dbias from x and the split upstream gradients dy[g]. */
+int gdn_conv_bwd(const gdn_conv_problem* p, const void* x, const float* weight, const float* bias,
+                 const int32_t* cu_seqlens, const void* const* dy, void* dx, float* dweight, float* dbias,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* gdn_last_error(void);
 

@@ -131,3 +131,71 @@ def make_inputs(w: Workload, device="cpu", with_grads: bool = True) -> Dict[str,
     cu[1:] = np.cumsum(np.asarray(w.lengths, dtype=np.int64))
     out["cu_seqlens"] = torch.from_numpy(cu).to(device)
     return out
+
+
+# ----------------------------------------------------------------------------------------------
+# The short causal conv1d + SiLU front-end over the packed q/k/v channels (the pages' shape B23:
+# 4 documents 12288/8192/7168/5120 = 32768 tokens, (H, HV) = (16, 48), d = 128, so 2048 + 2048 +
+# 6144 = 10240 channels; flashinfer PR #8542 "Conventions"). Distributions:
+#   x      ~ N(0, 1)              [T, C], rounded to the io dtype (RNE)
+#   weight ~ N(0, 1) / sqrt(W)    [C, W] float32
+#   bias   ~ N(0, 0.1^2)          [C] float32
+#   dy     ~ N(0, 1)              one [T, C_g] tensor per output group, io dtype
+# drawn in that order from one torch.Generator seeded with the workload's seed.
+
+
+@dataclasses.dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    seed: int
+    lengths: tuple
+    groups: tuple  # channels of each output group
+    width: int
+    dtype: str
+    silu: bool = True
+    bias: bool = True
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.lengths))
+
+    @property
+    def C(self) -> int:
+        return int(sum(self.groups))
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+CONV_WORKLOADS: Dict[str, ConvWorkload] = {
+    "b23_conv": ConvWorkload("b23_conv", 1006, (12288, 8192, 7168, 5120), (2048, 2048, 6144), 4, "bf16"),
+}
+
+# the gated delta rule layer of shape B23, fed by the conv front-end's q, k, v
+WORKLOADS["b23"] = Workload("b23", 1007, (12288, 8192, 7168, 5120), 16, 48, 128, "bf16", True, False, False, False,
+                            False, ("fwd", "bwd", "ckpt"))
+
+
+def make_conv_inputs(w: ConvWorkload, device="cpu") -> Dict[str, Optional[torch.Tensor]]:
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    out: Dict[str, Optional[torch.Tensor]] = {}
+    out["x"] = normal(w.T, w.C).to(w.torch_dtype)
+    out["weight"] = normal(w.C, w.width) / float(np.sqrt(w.width))
+    b = 0.1 * normal(w.C)
+    out["bias"] = b if w.bias else None
+    out["dy"] = [normal(w.T, c).to(w.torch_dtype) for c in w.groups]
+    cu = np.zeros(len(w.lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(w.lengths, dtype=np.int64))
+    out["cu_seqlens"] = torch.from_numpy(cu).to(device)
+    return out
+
+
+def conv_custom(name, lengths, groups, width=4, dtype="bf16", silu=True, bias=True, seed=31) -> ConvWorkload:
+    return ConvWorkload(name, seed, tuple(int(x) for x in lengths), tuple(int(c) for c in groups), int(width), dtype,
+                        silu, bias)

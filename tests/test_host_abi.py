@@ -178,3 +178,20 @@ def test_binding_refuses_without_library(tmp_path):
             G.load_library(str(tmp_path / "missing.so"))
         finally:
             G._lib = G._lib_backup
+
+
+def test_conv_problem_validation_and_workspace():
+    lens = [1024, 1, 2000]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    p = G.ConvProblem(cu, [2048, 2048, 6144], width=4)
+    blocks = (sum(lens) + 1023) // 1024
+    assert G.gdn_conv_workspace_bytes(p) == _align(blocks * 10240 * 5 * 4)
+    for groups, width, frag in (([2048, 12], 4, "multiple of 8"), ([2048], 5, "width"), ([8, 8, 8, 8, 8], 4, "n_groups")):
+        q = G.ConvProblem(cu, groups[:4], width=width)
+        if len(groups) > 4:
+            q.st.n_groups = 5
+        assert _lib().gdn_conv_workspace_bytes(q.ref()) == 0
+        assert frag in _lib().gdn_last_error().decode()
+    q = G.ConvProblem(cu, [16, 16])
+    q.st.channels = 40
+    assert _lib().gdn_conv_workspace_bytes(q.ref()) == 0 and "sum of group_channels" in _lib().gdn_last_error().decode()
