@@ -357,13 +357,13 @@ def _workload_desc(w, save_mode, det):
 class Runner:
     """Buffers and calls of one workload on the GPU (inputs resident in HBM)."""
 
-    def __init__(self, G, syn, w, dev, save_mode="light", det=True):
+    def __init__(self, G, syn, w, dev, save_mode="light", det=True, segments=0):
         import torch
         self.G, self.w, self.dev = G, w, dev
         modes = {"light": G.SAVE_LIGHT, "full": G.SAVE_FULL, "tape": G.SAVE_TAPE}
         self.inp = syn.make_inputs(w, device=dev)
-        self.p = G.problem_for(w, save_mode=modes[save_mode], deterministic=det)
-        self.pt = G.problem_for(w, save_mode=G.SAVE_TAPE, deterministic=det)  # kept-tape checkpoint
+        self.p = G.problem_for(w, save_mode=modes[save_mode], deterministic=det, segments=segments)
+        self.pt = G.problem_for(w, save_mode=G.SAVE_TAPE, deterministic=det, segments=segments)  # kept-tape ckpt
         e = lambda n: torch.empty(n, dtype=torch.uint8, device=dev)
         self.saved = e(G.gdn_saved_bytes(self.p))
         self.saved_t = e(G.gdn_saved_bytes(self.pt))
@@ -686,17 +686,23 @@ def main():
         del r
         torch.cuda.empty_cache()
         cfgs = {}
-        for name, op in (("single8k", "fwd"), ("cp4share", "fwdbwd"), ("short512", "ckpt")):
+        # segments: 0 = the library's plan (the 8k document in 4 segments, the CP share in 3, the
+        # pack and the short documents unsegmented), 1 = unsegmented, 3 = forced
+        for key, name, op, segs in (("single8k", "single8k", "fwd", 0), ("single8k_unsegmented", "single8k", "fwd", 1),
+                                    ("cp4share", "cp4share", "fwdbwd", 0),
+                                    ("cp4share_unsegmented", "cp4share", "fwdbwd", 1),
+                                    ("pack262k_fwd_3_segments", "pack262k", "fwd", 3),
+                                    ("short512", "short512", "ckpt", 0)):
             wc = syn.WORKLOADS[name]
-            rc = Runner(G, syn, wc, dev, save_mode="light", det=wc.deterministic or det)
+            rc = Runner(G, syn, wc, dev, save_mode="light", det=wc.deterministic or det, segments=segs)
             t = protocol_time(rc.op(op), flush, stream)
             ioc = 2 if wc.dtype == "bf16" else 4
             src = step_roofline(wc.T, wc.HV, wc.d, ioc, H=wc.H, NT=_nt(wc), N=wc.N, has_h0=wc.has_h0,
                                 want_ht=wc.want_ht, has_dht=wc.has_dht)[op]
-            t.update(op=op, workload=_workload_desc(wc, "light", wc.deterministic or det),
+            t.update(op=op, segments=segs, workload=_workload_desc(wc, "light", wc.deterministic or det),
                      tokens_per_s=wc.T / (t["median_ms"] / 1e3), roofline_ms=1e3 * src["roofline_s"],
                      roofline_frac=src["roofline_s"] / (t["median_ms"] / 1e3))
-            cfgs[name] = t
+            cfgs[key] = t
             del rc
             torch.cuda.empty_cache()
         # the pages' shape B23: conv front-end + gated delta rule layer

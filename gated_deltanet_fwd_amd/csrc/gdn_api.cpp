@@ -58,7 +58,6 @@ int check_problem(const gdn_problem* p, Sizes* s) {
   if (p->save_mode != GDN_SAVE_LIGHT && p->save_mode != GDN_SAVE_FULL && p->save_mode != GDN_SAVE_TAPE)
     return fail(GDN_EINVAL, "save_mode must be light (0), full (1) or tape (2)");
   if (p->segments < 0) return fail(GDN_EINVAL, "segments must be >= 0 (got %d)", p->segments);
-  if (p->segments > 1) return fail(GDN_EUNSUPPORTED, "segmented walks are not available in this build");
   if (p->reserved0 != 0) return fail(GDN_EINVAL, "reserved0 must be 0");
   if (!p->cu_seqlens_host) return fail(GDN_EINVAL, "cu_seqlens_host is NULL");
   const int32_t* cu = p->cu_seqlens_host;
@@ -86,10 +85,10 @@ int check_problem(const gdn_problem* p, Sizes* s) {
 bool keeps_tape(int save_mode) { return save_mode == GDN_SAVE_FULL || save_mode == GDN_SAVE_TAPE; }
 
 struct SavedLayout {
-  size_t akk, gcum, gamma, htape, vnew, w, u, aqk, total;
+  size_t akk, gcum, gamma, htape, vnew, w, u, aqk, plane, total;
 };
 
-SavedLayout saved_layout(const Sizes& s, int save_mode) {
+SavedLayout saved_layout(const Sizes& s, int save_mode, int plane_slots = 0) {
   SavedLayout L{};
   size_t off = kTagBytes;
   auto take = [&](size_t bytes) {
@@ -107,16 +106,18 @@ SavedLayout saved_layout(const Sizes& s, int save_mode) {
     L.u = take((size_t)s.T * s.HV * s.D * 2);
     L.aqk = take((size_t)s.T * s.HV * kChunk * 2);
   }
+  // segmented walks: the segments' FP32 start states (the carry plane)
+  if (plane_slots > 0) L.plane = take((size_t)plane_slots * s.HV * s.D * s.D * 4);
   L.total = off;
   return L;
 }
 
 struct WorkLayout {
   size_t seq_c0, c_t0, c_len, seq_order, pair_order, status, rk, rq, qk, htape, dstape, dqacc, dkacc, state,
-      total;
+      carry, total;
 };
 
-WorkLayout work_layout(const Sizes& s, int op, int save_mode, int deterministic) {
+WorkLayout work_layout(const Sizes& s, int op, int save_mode, int deterministic, int carry_slots = 0) {
   WorkLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -135,6 +136,8 @@ WorkLayout work_layout(const Sizes& s, int op, int save_mode, int deterministic)
   L.qk = take((size_t)s.NT * s.HV * kChunk * kChunk * 2);
   // the state handed from one piece of the longest document's walk to the next
   if (op != GDN_OP_BWD) L.state = take((size_t)s.HV * s.D * s.D * 4);
+  // segmented walks: start states, transfer matrices and zero-start end states of the segments
+  if (op != GDN_OP_BWD && carry_slots > 0) L.carry = take((size_t)carry_slots * s.HV * s.D * s.D * 4);
   if (op == GDN_OP_BWD) {
     if (!keeps_tape(save_mode)) L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
     L.dstape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
@@ -320,6 +323,131 @@ Split plan_split(const gdn_problem* p, const Sizes& s) {
   return sp;
 }
 
+// Segment plan (problem->segments >= 2, or the library's count for 0). Document n of c_n chunks is
+// walked as P_n = min(segments, c_n / kMinSegChunks) segments of about equal length (at least 1).
+//   forward: phase 1 walks every document's segment 0 truly (a document of one segment whole),
+//     beside the transfer walks of the middle segments 1 .. P_n - 2 (from the identity with v = 0,
+//     and from zero); the carry merge composes the middle segments' start states; phase 2 walks
+//     segments 1 .. P_n - 1 from them. The start states S_in(1 .. P_n - 1) are the saved set's
+//     carry plane (as the pages' saved set keeps its per-segment FP32 carry states at P > 1).
+//   light recompute: the plane again (segment 0 walked to its end, the transfer walks, the merge).
+//   light backward: the state tape replayed one segment per chain from the saved plane, beside
+//     the reverse walk (which walks each document whole).
+// If a table of the plan would not hold its units, the largest segment count is lowered; a
+// problem with more documents than a table holds is walked unsegmented.
+constexpr int kMinSegChunks = 8;
+
+struct SegPlans {
+  bool on = false;
+  gdn::SegPlan phase1{}, transfer{}, phase2{}, recompute{}, replay{};
+  gdn::MergePlan merge{};
+  int plane_slots = 0, work_slots = 0;
+};
+
+// CUs of the current device (256 when no device can be queried, e.g. a host-only byte query).
+int device_cus() {
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev] = n;
+  return n;
+}
+
+// The segment count of the library's plan (segments = 0), from the problem's shape and the CU
+// count only: split only when the unsegmented chains (documents x value heads) fill at most half
+// of the CUs, then as many segments (at most 8) as keep phase 1 (every document's first segment
+// and the middle segments' two transfer walks, one workgroup per value head each) within about
+// 1.25 rounds of the CUs. Measured on one MI355X (forward, bf16, (16, 48), d = 128): the
+// 8,192-token document 0.52 -> 0.38 ms at 4 segments; the two-fragment 65,536-token share
+// 2.52 -> 2.01 ms at 3; the 4-document 262,144-token pack slower at every count (its 192 chains
+// already fill the chip, and its longest document's intra pass hides behind the others' walks
+// only unsegmented).
+int auto_segments(const Sizes& s, const std::vector<int>& chunks) {
+  const int cus = device_cus();
+  if ((long)s.N * s.HV * 2 > cus) return 1;
+  int long_docs = 0;
+  for (int c : chunks) long_docs += c >= 2 * kMinSegChunks ? 1 : 0;
+  if (long_docs == 0) return 1;
+  int best = 1;
+  for (int P = 2; P <= 8; ++P)
+    if ((long)s.N * s.HV + 2L * (P - 2) * long_docs * s.HV <= (long)cus * 5 / 4) best = P;
+  return best;
+}
+
+SegPlans plan_segments(const gdn_problem* p, const Sizes& s) {
+  SegPlans sp;
+  const int U = gdn::MAX_SEG_UNITS;
+  if (p->segments == 1 || s.N > U) return sp;
+  const int32_t* cu = p->cu_seqlens_host;
+  std::vector<int> chunks(s.N), P(s.N);
+  for (int n = 0; n < s.N; ++n) chunks[n] = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+  int pmax = p->segments >= 2 ? p->segments : auto_segments(s, chunks);
+  for (; pmax >= 2; --pmax) {
+    int nt = 0, n2 = 0, nm = 0, nseg = 0;
+    for (int n = 0; n < s.N; ++n) {
+      P[n] = std::max(1, std::min(pmax, chunks[n] / kMinSegChunks));
+      nt += 2 * std::max(0, P[n] - 2);
+      n2 += P[n] - 1;
+      nm += P[n] >= 3 ? 1 : 0;
+      nseg += P[n] >= 2 ? 1 : 0;
+    }
+    if (nseg == 0) return sp;
+    if (nt + nseg <= U && n2 <= U && s.N + n2 <= U && nm <= gdn::MAX_MERGE_DOCS) break;
+  }
+  if (pmax < 2) return sp;
+  auto bound = [&](int n, int i) { return (int)((long)chunks[n] * i / P[n]); };
+  auto add = [](gdn::SegPlan& pl, gdn::SegUnit u) { pl.u[pl.n_units++] = u; };
+  int plane = 0, work = 0;
+  for (int n = 0; n < s.N; ++n) {
+    const int Pn = P[n];
+    if (Pn == 1) {
+      add(sp.phase1, gdn::SegUnit{n, 0, chunks[n], 0, -1, -1, 0, 1});
+      add(sp.replay, gdn::SegUnit{n, 0, chunks[n], 0, -1, -1, 0, 0});
+      continue;
+    }
+    const int s_base = plane;
+    plane += Pn - 1;
+    int m_base = -1, b_base = -1;
+    if (Pn >= 3) {
+      m_base = work;
+      work += Pn - 2;
+      b_base = work;
+      work += Pn - 2;
+      sp.merge.d[sp.merge.n_docs++] = gdn::MergeDoc{s_base, m_base, b_base, Pn - 2};
+    }
+    const gdn::SegUnit seg0{n, 0, bound(n, 1), 0, -1, s_base, 1, 0};
+    add(sp.phase1, seg0);
+    add(sp.recompute, seg0);
+    add(sp.replay, gdn::SegUnit{n, 0, bound(n, 1), 0, -1, -1, 0, 0});
+    for (int i = 1; i + 1 < Pn; ++i) {
+      const gdn::SegUnit m{n, bound(n, i), bound(n, i + 1), 1, -1, m_base + i - 1, 0, 0};
+      const gdn::SegUnit b{n, bound(n, i), bound(n, i + 1), 2, -1, b_base + i - 1, 0, 0};
+      add(sp.transfer, m);
+      add(sp.transfer, b);
+      add(sp.recompute, m);
+      add(sp.recompute, b);
+    }
+    for (int i = 1; i < Pn; ++i) {
+      add(sp.phase2, gdn::SegUnit{n, bound(n, i), bound(n, i + 1), 0, s_base + i - 1, -1, 0, i + 1 == Pn ? 1 : 0});
+      add(sp.replay, gdn::SegUnit{n, bound(n, i), bound(n, i + 1), 0, s_base + i - 1, -1, 0, 0});
+    }
+  }
+  // longest units first, so that the workgroups left waiting for a free CU are the shortest
+  for (gdn::SegPlan* pl : {&sp.phase1, &sp.transfer, &sp.phase2, &sp.recompute, &sp.replay})
+    std::stable_sort(pl->u, pl->u + pl->n_units,
+                     [](const gdn::SegUnit& x, const gdn::SegUnit& y) { return x.hi - x.lo > y.hi - y.lo; });
+  sp.plane_slots = plane;
+  sp.work_slots = work;
+  sp.on = true;
+  return sp;
+}
+
 // The caller's auxiliary stream, or NULL if there is none (or it is `stream` itself).
 hipStream_t aux_of(const gdn_problem* p, void* stream) {
   if (!p->aux_stream || p->aux_stream == stream) return nullptr;
@@ -361,6 +489,7 @@ void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
   if (W.dstape) a.dstape = (uint16_t*)(b + W.dstape);
   if (W.dqacc) a.dqacc = (float*)(b + W.dqacc);
   if (W.dkacc) a.dkacc = (float*)(b + W.dkacc);
+  if (W.carry) a.carry = (float*)(b + W.carry);
 }
 
 // Workspace area that holds the state between the pieces of a split walk (forward ops only).
@@ -378,6 +507,7 @@ void bind_saved(gdn::Args& a, const SavedLayout& L, void* saved) {
     a.u = (uint16_t*)(b + L.u);
     a.aqk = (uint16_t*)(b + L.aqk);
   }
+  if (L.plane) a.splane = (float*)(b + L.plane);
 }
 
 // Per-token tensors may be NULL when there are no tokens.
@@ -414,10 +544,15 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
   CHECK(check_ptr(workspace, "workspace"));
   const int full = p->save_mode == GDN_SAVE_FULL;
   const bool tape = keeps_tape(p->save_mode);
-  const WorkLayout W = work_layout(s, write_o ? GDN_OP_FWD : GDN_OP_RECOMPUTE, p->save_mode, p->deterministic);
+  const SegPlans seg = plan_segments(p, s);
+  // the light recompute of an unsegmented problem runs no walk: its saved set needs only the chunk
+  // tables and the intra pass
+  const bool walk = write_o || tape || seg.on;
+  const WorkLayout W = work_layout(s, write_o ? GDN_OP_FWD : GDN_OP_RECOMPUTE, p->save_mode, p->deterministic,
+                                   seg.work_slots);
   if (workspace_bytes < W.total)
     return fail(GDN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
-  const SavedLayout L = saved_layout(s, p->save_mode);
+  const SavedLayout L = saved_layout(s, p->save_mode, seg.plane_slots);
   gdn::Args a;
   fill_common(a, s, p);
   a.q = q;
@@ -433,15 +568,36 @@ int forward_common(const gdn_problem* p, const void* q, const void* k, const voi
   bind_workspace(a, W, workspace);
   bind_saved(a, L, saved);
 
-  // the light recompute runs no walk: the saved set needs only the chunk tables and the intra pass
-  const bool walk = write_o || tape;
-  const Split sp = walk ? plan_split(p, s) : Split{};
+  const Split sp = walk && !seg.on ? plan_split(p, s) : Split{};
   hipStream_t side = sp.on ? aux_of(p, stream) : nullptr;
   CallEvents ev;
   if (side) a.grp_split = a.H;
   LAUNCH("gdn_tables", gdn::launch_tables(a, nullptr, nullptr, stream));
   const char* walk_name = write_o ? "gdn_walk_fwd" : "gdn_walk_tape";
-  if (!side) {
+  if (seg.on && !write_o && !tape) {
+    // light recompute of a segmented problem: only the carry plane (segment 0 of each segmented
+    // document walked to its end, the transfer walks, the merge)
+    LAUNCH("gdn_intra", gdn::launch_intra(a, 0, stream));
+    LAUNCH("gdn_walk_transfer", gdn::launch_walk_seg(a, seg.recompute, 0, 0, 0, 1, stream));
+    LAUNCH("gdn_seg_merge", gdn::launch_seg_merge(a, seg.merge, stream));
+  } else if (seg.on) {
+    // segmented: the transfer walks beside phase 1 (on the auxiliary stream when there is one),
+    // the carry merge, then phase 2
+    LAUNCH("gdn_intra", gdn::launch_intra(a, 0, stream));
+    hipStream_t xs = aux_of(p, stream);
+    if (seg.transfer.n_units) {
+      if (xs) {
+        CHECK(ev.order((hipStream_t)stream, xs));
+        LAUNCH_ON(xs, "gdn_walk_transfer", gdn::launch_walk_seg(a, seg.transfer, 0, 0, 0, 1, xs));
+      } else {
+        LAUNCH("gdn_walk_transfer", gdn::launch_walk_seg(a, seg.transfer, 0, 0, 0, 1, stream));
+      }
+    }
+    LAUNCH(walk_name, gdn::launch_walk_seg(a, seg.phase1, write_o, tape, full, 0, stream));
+    if (xs && seg.transfer.n_units) CHECK(ev.order(xs, (hipStream_t)stream));
+    LAUNCH("gdn_seg_merge", gdn::launch_seg_merge(a, seg.merge, stream));
+    LAUNCH(walk_name, gdn::launch_walk_seg(a, seg.phase2, write_o, tape, full, 0, stream));
+  } else if (!side) {
     LAUNCH("gdn_intra", gdn::launch_intra(a, 0, stream));
     if (walk) LAUNCH(walk_name, gdn::launch_walk_fwd(a, write_o, tape, full, stream));
   } else {
@@ -504,7 +660,7 @@ extern "C" {
 size_t gdn_saved_bytes(const gdn_problem* p) {
   Sizes s;
   if (check_problem(p, &s) != GDN_OK) return 0;
-  return saved_layout(s, p->save_mode).total;
+  return saved_layout(s, p->save_mode, plan_segments(p, s).plane_slots).total;
 }
 
 size_t gdn_workspace_bytes(const gdn_problem* p, int op) {
@@ -514,7 +670,7 @@ size_t gdn_workspace_bytes(const gdn_problem* p, int op) {
     fail(GDN_EINVAL, "unknown op %d", op);
     return 0;
   }
-  return work_layout(s, op, p->save_mode, p->deterministic).total;
+  return work_layout(s, op, p->save_mode, p->deterministic, plan_segments(p, s).work_slots).total;
 }
 
 int gdn_fwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -552,7 +708,8 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   const WorkLayout W = work_layout(s, GDN_OP_BWD, p->save_mode, p->deterministic);
   if (workspace_bytes < W.total)
     return fail(GDN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
-  const SavedLayout L = saved_layout(s, p->save_mode);
+  const SegPlans seg = plan_segments(p, s);
+  const SavedLayout L = saved_layout(s, p->save_mode, seg.plane_slots);
   gdn::Args a;
   fill_common(a, s, p);
   a.q = q;
@@ -573,7 +730,7 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   bind_workspace(a, W, workspace);
   bind_saved(a, L, const_cast<void*>(saved));
 
-  const Split sp = plan_split(p, s);
+  const Split sp = seg.on ? Split{} : plan_split(p, s);
   hipStream_t side = sp.on ? aux_of(p, stream) : nullptr;
   CallEvents ev;
   if (side) a.grp_split = a.H;
@@ -589,7 +746,20 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
     else LAUNCH_ON(st, "gdn_walk_bwd", gdn::launch_walk_bwd(x, st));
     return GDN_OK;
   };
-  if (!side) {
+  if (seg.on && !tape) {
+    // segmented, light: the state tape replayed one segment per chain from the saved carry plane
+    // (on the auxiliary stream when there is one), beside the reverse walk
+    LAUNCH("gdn_intra_bwd", gdn::launch_intra(a, 1, stream));
+    hipStream_t xs = aux_of(p, stream);
+    if (xs) {
+      CHECK(ev.order((hipStream_t)stream, xs));
+      LAUNCH_ON(xs, "gdn_walk_tape", gdn::launch_walk_seg(a, seg.replay, 0, 1, 0, 0, xs));
+    } else {
+      LAUNCH("gdn_walk_tape", gdn::launch_walk_seg(a, seg.replay, 0, 1, 0, 0, stream));
+    }
+    LAUNCH("gdn_walk_bwd", gdn::launch_walk_bwd(a, stream));
+    if (xs) CHECK(ev.order(xs, (hipStream_t)stream));
+  } else if (!side) {
     LAUNCH("gdn_intra_bwd", gdn::launch_intra(a, 1, stream));
     CHECK(walks(a, (hipStream_t)stream));
   } else {
@@ -619,7 +789,7 @@ int gdn_status(const gdn_problem* p, int op, const void* workspace, void* stream
   CHECK(check_problem(p, &s));
   if (op != GDN_OP_FWD && op != GDN_OP_RECOMPUTE && op != GDN_OP_BWD) return fail(GDN_EINVAL, "unknown op %d", op);
   CHECK(check_ptr(workspace, "workspace"));
-  const WorkLayout W = work_layout(s, op, p->save_mode, p->deterministic);
+  const WorkLayout W = work_layout(s, op, p->save_mode, p->deterministic, plan_segments(p, s).work_slots);
   int32_t st = 0;
   hipError_t r = hipMemcpyAsync(&st, (const char*)workspace + W.status, sizeof st, hipMemcpyDeviceToHost,
                                 (hipStream_t)stream);

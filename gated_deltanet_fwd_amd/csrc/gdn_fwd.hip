@@ -417,6 +417,90 @@ __global__ __launch_bounds__(walk_threads<D>(), 1) void k_walk_fwd(Args a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Segmented walks. Workgroup b walks unit u of the plan for one value head: the (unit, q/k head)
+// groups are dealt 8 at a time to the 8 XCDs (as decode_chain does), so the value heads that share
+// a q/k head run on one XCD.
+template <int D, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL, int SEG>
+__global__ __launch_bounds__(walk_threads<D>(), 1) void k_walk_seg(Args a, SegPlan plan) {
+  __shared__ __attribute__((aligned(16))) WalkSmem<D, WRITE_O> sm;
+  const int b = blockIdx.x, GS = a.G;
+  const int sg = b / (8 * GS), rem = b - sg * 8 * GS, x = rem & 7, gi = rem >> 3;
+  const int grp = sg * 8 + x; // (unit, q/k head), unit-major
+  if (grp >= plan.n_units * a.H) return;
+  const int u = grp / a.H;
+  const SegUnit su = plan.u[u];
+  SegChain sc;
+  sc.n = su.doc;
+  sc.j = grp - u * a.H;
+  sc.gi = gi;
+  sc.lo = su.lo;
+  sc.hi = su.hi;
+  sc.kind = su.kind;
+  const size_t slot = (size_t)a.HV * D * D;
+  sc.s_in = su.in_slot >= 0 ? a.splane + su.in_slot * slot : nullptr;
+  sc.s_out = su.out_slot >= 0 ? (su.out_plane ? a.splane : a.carry) + su.out_slot * slot : nullptr;
+  sc.write_ht = su.write_ht;
+  walk_fwd_body<D, TI, WRITE_O, WRITE_TAPE, FULL, SEG>(a, b, sm, sc);
+}
+
+// Carry merge: S_in(i + 1) = M(i) S_in(i) + B(i) for i = 1 .. n_mid of one document, in FP32.
+// Workgroup (document, value head, 16-column tile): the columns of S are independent, so the
+// tile's chain of products runs alone. M(i) is staged in LDS (rows padded to 132 floats, read as
+// float4 along k) and the current S tile beside it; thread (row group, column) forms D/16 rows of
+// one column.
+__global__ __launch_bounds__(256) void k_seg_merge(Args a, MergePlan plan, int D) {
+  if (a.status[0]) return;
+  constexpr int SM_ = 132;
+  const int ntile = D / 16;
+  const int b = blockIdx.x;
+  const int doc = b / (a.HV * ntile), rem = b - doc * a.HV * ntile, h = rem / ntile, tile = rem - h * ntile;
+  if (doc >= plan.n_docs) return;
+  const MergeDoc md = plan.d[doc];
+  __shared__ __attribute__((aligned(16))) float sM[128 * SM_];
+  __shared__ float sS[128][17];
+  const int tid = threadIdx.x, col = tid & 15, nr = D / 16, r0 = (tid >> 4) * nr;
+  const size_t slot = (size_t)a.HV * D * D, head = (size_t)h * D * D;
+  const int c = 16 * tile + col;
+  for (int r = tid >> 4; r < D; r += 16) sS[r][col] = a.splane[(md.s_base) * slot + head + (size_t)r * D + c];
+  for (int i = 1; i <= md.n_mid; ++i) {
+    const float* M = a.carry + (md.m_base + i - 1) * slot + head;
+    const float* B = a.carry + (md.b_base + i - 1) * slot + head;
+    // stage M(i): D rows of D floats, 16-byte pieces
+    for (int pc = tid; pc < D * D / 4; pc += 256) {
+      const int r = pc / (D / 4), k4 = pc - r * (D / 4);
+      *reinterpret_cast<float4*>(&sM[r * SM_ + 4 * k4]) = reinterpret_cast<const float4*>(M)[pc];
+    }
+    float bv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bv[q] = q < nr ? B[(size_t)(r0 + q) * D + c] : 0.f;
+    __syncthreads(); // M(i) and the current S tile are staged
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = bv[q];
+    for (int k = 0; k < D; k += 4) {
+      const float s0 = sS[k][col], s1 = sS[k + 1][col], s2 = sS[k + 2][col], s3 = sS[k + 3][col];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < nr) {
+          const float4 m = *reinterpret_cast<const float4*>(&sM[(r0 + q) * SM_ + k]);
+          acc[q] = __builtin_fmaf(m.x, s0, acc[q]);
+          acc[q] = __builtin_fmaf(m.y, s1, acc[q]);
+          acc[q] = __builtin_fmaf(m.z, s2, acc[q]);
+          acc[q] = __builtin_fmaf(m.w, s3, acc[q]);
+        }
+    }
+    __syncthreads(); // every read of M(i) and the current S tile is done
+    float* out = a.splane + (md.s_base + i) * slot + head;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < nr) {
+        sS[r0 + q][col] = acc[q];
+        out[(size_t)(r0 + q) * D + c] = acc[q];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // launchers
 
 static inline hipStream_t S_(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -483,6 +567,43 @@ int launch_walk_fwd(const Args& a, int write_o, int write_tape, int write_vnew, 
                         : walk_t<128, float>(a, write_o, write_tape, write_vnew, s);
   return a.dtype == 0 ? walk_t<64, bf16>(a, write_o, write_tape, write_vnew, s)
                       : walk_t<64, float>(a, write_o, write_tape, write_vnew, s);
+}
+
+} // namespace gdn
+
+namespace gdn {
+
+template <int D, typename TI>
+static int walk_seg_t(const Args& a, const SegPlan& plan, int write_o, int write_tape, int write_vnew, int transfer,
+                      hipStream_t s) {
+  if (plan.n_units == 0) return 0;
+  const dim3 grid(((plan.n_units * a.H + 7) / 8) * 8 * a.G), blk(walk_threads<D>());
+  if (!write_tape) write_vnew = 0;
+  if (transfer) hipLaunchKernelGGL((k_walk_seg<D, TI, false, false, false, 2>), grid, blk, 0, s, a, plan);
+  else if (write_o && !write_tape) hipLaunchKernelGGL((k_walk_seg<D, TI, true, false, false, 1>), grid, blk, 0, s, a, plan);
+  else if (write_o && write_vnew) hipLaunchKernelGGL((k_walk_seg<D, TI, true, true, true, 1>), grid, blk, 0, s, a, plan);
+  else if (write_o) hipLaunchKernelGGL((k_walk_seg<D, TI, true, true, false, 1>), grid, blk, 0, s, a, plan);
+  else if (write_vnew) hipLaunchKernelGGL((k_walk_seg<D, TI, false, true, true, 1>), grid, blk, 0, s, a, plan);
+  else if (write_tape) hipLaunchKernelGGL((k_walk_seg<D, TI, false, true, false, 1>), grid, blk, 0, s, a, plan);
+  else return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_walk_seg(const Args& a, const SegPlan& plan, int write_o, int write_tape, int write_vnew, int transfer,
+                    void* stream) {
+  const hipStream_t s = S_(stream);
+  if (a.D == 128)
+    return a.dtype == 0 ? walk_seg_t<128, bf16>(a, plan, write_o, write_tape, write_vnew, transfer, s)
+                        : walk_seg_t<128, float>(a, plan, write_o, write_tape, write_vnew, transfer, s);
+  return a.dtype == 0 ? walk_seg_t<64, bf16>(a, plan, write_o, write_tape, write_vnew, transfer, s)
+                      : walk_seg_t<64, float>(a, plan, write_o, write_tape, write_vnew, transfer, s);
+}
+
+int launch_seg_merge(const Args& a, const MergePlan& plan, void* stream) {
+  if (plan.n_docs == 0) return 0;
+  const dim3 grid(plan.n_docs * a.HV * (a.D / 16));
+  hipLaunchKernelGGL(k_seg_merge, grid, dim3(256), 0, S_(stream), a, plan, a.D);
+  return (int)hipGetLastError();
 }
 
 } // namespace gdn

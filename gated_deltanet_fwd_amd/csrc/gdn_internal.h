@@ -74,6 +74,41 @@ struct Args {
   int piece_lo, piece_hi;
   const float* state_in;
   float* state_out;
+  // Segmented walks: f32 [slots][HV, d, d] transfer matrices and zero-start end states of the
+  // middle segments (workspace), and the segments' start states (the saved set's carry plane).
+  float* carry;
+  float* splane;
+};
+
+// Segmented walks of long documents (problem->segments >= 2). A document of P segments is walked
+// as: its segment 0 from its true start (h0 or 0), and for each middle segment 1..P-2 a transfer
+// walk from the identity with v = 0 (the segment's linear map M) and one from zero (its affine
+// part B), side by side; then a carry merge S_in(i+1) = M(i) S_in(i) + B(i); then segments 1..P-1
+// from their true start states, side by side. Each unit below is one (document, chunk range)
+// walked for every value head of the document.
+constexpr int MAX_SEG_UNITS = 80;
+struct SegUnit {
+  int doc;       // document index
+  int lo, hi;    // chunks [lo, hi) counted from the document's first
+  int kind;      // 0: true walk; 1: transfer walk from the identity with v = 0; 2: walk from zero
+  int in_slot;   // carry-plane slot of the start state (-1: h0 or zero)
+  int out_slot;  // slot for the end state (-1: none)
+  int out_plane; // 1: out_slot is a carry-plane slot (a start state); 0: a workspace slot (M or B)
+  int write_ht;  // 1: the document's last segment, writes ht (when the problem wants it)
+};
+struct SegPlan {
+  int n_units;
+  SegUnit u[MAX_SEG_UNITS];
+};
+// Carry merge of one document: S_in(i + 1) = M(i) S_in(i) + B(i), i = 1 .. n_mid, with S_in(i) in
+// carry-plane slot s_base + i - 1, M(i) in workspace slot m_base + i - 1, B(i) in b_base + i - 1.
+constexpr int MAX_MERGE_DOCS = 32;
+struct MergeDoc {
+  int s_base, m_base, b_base, n_mid;
+};
+struct MergePlan {
+  int n_docs;
+  MergeDoc d[MAX_MERGE_DOCS];
 };
 
 int chain_blocks(const Args& a, int ntile);
@@ -88,6 +123,11 @@ int launch_tables(const Args& a, const uint64_t* tag, const uint64_t* tag_words,
 int launch_intra(const Args& a, int bwd_prep, void* stream);
 // write_tape: the chunk-start state tape; write_vnew: v_new (the full saved set)
 int launch_walk_fwd(const Args& a, int write_o, int write_tape, int write_vnew, void* stream);
+// The units of a segment plan: true walks (transfer = 0) or transfer walks (transfer = 1, which
+// write nothing but their end states).
+int launch_walk_seg(const Args& a, const SegPlan& plan, int write_o, int write_tape, int write_vnew, int transfer,
+                    void* stream);
+int launch_seg_merge(const Args& a, const MergePlan& plan, void* stream);
 int launch_walk_pair(const Args& a, void* stream); // tape walk and reverse walk in one launch
 int launch_wy_full(const Args& a, void* stream);
 int launch_walk_bwd(const Args& a, void* stream);

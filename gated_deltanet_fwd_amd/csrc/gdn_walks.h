@@ -47,19 +47,49 @@ struct WalkSmem {
   float sgam[2];
 };
 
-template <int D, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL>
-__device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D, WRITE_O>& sm) {
+// One chain of a segmented walk (see SegPlan): the unit's document, chunk range and carry slots,
+// and the value head.
+struct SegChain {
+  int n, j, gi;       // document, q/k head, value head within the group
+  int lo, hi;         // chunks [lo, hi) counted from the document's first
+  int kind;           // SegUnit::kind
+  const float* s_in;  // start states [HV, d, d] (NULL: h0 or zero)
+  float* s_out;       // end states [HV, d, d] (NULL: none)
+  int write_ht;
+};
+
+// SEG = 0: a chain of a whole-document launch (decode_chain, pieces); SEG = 1: a true walk of a
+// segment; SEG = 2: a walk that writes only its end state (kind 0: from the true start state;
+// kind 1: from the identity with v = 0; kind 2: from zero).
+template <int D, typename TI, bool WRITE_O, bool WRITE_TAPE, bool FULL, int SEG = 0>
+__device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D, WRITE_O>& sm,
+                                              const SegChain& sc = SegChain{}) {
   if (a.status[0]) return;
-  const ChainMap cm = decode_chain(blk, a, 1);
-  if (!cm.valid) return;
-  // chain constants are uniform: held in scalar registers (the chunk's buffer resources below
-  // are built from them)
-  const int n = __builtin_amdgcn_readfirstlane(a.seq_order[cm.rank]);
-  const int j = cm.j, h = j * a.G + cm.gi;
-  // this launch's piece of the document: chunks [piece_lo, piece_hi) from its first
-  const int c_doc = __builtin_amdgcn_readfirstlane(a.seq_c0[n]);
-  const int c_begin = c_doc + a.piece_lo;
-  const int c_end = c_doc + min(__builtin_amdgcn_readfirstlane(a.seq_c0[n + 1]) - c_doc, a.piece_hi);
+  int n, j, h, c_begin, c_end, piece_lo;
+  if constexpr (SEG == 0) {
+    const ChainMap cm = decode_chain(blk, a, 1);
+    if (!cm.valid) return;
+    // chain constants are uniform: held in scalar registers (the chunk's buffer resources below
+    // are built from them)
+    n = __builtin_amdgcn_readfirstlane(a.seq_order[cm.rank]);
+    j = cm.j;
+    h = j * a.G + cm.gi;
+    // this launch's piece of the document: chunks [piece_lo, piece_hi) from its first
+    const int c_doc = __builtin_amdgcn_readfirstlane(a.seq_c0[n]);
+    piece_lo = a.piece_lo;
+    c_begin = c_doc + a.piece_lo;
+    c_end = c_doc + min(__builtin_amdgcn_readfirstlane(a.seq_c0[n + 1]) - c_doc, a.piece_hi);
+  } else {
+    n = sc.n;
+    j = sc.j;
+    h = j * a.G + sc.gi;
+    const int c_doc = __builtin_amdgcn_readfirstlane(a.seq_c0[n]);
+    piece_lo = sc.lo;
+    c_begin = c_doc + sc.lo;
+    c_end = c_doc + sc.hi;
+  }
+  // transfer walk from the identity: v contributes nothing
+  const bool zero_v = SEG == 2 && sc.kind == 1;
   constexpr int NT = walk_threads<D>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -77,7 +107,7 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
   const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
   const int v0 = 16 * w;
   // chunk c of the piece starts at token doc_t0 + 64 (c - c_begin)
-  const int doc_t0 = __builtin_amdgcn_readfirstlane(a.cu[n]) + a.piece_lo * CH;
+  const int doc_t0 = __builtin_amdgcn_readfirstlane(a.cu[n]) + piece_lo * CH;
   const int doc_t1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
 
   // ---- staging: global -> registers (issued before a chunk's compute) -> LDS (after it).
@@ -111,6 +141,10 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
       rK[it] = IO<TI>::bload8(kr, oK[it]);
       rV[it] = IO<TI>::bload8(vr, oV[it]);
       if (WRITE_O) rQ[it] = IO<TI>::bload8(qr, oK[it]);
+    }
+    if (SEG == 2) {
+#pragma unroll
+      for (int it = 0; it < PPT; ++it) rV[it] = keep8(rV[it], !zero_v);
     }
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(akk + ((size_t)t0 * a.HV + h) * CH, (last * a.HV * CH + CH) * 2);
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(pm + ((size_t)c * a.HV + h) * CH * CH, CH * CH * 2);
@@ -159,14 +193,20 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
 
   // ---- state: rows 16 rt + 4 lg + i (key), column v0 + lr (value)
   f32x4 S[NRT];
+  const float* s_in = SEG ? sc.s_in : a.state_in;
+  // segment walks: h0 only for a document's first segment (true walk from no slot)
+  const bool use_h0 = a.has_h0 && (SEG == 0 || sc.kind == 0);
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 16 * rt + 4 * lg + i;
-      S[rt][i] = a.state_in ? a.state_in[((size_t)h * D + d) * D + v0 + lr]
-                 : a.has_h0   ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr]
-                              : 0.f;
+      if (SEG == 2 && sc.kind == 1) S[rt][i] = d == v0 + lr ? 1.f : 0.f;
+      else if (SEG == 2 && sc.kind == 2) S[rt][i] = 0.f;
+      else
+        S[rt][i] = s_in ? s_in[((size_t)h * D + d) * D + v0 + lr]
+                   : use_h0 ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr]
+                            : 0.f;
     }
 
   auto step = [&](int b, int c) {
@@ -303,13 +343,14 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
     store_chunk(b ^ 1, cn);
     __syncthreads();
   }
-  if (a.state_out) {
+  float* s_out = SEG ? sc.s_out : a.state_out;
+  if (s_out) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.state_out[((size_t)h * D + 16 * rt + 4 * lg + i) * D + v0 + lr] = S[rt][i];
+      for (int i = 0; i < 4; ++i) s_out[((size_t)h * D + 16 * rt + 4 * lg + i) * D + v0 + lr] = S[rt][i];
   }
-  if (WRITE_O && a.want_ht) {
+  if (WRITE_O && a.want_ht && (SEG == 0 || sc.write_ht)) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll

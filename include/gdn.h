@@ -107,10 +107,14 @@ typedef struct gdn_problem {
   void* aux_stream;               /* optional second stream (hipStream_t) of the caller on the
                                      device of `stream`; NULL: every launch on `stream` */
   int32_t segments;               /* walk segments per document (the PR #8172 README option
-                                     table's `segments` / `walk_seg`): 0 or 1 = each document's
-                                     state walk is one serial chain; P >= 2 = documents long
-                                     enough are walked as up to P segments (transfer walks,
-                                     a carry merge, then the segments' walks side by side) */
+                                     table's `segments` / `walk_seg` and its plan policy):
+                                     1 = each document's state walk is one serial chain;
+                                     P >= 2 = documents of at least 16 chunks are walked as up to
+                                     P segments (transfer walks, a carry merge, then the
+                                     segments' walks side by side); 0 = the library's count,
+                                     from the shape and the device's CU count (segments only
+                                     when the chains fill at most half of the CUs). At P > 1
+                                     the saved set ends with the segments' start states */
   int32_t reserved0;              /* must be 0 */
 } gdn_problem;
 

@@ -24,12 +24,14 @@ def _dev(inp):
 
 
 def _run(w, inp, save_mode=G.SAVE_LIGHT, det=None, bwd=True, recompute=False, poison=False, l2norm=None,
-         aux=True, recompute_mode=None, dht=True):
+         aux=True, recompute_mode=None, dht=True, segments=0):
     """fwd (save_mode), optionally recompute (recompute_mode, default save_mode) into a fresh saved
-    buffer, then bwd with the problem of the saved set it reads."""
-    p = G.problem_for(w, save_mode=save_mode, deterministic=det, l2norm=l2norm, use_aux_stream=aux)
+    buffer, then bwd with the problem of the saved set it reads. segments = 0: the library's plan;
+    1: unsegmented walks (the two-part launch plan when one document dominates)."""
+    p = G.problem_for(w, save_mode=save_mode, deterministic=det, l2norm=l2norm, use_aux_stream=aux,
+                      segments=segments)
     pr = p if recompute_mode is None else G.problem_for(w, save_mode=recompute_mode, deterministic=det,
-                                                         l2norm=l2norm, use_aux_stream=aux)
+                                                         l2norm=l2norm, use_aux_stream=aux, segments=segments)
     a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
     fill = float("nan") if poison else 0.0
     o = torch.full_like(inp["v"], fill)
@@ -205,8 +207,8 @@ def test_split_launch_light_full_recompute_bitwise():
     the split reverse walk alone)."""
     w = [x for x in EDGE if x.name == "split_mid"][0]
     inp = _dev(syn.make_inputs(w))
-    a = _run(w, inp, save_mode=G.SAVE_LIGHT, det=True)
-    b = _run(w, inp, save_mode=G.SAVE_FULL, det=True, recompute=True)
+    a = _run(w, inp, save_mode=G.SAVE_LIGHT, det=True, segments=1)
+    b = _run(w, inp, save_mode=G.SAVE_FULL, det=True, recompute=True, segments=1)
     assert torch.equal(b["saved"], b["saved_recompute"])
     for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
         assert torch.equal(a[k], b[k]), k
@@ -219,9 +221,9 @@ def test_split_walk_in_pieces():
     w = syn.custom("pieces", [3000, 49252, 700], 1, 2, 64, "bf16", has_h0=True, want_ht=True, has_dht=True,
                    seed=14)
     inp = _dev(syn.make_inputs(w))
-    a = _run(w, inp, save_mode=G.SAVE_LIGHT, det=True)
+    a = _run(w, inp, save_mode=G.SAVE_LIGHT, det=True, segments=1)
     _check_all(w, inp, a)
-    b = _run(w, inp, save_mode=G.SAVE_FULL, det=True)
+    b = _run(w, inp, save_mode=G.SAVE_FULL, det=True, segments=1)
     for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
         assert torch.equal(a[k], b[k]), k
 
@@ -234,7 +236,7 @@ def test_concurrent_calls_on_two_streams_bitwise():
 
     w = [x for x in EDGE if x.name == "split_mid"][0]
     inp = _dev(syn.make_inputs(w))
-    ref = _run(w, inp, det=True)
+    ref = _run(w, inp, det=True, segments=1)
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     aux_streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = [None, None]
@@ -243,7 +245,7 @@ def test_concurrent_calls_on_two_streams_bitwise():
     def work(i):
         try:
             with torch.cuda.stream(streams[i]):
-                p = G.problem_for(w, deterministic=True, use_aux_stream=aux_streams[i])
+                p = G.problem_for(w, deterministic=True, use_aux_stream=aux_streams[i], segments=1)
                 a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
                 o, ht, saved = G.gdn_fwd(p, *a, h0=inp["h0"], stream=streams[i])
                 gr = G.gdn_bwd(p, *a, saved, inp["dO"], h0=inp["h0"], dht=inp["dht"], stream=streams[i])
@@ -369,8 +371,8 @@ def test_single_stream_bitwise(name):
         w = [x for x in EDGE if x.name == name][0]
     inp = _dev(syn.make_inputs(w))
     for mode in (G.SAVE_LIGHT, G.SAVE_FULL):
-        a = _run(w, inp, save_mode=mode, det=True, aux=True)
-        b = _run(w, inp, save_mode=mode, det=True, aux=False)
+        a = _run(w, inp, save_mode=mode, det=True, aux=True, segments=1)
+        b = _run(w, inp, save_mode=mode, det=True, aux=False, segments=1)
         assert torch.equal(a["saved"], b["saved"])
         for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
             assert torch.equal(a[k], b[k]), k
@@ -441,9 +443,9 @@ def test_pack262k_longest_document_alone_bitwise():
     launch per kernel, one walk per chain) it gives the same bits."""
     w, inp = _big("pack262k")
     assert not w.has_h0
-    a = _run(w, inp, det=True)
+    a = _run(w, inp, det=True, segments=1)
     L0 = w.lengths[0]
-    w2 = syn.custom("pack_doc0_twice", [L0, L0], w.H, w.HV, w.d, w.dtype, want_ht=True)
+    w2 = syn.custom("pack_doc0_twice", [L0, L0], w.H, w.HV, w.d, w.dtype, want_ht=True)  # unsegmented below
     two = {k: (torch.cat([v[:L0], v[:L0]]).contiguous() if v is not None and k not in ("cu_seqlens", "h0", "dht")
                else v) for k, v in inp.items()}
     two["cu_seqlens"] = torch.tensor([0, L0, 2 * L0], dtype=torch.int32, device=DEV)
@@ -451,7 +453,7 @@ def test_pack262k_longest_document_alone_bitwise():
     grads = {k: a[k][:L0].clone() for k in ("dq", "dk", "dv", "dg", "dbeta")}
     del a
     torch.cuda.empty_cache()
-    b = _run(w2, two, det=True)
+    b = _run(w2, two, det=True, segments=1)
     for half in (slice(0, L0), slice(L0, 2 * L0)):
         assert torch.equal(a_o, b["o"][half])
         for k, v in grads.items():

@@ -195,3 +195,38 @@ def test_conv_problem_validation_and_workspace():
     q = G.ConvProblem(cu, [16, 16])
     q.st.channels = 40
     assert _lib().gdn_conv_workspace_bytes(q.ref()) == 0 and "sum of group_channels" in _lib().gdn_last_error().decode()
+
+
+def test_segmented_workspace_carry_slots():
+    """A document of 128 chunks walked as 4 segments keeps 2 transfer matrices and 2 zero-start end
+    states (f32 [HV, d, d] each) in the forward and recompute workspaces, and its 3 segment start
+    states (the carry plane) at the end of the saved set, in every form; a document shorter than
+    two segments' minimum length is not split."""
+    HV, d = 6, 128
+    base = G.gdn_workspace_bytes(_prob([8192], 2, HV, d, segments=1), G.OP_FWD)
+    seg = G.gdn_workspace_bytes(_prob([8192], 2, HV, d, segments=4), G.OP_FWD)
+    assert seg - base == _align(4 * HV * d * d * 4)
+    for mode in (G.SAVE_LIGHT, G.SAVE_FULL, G.SAVE_TAPE):
+        assert G.gdn_saved_bytes(_prob([8192], 2, HV, d, segments=4, save_mode=mode)) == \
+            G.gdn_saved_bytes(_prob([8192], 2, HV, d, segments=1, save_mode=mode)) + _align(3 * HV * d * d * 4)
+    assert G.gdn_workspace_bytes(_prob([8192], 2, HV, d, segments=4, save_mode=G.SAVE_TAPE), G.OP_RECOMPUTE) > \
+        G.gdn_workspace_bytes(_prob([8192], 2, HV, d, segments=1, save_mode=G.SAVE_TAPE), G.OP_RECOMPUTE)
+    # 15 chunks: fewer than two segments of 8 chunks, so one segment and no carry slots
+    assert G.gdn_workspace_bytes(_prob([960], 2, HV, d, segments=4), G.OP_FWD) == \
+        G.gdn_workspace_bytes(_prob([960], 2, HV, d, segments=1), G.OP_FWD)
+    # the backward keeps no transfer matrices (it replays from the saved start states)
+    assert G.gdn_workspace_bytes(_prob([8192], 2, HV, d, segments=4), G.OP_BWD) == \
+        G.gdn_workspace_bytes(_prob([8192], 2, HV, d, segments=1), G.OP_BWD)
+
+
+def test_library_segment_plan():
+    """segments = 0: the library's count from the shape and the CU count (256 without a device):
+    the 8,192-token document at (16, 48) is split in 4, the two-fragment share in 3, the 4-document
+    pack not at all (its chains already fill the CUs)."""
+    HV, d = 48, 128
+    extra = lambda lengths, segs: (G.gdn_saved_bytes(_prob(lengths, 16, HV, d, segments=segs)) -
+                                   G.gdn_saved_bytes(_prob(lengths, 16, HV, d, segments=1)))
+    plane = lambda k: _align(k * HV * d * d * 4)
+    assert extra([8192], 0) == plane(3) == extra([8192], 4)
+    assert extra([40960, 24576], 0) == plane(4) == extra([40960, 24576], 3)
+    assert extra([98304, 65536, 57344, 40960], 0) == 0

@@ -20,9 +20,9 @@ def _dev(inp):
     return {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
 
 
-def _both(w, check_oracle=True):
+def _both(w, check_oracle=True, segments=0):
     inp = _dev(syn.make_inputs(w))
-    p = G.problem_for(w, use_aux_stream=False)
+    p = G.problem_for(w, use_aux_stream=False, segments=segments)
     a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"])
     # both saved buffers start with the same bytes: the alignment gaps between the saved regions
     # and the tag's unused words are never written
@@ -56,11 +56,14 @@ def test_noalloc_two_calls_second_smaller():
 
 
 def test_noalloc_near_the_array_size():
-    """The 8,192-token document at (16, 48), d = 128: a forward workspace of about 55 MiB."""
+    """The 8,192-token document at (16, 48), d = 128, unsegmented: a forward workspace of about
+    55 MiB. (The library's plan walks it in 4 segments, whose transfer matrices take it past the
+    array: that call is refused.)"""
     w = syn.WORKLOADS["single8k"]
-    p = G.problem_for(w)
+    p = G.problem_for(w, segments=1)
     assert G.gdn_workspace_bytes(p, G.OP_FWD) > (48 << 20)
-    _both(w, check_oracle=False)
+    _both(w, check_oracle=False, segments=1)
+    assert G.gdn_workspace_bytes(G.problem_for(w), G.OP_FWD) > (64 << 20)
 
 
 def test_noalloc_refuses_a_problem_beyond_the_array():
