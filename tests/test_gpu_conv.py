@@ -73,8 +73,8 @@ def test_conv_small(w):
 
 
 MULTI = [
-    # documents ending at a wave's (256) and a workgroup's (1024) token boundary, a one-token
-    # document across a boundary, a last partial workgroup; groups split the 512-channel tiles
+    # documents ending at a wave's (128) and a workgroup's (512) token boundary, a one-token
+    # document across a boundary, a last partial workgroup; groups split the 256-channel tiles
     syn.conv_custom("blocks_bf16", [1024, 1, 255, 769, 700, 251], [512, 16, 520], seed=52),
     syn.conv_custom("blocks_f32_w3", [300, 1500, 3], [24, 1000], width=3, dtype="f32", seed=53),
 ]

@@ -184,7 +184,7 @@ def test_conv_problem_validation_and_workspace():
     lens = [1024, 1, 2000]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     p = G.ConvProblem(cu, [2048, 2048, 6144], width=4)
-    blocks = (sum(lens) + 1023) // 1024
+    blocks = (sum(lens) + 511) // 512  # workgroups of 4 waves x 128 tokens
     assert G.gdn_conv_workspace_bytes(p) == _align(blocks * 10240 * 5 * 4)
     for groups, width, frag in (([2048, 12], 4, "multiple of 8"), ([2048], 5, "width"), ([8, 8, 8, 8, 8], 4, "n_groups")):
         q = G.ConvProblem(cu, groups[:4], width=width)
