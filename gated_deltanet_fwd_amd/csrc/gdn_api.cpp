@@ -114,7 +114,7 @@ SavedLayout saved_layout(const Sizes& s, int save_mode, int plane_slots = 0) {
 
 struct WorkLayout {
   size_t seq_c0, c_t0, c_len, seq_order, pair_order, status, rk, rq, qk, htape, dstape, dqacc, dkacc, state,
-      carry, total;
+      carry, queue, total;
 };
 
 WorkLayout work_layout(const Sizes& s, int op, int save_mode, int deterministic, int carry_slots = 0) {
@@ -139,6 +139,7 @@ WorkLayout work_layout(const Sizes& s, int op, int save_mode, int deterministic,
   // segmented walks: start states, transfer matrices and zero-start end states of the segments
   if (op != GDN_OP_BWD && carry_slots > 0) L.carry = take((size_t)carry_slots * s.HV * s.D * s.D * 4);
   if (op == GDN_OP_BWD) {
+    L.queue = take(2 * 4); // chunk-gradient work queues of the two parts
     if (!keeps_tape(save_mode)) L.htape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
     L.dstape = take((size_t)s.NT * s.HV * s.D * s.D * 2);
     if (!deterministic) {
@@ -490,6 +491,7 @@ void bind_workspace(gdn::Args& a, const WorkLayout& W, void* ws) {
   if (W.dqacc) a.dqacc = (float*)(b + W.dqacc);
   if (W.dkacc) a.dkacc = (float*)(b + W.dkacc);
   if (W.carry) a.carry = (float*)(b + W.carry);
+  if (W.queue) a.gq = (int*)(b + W.queue);
 }
 
 // Workspace area that holds the state between the pieces of a split walk (forward ops only).
@@ -739,6 +741,10 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   uint64_t words[4];
   tag_words(p, words);
   LAUNCH("gdn_tables", gdn::launch_tables(a, (const uint64_t*)saved, words, stream));
+  if (!p->deterministic) { // accumulators of the atomic dq, dk reduction
+    LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
+    LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dkacc, (size_t)s.T * s.H * s.D, stream));
+  }
   // light: the state tape is replayed; the tape walk and the reverse walk are independent and
   // share one launch. full / kept tape: the tape is in the saved set.
   auto walks = [&](const gdn::Args& x, hipStream_t st) -> int {
@@ -763,21 +769,22 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
     LAUNCH("gdn_intra_bwd", gdn::launch_intra(a, 1, stream));
     CHECK(walks(a, (hipStream_t)stream));
   } else {
+    // the chunk gradients of the other documents run on the auxiliary stream as soon as their
+    // walks end, beside the longest document's walk; the longest document's follow its walk
     gdn::Args aa = a, ab = a;
     range_a(aa, sp);
     range_b(ab, sp);
+    ab.gq = a.gq + 1;
     LAUNCH("gdn_intra_bwd", gdn::launch_intra(aa, 1, stream));
     CHECK(ev.order((hipStream_t)stream, side));
     CHECK(walks(aa, (hipStream_t)stream));
     LAUNCH_ON(side, "gdn_intra_bwd", gdn::launch_intra(ab, 1, side));
     CHECK(walks(ab, side));
+    LAUNCH_ON(side, "gdn_chunk_grad", gdn::launch_chunk_grad(ab, p->deterministic, side));
+    LAUNCH("gdn_chunk_grad", gdn::launch_chunk_grad(aa, p->deterministic, stream));
     CHECK(ev.order(side, (hipStream_t)stream));
   }
-  if (!p->deterministic) {
-    LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
-    LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dkacc, (size_t)s.T * s.H * s.D, stream));
-  }
-  LAUNCH("gdn_chunk_grad", gdn::launch_chunk_grad(a, p->deterministic, stream));
+  if (!side) LAUNCH("gdn_chunk_grad", gdn::launch_chunk_grad(a, p->deterministic, stream));
   if (!p->deterministic) LAUNCH("gdn_finalize_qk", gdn::launch_finalize_qk(a, stream));
   LAUNCH("gdn_poison", gdn::launch_poison(a, GDN_OP_BWD, stream));
   g_err.clear();

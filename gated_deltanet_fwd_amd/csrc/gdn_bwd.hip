@@ -303,16 +303,23 @@ struct GradSmem {
       bf16 sE2[CH * SA];  // dKk^T diag(rk), row-major
     } t;
   } u;
+  int next_item; // the item claimed from the work queue, published by thread 0 (last: the tiles
+                 // above keep their 16-byte alignment)
 };
 
+
+static_assert(offsetof(GradSmem<128>, u) % 16 == 0 && offsetof(GradSmem<64>, u) % 16 == 0,
+              "the slice and tail tiles start 16-byte aligned");
 
 template <int D, typename TI, bool DET>
 __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   if (a.status[0]) return;
-  // Persistent: workgroup b takes items b, b + gridDim.x, ... (item = chunk x per-chunk index y;
-  // y is the q/k head, or the value head in atomic mode). The next item's first loads are issued
-  // during the current item's last head and before its epilogue, so they are in flight while it
-  // finishes instead of at the start of a new workgroup.
+  // Persistent: workgroup b takes item b, then items claimed from the launch's work queue
+  // (a.gq: gridDim.x + the counter's old value), until the queue runs past the last item (item =
+  // chunk x per-chunk index y; y is the q/k head, or the value head in atomic mode). Workgroups
+  // that start late, behind another launch's, take fewer items. The next item is claimed at the
+  // start of the current one and its first loads are issued during the current item's last head
+  // and before its epilogue, so they are in flight while it finishes.
   const int nj = DET ? a.H : a.HV;
   const int n_items = a.c_count * nj;
   int item = blockIdx.x;
@@ -403,11 +410,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   asm volatile("" : "+v"(tid_i));
   const int tid = tid_i, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rt = w & 3, half = w >> 2, lr = lane & 15, lg = lane >> 4, row0 = 16 * rt, arow = row0 + lr;
-  // the next item (this one again after the last: its loads then repeat this item's, unused)
-  const int item_n = item + (int)gridDim.x;
-  const bool has_next = item_n < n_items;
-  int c_n, j_n, hf_n, len_n, t0_n;
-  decode(has_next ? item_n : item, c_n, j_n, hf_n, len_n, t0_n);
+  // claim the next item; every thread reads it after the staging barrier below (and thread 0
+  // writes the slot again only in the next item, after several more barriers)
+  if (tid == 0) sm.next_item = (int)gridDim.x + atomicAdd(a.gq, 1);
 
   // ---- stage K, Q and the norms; Kk = Kh Kh^T, Qk = Qh Kh^T on this wave's tiles
 #pragma unroll
@@ -421,6 +426,11 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     sm.srq[tid] = keepf(rqv, tid < len);
   }
   __syncthreads();
+  // the next item (this one again after the last: its loads then repeat this item's, unused)
+  const int item_n = __builtin_amdgcn_readfirstlane(sm.next_item);
+  const bool has_next = item_n < n_items;
+  int c_n, j_n, hf_n, len_n, t0_n;
+  decode(has_next ? item_n : item, c_n, j_n, hf_n, len_n, t0_n);
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
     f32x4 Kk = zero4(), Qk = zero4();
@@ -452,12 +462,11 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   auto qdot_acc = [&](int row0, int lg, int half, int lr) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int t = 0; t < NT2; ++t)
+    for (int t = 0; t < NT2; ++t) {
+      const bf16x4 qv = lds_tr4c(sm.sQ, SK, row0, 16 * (half * NT2 + t)); // this lane's C rows
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = row0 + lg * 4 + i, dk = 16 * (half * NT2 + t) + lr;
-        acc[i] += (float)sm.sQ[r * SK + dk] * dQacc[t][i];
-      }
+      for (int i = 0; i < 4; ++i) acc[i] += (float)qv[i] * dQacc[t][i];
+    }
     const f32x4 rq_r = *reinterpret_cast<const f32x4*>(sm.srq + row0 + lg * 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] *= rq_r[i];
@@ -529,11 +538,10 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       for (int k2 = 0; k2 < 2; ++k2) pdv = mfma(lds8(sm.sP, SA, arow, k2 * 32 + lg * 8), lds_tr8(B.sdO, SDO, k2 * 32, cs), pdv);
       float xu[4], x[4], dr[4];
       const f32x4 rk_r = rk4();
+      const bf16x4 vv = lds_tr4c(B.sV, SV, row0, cs);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = row0 + lg * 4 + i, cc = cs + lr;
-        const float vv = (float)B.sV[r * SV + cc];
-        xu[i] = vv - brow[i] * rk_r[i] * ksv[i];
+        xu[i] = (float)vv[i] - brow[i] * rk_r[i] * ksv[i];
         x[i] = beta_r[i] * xu[i];
         dr[i] = pdv[i] + dec_r[i] * rk_r[i] * kdv[i];
       }
@@ -792,13 +800,15 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     const f32x4 rk_r = rk4(), rq_r = rq4();
     if (a.l2norm) {
 #pragma unroll
-      for (int t = 0; t < NT2; ++t)
+      for (int t = 0; t < NT2; ++t) {
+        const bf16x4 qv = lds_tr4c(sm.sQ, SK, row0, 16 * (half * NT2 + t));
+        const bf16x4 kv4 = lds_tr4c(sm.sK, SK, row0, 16 * (half * NT2 + t));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = row0 + lg * 4 + i, dk = 16 * (half * NT2 + t) + lr;
-          qd[i] += rq_r[i] * (float)sm.sQ[r * SK + dk] * dQacc[t][i];
-          kd[i] += rk_r[i] * (float)sm.sK[r * SK + dk] * dKacc[t][i];
+          qd[i] += rq_r[i] * (float)qv[i] * dQacc[t][i];
+          kd[i] += rk_r[i] * (float)kv4[i] * dKacc[t][i];
         }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         qd[i] = row_sum16(qd[i]);
@@ -821,19 +831,23 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < NT2; ++t)
+    for (int t = 0; t < NT2; ++t) {
+      const int dk = 16 * (half * NT2 + t) + lr;
+      const bf16x4 qv = lds_tr4c(sm.sQ, SK, row0, 16 * (half * NT2 + t));
+      const bf16x4 kv4 = lds_tr4c(sm.sK, SK, row0, 16 * (half * NT2 + t));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = row0 + lg * 4 + i, dk = 16 * (half * NT2 + t) + lr;
+        const int r = row0 + lg * 4 + i;
         float dqv = dQacc[t][i], dkv = dKacc[t][i];
         if (a.l2norm) { // (rows past the chunk's end hold zeros in LDS and are not stored)
-          dqv = rq_r[i] * (dqv - rq_r[i] * (float)sm.sQ[r * SK + dk] * qd[i]);
-          dkv = rk_r[i] * (dkv - rk_r[i] * (float)sm.sK[r * SK + dk] * kd[i]);
+          dqv = rq_r[i] * (dqv - rq_r[i] * (float)qv[i] * qd[i]);
+          dkv = rk_r[i] * (dkv - rk_r[i] * (float)kv4[i] * kd[i]);
         }
         if (r >= len) continue;
         IO<TI>::store1(dqp + ((size_t)(t0 + r) * a.H + j) * D + dk, dqv);
         IO<TI>::store1(dkp + ((size_t)(t0 + r) * a.H + j) * D + dk, dkv);
       }
+    }
   }
   if (!has_next) break;
   __syncthreads(); // the epilogue's reads of K, Q, the norms and the row sums are done
@@ -868,6 +882,7 @@ static int chunk_grad_t(const Args& a, int det, hipStream_t s) {
   }
   const long items = (long)a.c_count * (det ? a.H : a.HV);
   const dim3 grid((unsigned)(items < n ? items : n));
+  hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, s, reinterpret_cast<float*>(a.gq), (size_t)1); // queue := 0
   if (det) hipLaunchKernelGGL((k_chunk_grad<D, TI, true>), grid, dim3(GRAD_THREADS), 0, s, a);
   else hipLaunchKernelGGL((k_chunk_grad<D, TI, false>), grid, dim3(GRAD_THREADS), 0, s, a);
   return (int)hipGetLastError();

@@ -78,6 +78,9 @@ struct Args {
   // middle segments (workspace), and the segments' start states (the saved set's carry plane).
   float* carry;
   float* splane;
+  // k_chunk_grad's work queue: the number of items claimed beyond the grid's first (zeroed
+  // before each launch; a launch that runs beside another has its own counter)
+  int* gq;
 };
 
 // Segmented walks of long documents (problem->segments >= 2). A document of P segments is walked
