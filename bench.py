@@ -19,10 +19,11 @@ Prints one JSON line:
                         conv1d + SiLU front-end over 10,240 packed q/k/v channels with the layer),
                         same protocol, each with its op roofline fraction
   roofline              the kernel with the longest span on the step's critical path: its
-                        algorithmic bytes (inputs, outputs, saved set) or flops per launch over
-                        its mean launch duration, HIP events recorded on the stream each launch
-                        goes to, in a separate pass; `traffic` is the committed HBM counter
-                        figure for that kernel when its source is unchanged
+                        algorithmic bytes (inputs, outputs, saved set) or flops per step over its
+                        span per step (first launch's start to last launch's end, HIP events
+                        recorded on the stream each launch goes to, in a separate pass; with one
+                        launch per step, that launch's duration); `traffic` is the committed HBM
+                        counter figure for that kernel per step when its source is unchanged
   cpu_baseline          the FP64 oracle on the host cores on a bounded sample of the same workload
                         (every document, a few q/k-head groups), fwd+bwd, fwd and checkpointed
 
@@ -153,7 +154,7 @@ def source_sha(path):
 
 
 def load_traffic(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    """HBM bytes per step from committed rocprofv3 counter runs, if the kernel is unchanged."""
     path = os.path.join(ROOT, "profiles", "pmc_%s_%s.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
@@ -162,7 +163,7 @@ def load_traffic(kernel, workload):
     src = os.path.join(ROOT, "gated_deltanet_fwd_amd", "csrc", rec.get("source", ""))
     if not os.path.exists(src) or source_sha(src) != rec.get("source_sha"):
         return None
-    return float(rec["bytes_per_launch"])
+    return float(rec["bytes_per_step"])
 
 
 def cpu_baseline(w, inputs_dev):
@@ -326,20 +327,38 @@ def summarize_mfma(pmc_dir, command):
 
 
 def summarize_trace(trace_dir, command):
-    """Per-kernel count, total and average duration from a rocprofv3 --kernel-trace CSV."""
+    """Per-kernel count, total and average duration from a rocprofv3 --kernel-trace CSV, and the
+    mean span per fwd+bwd step (first start to last end of the kernel's launches between the
+    starts of consecutive forward calls; gdn_tables opens every call, the forward's first)."""
     import statistics
     rows = _csv_rows(trace_dir, "kernel_trace.csv")
     names = _kernel_names(rows)
-    agg = {}
+    agg, iv = {}, []
     for r in rows:
         n = names[r["Kernel_Id"]] or r["Kernel_Name"][:60]
-        agg.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6)
+        s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        agg.setdefault(n, []).append((e - s) * 1e-6)
+        iv.append((s, e, n))
+    iv.sort()
+    opens = [s for s, _, n in iv if n == "gdn_tables"][::2]  # forward calls
+    spans = {}
+    for a, b in zip(opens, opens[1:] + [float("inf")]):
+        step = {}
+        for s, e, n in iv:
+            if a <= s < b:
+                lo, hi = step.get(n, (s, e))
+                step[n] = (min(lo, s), max(hi, e))
+        for n, (lo, hi) in step.items():
+            spans.setdefault(n, []).append((hi - lo) * 1e-6)
     total = sum(sum(v) for v in agg.values())
     lines = ["Command (from the repository root on one MI355X):", "", "```", command, "```", "",
-             "| kernel | calls | total ms | avg ms | median ms | % of GPU time |", "|---|---|---|---|---|---|"]
+             "| kernel | calls | total ms | avg ms | median ms | span ms/step | % of GPU time |",
+             "|---|---|---|---|---|---|---|"]
     for n, v in sorted(agg.items(), key=lambda x: -sum(x[1])):
-        lines.append("| `%s` | %d | %.3f | %.3f | %.3f | %.1f |" % (n, len(v), sum(v), sum(v) / len(v),
-                                                                  statistics.median(v), 100 * sum(v) / total))
+        sp = "%.3f" % statistics.mean(spans[n]) if n in spans and n.startswith("gdn_") else ""
+        lines.append("| `%s` | %d | %.3f | %.3f | %.3f | %s | %.1f |" % (n, len(v), sum(v), sum(v) / len(v),
+                                                                       statistics.median(v), sp,
+                                                                       100 * sum(v) / total))
     print("\n".join(lines))
 
 
@@ -528,15 +547,16 @@ def kernel_pass(lib, fn, steps):
 
 
 def roofline_of(kernels, models, workload_name, default_step):
-    """The kernel with the longest span per step (the largest block of the step's critical path;
-    kernels of a split launch plan overlap, so their summed launch time overstates it): its
-    algorithmic bytes or flops per launch over its mean launch duration, against the MI355X peak
-    that bounds it (the larger of the HBM and MFMA times at peak)."""
+    """The kernel with the longest span per step (the largest block of the step's critical path):
+    its algorithmic bytes or flops per step over its span per step, against the MI355X peak that
+    bounds it (the larger of the HBM and MFMA times at peak). With one launch per step the span is
+    that launch's duration; the launches of the two parts of a split plan overlap (and differ in
+    size), so their mean duration would misstate the time the kernel holds the step."""
     dom = max((k for k in kernels if k in models), key=lambda k: kernels[k]["span_ms_per_step"])
     kt = kernels[dom]
     per = kt["launches_per_step"]
-    by, fl, inter = (x / per for x in models[dom])
-    avg_s = kt["avg_launch_ms"] / 1e3
+    by, fl, inter = models[dom]
+    avg_s = kt["span_ms_per_step"] / 1e3
     t_hbm, t_mfma = by / PEAK_HBM, fl / PEAK_BF16
     if t_mfma > t_hbm:
         roof = {"bound": "mfma", "achieved": fl / avg_s / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s"}
@@ -546,8 +566,9 @@ def roofline_of(kernels, models, workload_name, default_step):
     traffic = load_traffic(dom, workload_name) if default_step else None
     roof["traffic"] = traffic
     roof.update({"kernel": dom, "algorithmic_bytes": by, "algorithmic_flops": fl, "intermediate_bytes": inter,
-                 "traffic_ratio": (traffic / by) if traffic else None, "avg_launch_ms": kt["avg_launch_ms"],
-                 "launches_per_step": per, "span_ms_per_step": kt["span_ms_per_step"],
+                 "traffic_ratio": (traffic / by) if traffic else None, "per": "step",
+                 "avg_launch_ms": kt["avg_launch_ms"], "launches_per_step": per,
+                 "span_ms_per_step": kt["span_ms_per_step"],
                  "mfma_frac": fl / avg_s / PEAK_BF16, "hbm_frac": by / avg_s / PEAK_HBM})
     return roof
 
@@ -635,12 +656,11 @@ def main():
     for k, v in sorted(kernels.items()):
         d = dict(v)
         if k in models:
-            per = v["launches_per_step"]
-            d.update(algorithmic_bytes_per_launch=models[k][0] / per, flops_per_launch=models[k][1] / per,
-                     intermediate_bytes_per_launch=models[k][2] / per)
+            d.update(algorithmic_bytes_per_step=models[k][0], flops_per_step=models[k][1],
+                     intermediate_bytes_per_step=models[k][2])
             tr = load_traffic(k, args.workload) if default_step else None
             if tr:
-                d.update(traffic_bytes_per_launch=tr, traffic_ratio=tr / (models[k][0] / per))
+                d.update(traffic_bytes_per_step=tr, traffic_ratio=tr / models[k][0])
         kern_out[k] = d
 
     sr = step_roofline(w.T, w.HV, w.d, io, H=w.H, NT=NT, N=w.N, has_h0=w.has_h0, want_ht=w.want_ht,

@@ -24,9 +24,16 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
 // consecutive values of one token's row. The waves never exchange data; LDS holds only the
 // chunk's shared inputs (K, Q, V, A, P and per-token factors), double-buffered, so the next chunk
 // is staged while this one computes, with one barrier per chunk.
+// 16-column value tiles per wave. Every K, Q, A, P and K^T fragment a wave reads from LDS feeds
+// one MFMA per tile, so two tiles would halve a chunk step's LDS traffic, but at one wave per
+// SIMD the step's dependent chain (K S, X, R, the state update) is no longer hidden by a second
+// wave: measured on the packed 262k-token workload, the forward took 7.5 ms with two tiles
+// against 6.05 ms with one.
+constexpr int WALK_CT = 1;
+
 template <int D>
 constexpr int walk_threads() {
-  return 64 * (D / 16);
+  return 64 * (D / (16 * WALK_CT));
 }
 
 template <int D, bool WRITE_O>
@@ -105,7 +112,8 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
   const TI* vp = (const TI*)a.v;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
-  const int v0 = 16 * w;
+  constexpr int CT = WALK_CT;
+  const int v0 = 16 * CT * w; // tile ct holds value columns v0 + 16 ct ..
   // chunk c of the piece starts at token doc_t0 + 64 (c - c_begin)
   const int doc_t0 = __builtin_amdgcn_readfirstlane(a.cu[n]) + piece_lo * CH;
   const int doc_t1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
@@ -191,23 +199,25 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
     }
   };
 
-  // ---- state: rows 16 rt + 4 lg + i (key), column v0 + lr (value)
-  f32x4 S[NRT];
+  // ---- state: rows 16 rt + 4 lg + i (key), column v0 + 16 ct + lr (value)
+  f32x4 S[CT][NRT];
   const float* s_in = SEG ? sc.s_in : a.state_in;
   // segment walks: h0 only for a document's first segment (true walk from no slot)
   const bool use_h0 = a.has_h0 && (SEG == 0 || sc.kind == 0);
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 16 * rt + 4 * lg + i;
-      if (SEG == 2 && sc.kind == 1) S[rt][i] = d == v0 + lr ? 1.f : 0.f;
-      else if (SEG == 2 && sc.kind == 2) S[rt][i] = 0.f;
-      else
-        S[rt][i] = s_in ? s_in[((size_t)h * D + d) * D + v0 + lr]
-                   : use_h0 ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr]
-                            : 0.f;
-    }
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * rt + 4 * lg + i, v = v0 + 16 * ct + lr;
+        if (SEG == 2 && sc.kind == 1) S[ct][rt][i] = d == v ? 1.f : 0.f;
+        else if (SEG == 2 && sc.kind == 2) S[ct][rt][i] = 0.f;
+        else
+          S[ct][rt][i] = s_in ? s_in[((size_t)h * D + d) * D + v]
+                         : use_h0 ? a.h0[(((size_t)n * a.HV + h) * D + d) * D + v]
+                                  : 0.f;
+      }
 
   auto step = [&](int b, int c) {
     const bf16* Kt = sm.sK[b];
@@ -224,106 +234,152 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
     const float gam = sm.sgam[b];
 
     // the state as operands in natural key order (k = key dim)
-    bf16x8 sb[KD];
+    bf16x8 sb[CT][KD];
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(S[2 * kd], S[2 * kd + 1]);
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) sb[ct][kd] = c_to_b(S[ct][2 * kd], S[ct][2 * kd + 1]);
     if (WRITE_TAPE) {
       // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
       const __amdgpu_buffer_rsrc_t tr = make_rsrc(reinterpret_cast<bf16*>(a.htape) + ((size_t)c * a.HV + h) * D * D, D * D * 2);
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) buf_store16(sb[kd], tr, ((v0 + lr) * D + 8 * lg + 32 * kd) * 2);
-    }
-    // K S (64 tokens x 16 columns) and (Q S)^T (16 columns x 64 tokens)
-    f32x4 ks[4], qsT[4];
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) ks[mt] = qsT[mt] = zero4();
+        for (int kd = 0; kd < KD; ++kd)
+          buf_store16(sb[ct][kd], tr, ((v0 + 16 * ct + lr) * D + 8 * lg + 32 * kd) * 2);
+    }
+    // K S (64 tokens x 16 columns) and (Q S)^T (16 columns x 64 tokens) of every tile
+    f32x4 ks[CT][4], qsT[CT][4];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) ks[ct][mt] = qsT[ct][mt] = zero4();
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        ks[mt] = mfma(lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg), sb[kd], ks[mt]);
-        if (WRITE_O) qsT[mt] = mfma(sb[kd], lds8(Qt, SK, 16 * mt + lr, 32 * kd + 8 * lg), qsT[mt]);
+        const bf16x8 kf = lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
+        bf16x8 qf;
+        if (WRITE_O) qf = lds8(Qt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          ks[ct][mt] = mfma(kf, sb[ct][kd], ks[ct][mt]);
+          if (WRITE_O) qsT[ct][mt] = mfma(sb[ct][kd], qf, qsT[ct][mt]);
+        }
       }
     // X = diag(beta) (V - diag(b rk) K S)
-    bf16x8 xb[2];
+    bf16x8 xb[CT][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x4 X[2];
+      f32x4 X[CT][2];
 #pragma unroll
       for (int hm = 0; hm < 2; ++hm) {
         const int mt = 2 * kt + hm, r0 = 16 * mt + 4 * lg;
         const float4 bk4 = *reinterpret_cast<const float4*>(BKs + r0);
         const float4 be4 = *reinterpret_cast<const float4*>(Bs + r0);
         const float bk[4] = {bk4.x, bk4.y, bk4.z, bk4.w}, be[4] = {be4.x, be4.y, be4.z, be4.w};
-        const bf16x4 vv = lds_tr4c(Vt, SK, 16 * mt, v0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[hm][i] = be[i] * __builtin_fmaf(-bk[i], ks[mt][i], (float)vv[i]);
+        for (int ct = 0; ct < CT; ++ct) {
+          const bf16x4 vv = lds_tr4c(Vt, SK, 16 * mt, v0 + 16 * ct);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) X[ct][hm][i] = be[i] * __builtin_fmaf(-bk[i], ks[ct][mt][i], (float)vv[i]);
+        }
       }
-      xb[kt] = pack_kp(X[0], X[1]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) xb[ct][kt] = pack_kp(X[ct][0], X[ct][1]);
     }
     // R = A X. The full saved set's v_new = R is formed a second time transposed, R^T = X^T A^T
     // (the same two fragments with their roles swapped), so that a lane holds 4 consecutive
     // values of one token's row: one 8-byte store, dropped past the chunk's end
-    f32x4 R[4];
+    f32x4 R[CT][4];
     __amdgpu_buffer_rsrc_t vr;
     if (FULL)
       vr = make_rsrc(reinterpret_cast<bf16*>(a.vnew) + ((size_t)t0 * a.HV + h) * D, ((len - 1) * a.HV * D + D) * 2);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      R[mt] = zero4();
-      f32x4 RT = zero4();
+      f32x4 RT[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) R[ct][mt] = RT[ct] = zero4();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const bf16x8 af = lds8(At, SA, 16 * mt + lr, 32 * kt + 8 * lg);
-        R[mt] = mfma(af, xb[kt], R[mt]);
-        if (FULL) RT = mfma(xb[kt], af, RT);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          R[ct][mt] = mfma(af, xb[ct][kt], R[ct][mt]);
+          if (FULL) RT[ct] = mfma(xb[ct][kt], af, RT[ct]);
+        }
       }
       if (FULL) {
-        const float x4[4] = {RT[0], RT[1], RT[2], RT[3]};
-        IO<bf16>::bstore4(vr, (16 * mt + lr) * a.HV * D + v0 + 4 * lg, x4);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const float x4[4] = {RT[ct][0], RT[ct][1], RT[ct][2], RT[ct][3]};
+          IO<bf16>::bstore4(vr, (16 * mt + lr) * a.HV * D + v0 + 16 * ct + 4 * lg, x4);
+        }
       }
     }
     // operands of R (for (P R)^T) and of diag(exp(G_last - G) rk) R (for the state update)
-    bf16x8 rb[2], rdb[2];
+    bf16x8 rb[CT][2], rdb[CT][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      if (WRITE_O) rb[kt] = pack_kp(R[2 * kt], R[2 * kt + 1]);
-      f32x4 d[2];
+      float4 dk4[2];
 #pragma unroll
-      for (int hm = 0; hm < 2; ++hm) {
-        const float4 dk4 = *reinterpret_cast<const float4*>(DKs + 16 * (2 * kt + hm) + 4 * lg);
-        d[hm][0] = dk4.x * R[2 * kt + hm][0];
-        d[hm][1] = dk4.y * R[2 * kt + hm][1];
-        d[hm][2] = dk4.z * R[2 * kt + hm][2];
-        d[hm][3] = dk4.w * R[2 * kt + hm][3];
+      for (int hm = 0; hm < 2; ++hm) dk4[hm] = *reinterpret_cast<const float4*>(DKs + 16 * (2 * kt + hm) + 4 * lg);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        if (WRITE_O) rb[ct][kt] = pack_kp(R[ct][2 * kt], R[ct][2 * kt + 1]);
+        f32x4 d[2];
+#pragma unroll
+        for (int hm = 0; hm < 2; ++hm) {
+          d[hm][0] = dk4[hm].x * R[ct][2 * kt + hm][0];
+          d[hm][1] = dk4[hm].y * R[ct][2 * kt + hm][1];
+          d[hm][2] = dk4[hm].z * R[ct][2 * kt + hm][2];
+          d[hm][3] = dk4[hm].w * R[ct][2 * kt + hm][3];
+        }
+        rdb[ct][kt] = pack_kp(d[0], d[1]);
       }
-      rdb[kt] = pack_kp(d[0], d[1]);
     }
-    // O^T = diag-column(b rq) (Q S)^T + (P R)^T; lane holds O[t][v0 + 4 lg .. +3], t = 16 mt + lr
+    // O^T = diag-column(b rq) (Q S)^T + (P R)^T; lane holds O[t][v0 + 16 ct + 4 lg .. +3],
+    // t = 16 mt + lr
     if (WRITE_O) {
       // rows of the chunk only: stores past the resource's end (tokens >= len) are dropped
       const __amdgpu_buffer_rsrc_t orr = make_rsrc((TI*)a.o + ((size_t)t0 * a.HV + h) * D,
                                                    ((len - 1) * a.HV * D + D) * (int)sizeof(TI));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc = zero4();
+        f32x4 acc[CT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) acc = mfma(rb[kt], lds8(Pt, SA, 16 * mt + lr, 32 * kt + 8 * lg), acc);
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = zero4();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 pf = lds8(Pt, SA, 16 * mt + lr, 32 * kt + 8 * lg);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma(rb[ct][kt], pf, acc[ct]);
+        }
         const int t = 16 * mt + lr;
         const float sq = BQs[t];
-        float ov[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = __builtin_fmaf(sq, qsT[mt][i], acc[i]);
-        IO<TI>::bstore4(orr, t * a.HV * D + v0 + 4 * lg, ov);
+        for (int ct = 0; ct < CT; ++ct) {
+          float ov[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = __builtin_fmaf(sq, qsT[ct][mt][i], acc[ct][i]);
+          IO<TI>::bstore4(orr, t * a.HV * D + v0 + 16 * ct + 4 * lg, ov);
+        }
       }
     }
     // S <- gamma S + K^T diag(exp(G_last - G) rk) R
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      f32x4 acc = S[rt] * gam;
+      f32x4 acc[CT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) acc = mfma(lds_tr_kp(Kt, SK, 32 * kt, 16 * rt), rdb[kt], acc);
-      S[rt] = acc;
+      for (int ct = 0; ct < CT; ++ct) acc[ct] = S[ct][rt] * gam;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 kT = lds_tr_kp(Kt, SK, 32 * kt, 16 * rt);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma(kT, rdb[ct][kt], acc[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) S[ct][rt] = acc[ct];
     }
   };
 
@@ -346,18 +402,23 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
   float* s_out = SEG ? sc.s_out : a.state_out;
   if (s_out) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_out[((size_t)h * D + 16 * rt + 4 * lg + i) * D + v0 + lr] = S[rt][i];
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_out[((size_t)h * D + 16 * rt + 4 * lg + i) * D + v0 + 16 * ct + lr] = S[ct][rt][i];
   }
   if (WRITE_O && a.want_ht && (SEG == 0 || sc.write_ht)) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 16 * rt + 4 * lg + i;
-        a.ht[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] = S[rt][i];
-      }
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * rt + 4 * lg + i;
+          a.ht[(((size_t)n * a.HV + h) * D + d) * D + v0 + 16 * ct + lr] = S[ct][rt][i];
+        }
   }
 }
 
@@ -370,7 +431,7 @@ __device__ __forceinline__ void walk_fwd_body(const Args& a, int blk, WalkSmem<D
 // P^T and per-token factors), one barrier per chunk.
 template <int D>
 constexpr int bwalk_threads() {
-  return 64 * (D / 16);
+  return 64 * (D / (16 * WALK_CT));
 }
 
 template <int D>
@@ -408,7 +469,8 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
   const TI* dop = (const TI*)a.dO;
   const bf16* akk = reinterpret_cast<const bf16*>(a.akk);
   const bf16* pm = reinterpret_cast<const bf16*>(a.qk);
-  const int v0 = 16 * w;
+  constexpr int CT = WALK_CT;
+  const int v0 = 16 * CT * w; // tile ct holds value columns v0 + 16 ct ..
   const int doc_t0 = __builtin_amdgcn_readfirstlane(a.cu[n]), doc_t1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
 
   // staging through buffer resources bounded at the chunk's last row, at per-lane offsets fixed
@@ -491,14 +553,16 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
     }
   };
 
-  f32x4 dS[NRT];
+  f32x4 dS[CT][NRT];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 16 * rt + 4 * lg + i;
-      dS[rt][i] = a.dht ? a.dht[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] : 0.f;
-    }
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * rt + 4 * lg + i;
+        dS[ct][rt][i] = a.dht ? a.dht[(((size_t)n * a.HV + h) * D + d) * D + v0 + 16 * ct + lr] : 0.f;
+      }
 
   auto step = [&](int b, int c) {
     const bf16* Kt = sm.sK[b];
@@ -510,69 +574,108 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
     const float* YKs = sm.sc[b][1];
     const float gam = sm.sgam[b];
 
-    bf16x8 sb[KD];
+    bf16x8 sb[CT][KD];
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd) sb[kd] = c_to_b(dS[2 * kd], dS[2 * kd + 1]);
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) sb[ct][kd] = c_to_b(dS[ct][2 * kd], dS[ct][2 * kd + 1]);
     {
       // tape[v][k]: this lane's column, key rows 32 kd + 8 lg .. +7
       const __amdgpu_buffer_rsrc_t tr = make_rsrc(reinterpret_cast<bf16*>(a.dstape) + ((size_t)c * a.HV + h) * D * D, D * D * 2);
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) buf_store16(sb[kd], tr, ((v0 + lr) * D + 8 * lg + 32 * kd) * 2);
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd)
+          buf_store16(sb[ct][kd], tr, ((v0 + 16 * ct + lr) * D + 8 * lg + 32 * kd) * 2);
     }
     // dO as operands (k = tokens), shared by P^T dO and (Q')^T dO
-    bf16x8 db[2];
+    bf16x8 db[CT][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) db[kt] = lds_tr_kp(Dt, SK, 32 * kt, v0);
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) db[ct][kt] = lds_tr_kp(Dt, SK, 32 * kt, v0 + 16 * ct);
     // dR = P^T dO + diag(exp(G_last - G) rk) K dS
-    bf16x8 drb[2];
+    bf16x8 drb[CT][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x4 dR[2];
+      f32x4 dR[CT][2];
 #pragma unroll
       for (int hm = 0; hm < 2; ++hm) {
         const int mt = 2 * kt + hm;
-        f32x4 kd_ = zero4(), pd = zero4();
+        f32x4 kd_[CT], pd[CT];
 #pragma unroll
-        for (int kd = 0; kd < KD; ++kd) kd_ = mfma(lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg), sb[kd], kd_);
+        for (int ct = 0; ct < CT; ++ct) kd_[ct] = pd[ct] = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) pd = mfma(lds8(PTt, SA, 16 * mt + lr, 32 * k2 + 8 * lg), db[k2], pd);
+        for (int kd = 0; kd < KD; ++kd) {
+          const bf16x8 kf = lds8(Kt, SK, 16 * mt + lr, 32 * kd + 8 * lg);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) kd_[ct] = mfma(kf, sb[ct][kd], kd_[ct]);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const bf16x8 pf = lds8(PTt, SA, 16 * mt + lr, 32 * k2 + 8 * lg);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) pd[ct] = mfma(pf, db[ct][k2], pd[ct]);
+        }
         const float4 dk4 = *reinterpret_cast<const float4*>(DKs + 16 * mt + 4 * lg);
-        dR[hm][0] = __builtin_fmaf(dk4.x, kd_[0], pd[0]);
-        dR[hm][1] = __builtin_fmaf(dk4.y, kd_[1], pd[1]);
-        dR[hm][2] = __builtin_fmaf(dk4.z, kd_[2], pd[2]);
-        dR[hm][3] = __builtin_fmaf(dk4.w, kd_[3], pd[3]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          dR[ct][hm][0] = __builtin_fmaf(dk4.x, kd_[ct][0], pd[ct][0]);
+          dR[ct][hm][1] = __builtin_fmaf(dk4.y, kd_[ct][1], pd[ct][1]);
+          dR[ct][hm][2] = __builtin_fmaf(dk4.z, kd_[ct][2], pd[ct][2]);
+          dR[ct][hm][3] = __builtin_fmaf(dk4.w, kd_[ct][3], pd[ct][3]);
+        }
       }
-      drb[kt] = pack_kp(dR[0], dR[1]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) drb[ct][kt] = pack_kp(dR[ct][0], dR[ct][1]);
     }
     // -Y' = -diag(beta b rk) A^T dR
-    bf16x8 yb[2];
+    bf16x8 yb[CT][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x4 Y[2];
+      f32x4 Y[CT][2];
 #pragma unroll
       for (int hm = 0; hm < 2; ++hm) {
         const int mt = 2 * kt + hm;
-        f32x4 acc = zero4();
+        f32x4 acc[CT];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) acc = mfma(lds_tr_kp(At, SA, 32 * k2, 16 * mt), drb[k2], acc);
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = zero4();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const bf16x8 aT = lds_tr_kp(At, SA, 32 * k2, 16 * mt);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma(aT, drb[ct][k2], acc[ct]);
+        }
         const float4 y4 = *reinterpret_cast<const float4*>(YKs + 16 * mt + 4 * lg);
-        Y[hm][0] = y4.x * acc[0];
-        Y[hm][1] = y4.y * acc[1];
-        Y[hm][2] = y4.z * acc[2];
-        Y[hm][3] = y4.w * acc[3];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          Y[ct][hm][0] = y4.x * acc[ct][0];
+          Y[ct][hm][1] = y4.y * acc[ct][1];
+          Y[ct][hm][2] = y4.z * acc[ct][2];
+          Y[ct][hm][3] = y4.w * acc[ct][3];
+        }
       }
-      yb[kt] = pack_kp(Y[0], Y[1]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) yb[ct][kt] = pack_kp(Y[ct][0], Y[ct][1]);
     }
     // dS <- gamma dS + (Q')^T dO - K^T Y'
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      f32x4 acc = dS[rt] * gam;
+      f32x4 acc[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] = dS[ct][rt] * gam;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        acc = mfma(lds_tr_kp(Qt, SK, 32 * kt, 16 * rt), db[kt], acc);
-        acc = mfma(lds_tr_kp(Kt, SK, 32 * kt, 16 * rt), yb[kt], acc);
+        const bf16x8 qT = lds_tr_kp(Qt, SK, 32 * kt, 16 * rt);
+        const bf16x8 kT = lds_tr_kp(Kt, SK, 32 * kt, 16 * rt);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          acc[ct] = mfma(qT, db[ct][kt], acc[ct]);
+          acc[ct] = mfma(kT, yb[ct][kt], acc[ct]);
+        }
       }
-      dS[rt] = acc;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) dS[ct][rt] = acc[ct];
     }
   };
 
@@ -593,12 +696,14 @@ __device__ __forceinline__ void walk_bwd_body(const Args& a, int blk, BWalkSmem<
   }
   if (a.dh0) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 16 * rt + 4 * lg + i;
-        a.dh0[(((size_t)n * a.HV + h) * D + d) * D + v0 + lr] = dS[rt][i];
-      }
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * rt + 4 * lg + i;
+          a.dh0[(((size_t)n * a.HV + h) * D + d) * D + v0 + 16 * ct + lr] = dS[ct][rt][i];
+        }
   }
 }
 
