@@ -124,9 +124,10 @@ typedef struct gdn_problem {
  * HV = 48, d = 128, all chunks full). 0 if the problem is invalid (see gdn_last_error). */
 size_t gdn_saved_bytes(const gdn_problem* p);
 
-/* Bytes of device workspace one call of `op` needs: chunk tables, inverse q/k norms, the
- * per-value-head decayed q.k tiles, the replayed state tape and the end-state-gradient tape
- * (backward), FP32 dq/dk accumulators (atomic reduction), the segment carry states. The
+/* Bytes of device workspace one call of `op` needs: chunk tables, the status word, inverse q/k
+ * norms, the per-value-head decayed q.k tiles, the replayed state tape, the end-state-gradient
+ * tape and the chunk-gradient work-queue counters (backward), FP32 dq/dk accumulators (atomic
+ * reduction), the segment carry states. The
  * pages' byte queries (flashinfer PR #8172 description: saved, workspace and communication
  * byte-accounting APIs) are the model. 0 if the problem is invalid. */
 size_t gdn_workspace_bytes(const gdn_problem* p, int op);
