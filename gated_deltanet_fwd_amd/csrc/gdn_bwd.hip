@@ -508,8 +508,12 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         if (dvl < DC) {
           *reinterpret_cast<bf16x8*>(B.sS + dvl * SK + pc * 8) = nS;
           *reinterpret_cast<bf16x8*>(B.sdS + dvl * SK + pc * 8) = ndS;
+          // <dSn, S> of this piece: bf16 pair products (exact in f32) summed two at a time
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          struct Pairs { bf16x2_t p[4]; };
+          const Pairs ps = __builtin_bit_cast(Pairs, nS), pd = __builtin_bit_cast(Pairs, ndS);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sdot += (float)nS[e] * (float)ndS[e];
+          for (int e = 0; e < 4; ++e) sdot = __builtin_amdgcn_fdot2_f32_bf16(ps.p[e], pd.p[e], sdot, false);
         }
         const int u = tid & 255, r = u >> 2, pv = u & 3;
         const bf16x8 xv = r < len ? nx : zero8();
