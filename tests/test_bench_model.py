@@ -60,3 +60,22 @@ def test_kernel_models_count_no_intermediates_as_algorithmic():
     # in the kept-tape form the chunk-gradient kernel's read of the state tape is a saved-set read
     mt = bench.kernel_models(T, NT, N, H, HV, d, io, save_mode="tape")
     assert mt["gdn_chunk_grad"][0] == m["gdn_chunk_grad"][0] + tape
+
+
+def test_roofline_is_bytes_per_step_over_span():
+    """The dominant kernel is the one with the longest span per step; its achieved rate is its
+    algorithmic bytes per step over that span, whether it ran as one launch or as two overlapping
+    launches of different sizes (whose mean duration would misstate the time it holds the step)."""
+    models = {"gdn_chunk_grad": (15.77e9, 4.05e12, 14.5e9), "gdn_walk_pair": (13.09e9, 2.68e12, 14.5e9)}
+    two = {"gdn_chunk_grad": {"launches_per_step": 2.0, "sum_ms_per_step": 14.7, "span_ms_per_step": 10.5,
+                              "avg_launch_ms": 7.35},
+           "gdn_walk_pair": {"launches_per_step": 2.0, "sum_ms_per_step": 13.9, "span_ms_per_step": 7.4,
+                             "avg_launch_ms": 6.95}}
+    r = bench.roofline_of(two, models, "no-such-workload", False)
+    assert r["kernel"] == "gdn_chunk_grad" and r["bound"] == "hbm" and r["per"] == "step"
+    assert abs(r["achieved"] - 15.77e9 / 10.5e-3 / 1e9) < 1e-6
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-12
+    assert r["traffic"] is None and r["traffic_ratio"] is None
+    one = {"gdn_chunk_grad": {"launches_per_step": 1.0, "sum_ms_per_step": 10.5, "span_ms_per_step": 10.5,
+                              "avg_launch_ms": 10.5}}
+    assert abs(bench.roofline_of(one, models, "no-such-workload", False)["achieved"] - r["achieved"]) < 1e-9
