@@ -610,7 +610,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (it would shard the "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (it would shard the "
               "q/k-head groups or the sequence across GPUs)", file=sys.stderr)
         sys.exit(2)
 
