@@ -140,6 +140,21 @@ def test_edge_cases(w, det):
     _check_all(w, inp, out)
 
 
+# More documents than the chunk tables order by length (above 8,192 they keep the identity order,
+# the paired walks alternate their two kinds, and neither the two-part plan nor segments apply):
+# 9,000 documents of 0..24 tokens (395 empty), every element compared.
+MANY = syn.custom("many_docs", np.random.default_rng(21).integers(0, 25, size=9000).tolist(), 1, 2, 64, "bf16",
+                  seed=21)
+
+
+@pytest.mark.parametrize("det", [True, False])
+def test_many_documents_identity_order(det):
+    assert MANY.N > 8192
+    inp = _dev(syn.make_inputs(MANY))
+    out = _run(MANY, inp, det=det)
+    _check_all(MANY, inp, out)
+
+
 def _saved_regions(w, full):
     """Byte offsets of the saved set's regions: a 256-byte tag, then each region aligned to 256."""
     NT = sum((L + 63) // 64 for L in w.lengths)
