@@ -648,7 +648,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + lg * 4 + i;
-        const bool lo = r >= cc;
+        // rows past the chunk's end are masked too: their G is staged as 0, so exp(G_r - G_c) may
+        // overflow there, and an infinite factor would turn their zero dP into NaN
+        const bool lo = r >= cc && r < len;
         gm[c2][i] = keepf(__expf(g_r[i] - g_c), lo);
         const float dqk = lo ? dP[c2][i] * gm[c2][i] : 0.f;
         dgam[c2][i] = lo ? dP[c2][i] * Qk[i] : 0.f;

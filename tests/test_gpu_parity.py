@@ -103,6 +103,25 @@ def test_tiny(det, mode):
     _check_all(w, inp, out)
 
 
+@pytest.mark.parametrize("det", [True, False])
+@pytest.mark.parametrize("mode", [G.SAVE_LIGHT, G.SAVE_FULL])
+def test_strong_decay(det, mode):
+    """Log decays far below the pages' distribution: about -4 per token, some tokens at 0 (no
+    decay) and some at -80, so the in-chunk cumulative gates reach hundreds and their exponentials
+    span the whole f32 range (underflowing to zero) inside the chunk."""
+    w = syn.custom("strong_decay", [200, 77, 130], 2, 6, 128, "bf16", has_h0=True, want_ht=True, has_dht=True,
+                   seed=17)
+    inp = syn.make_inputs(w)
+    gen = torch.Generator().manual_seed(171)
+    g = torch.nn.functional.logsigmoid(torch.randn(w.T, w.HV, generator=gen) - 4.0)
+    pick = torch.rand(w.T, w.HV, generator=gen)
+    g = torch.where(pick < 0.1, torch.zeros_like(g), torch.where(pick > 0.95, torch.full_like(g, -80.0), g))
+    inp["g"] = g.float()
+    inp = _dev(inp)
+    out = _run(w, inp, save_mode=mode, det=det)
+    _check_all(w, inp, out)
+
+
 def test_tiny_prenormalised_without_kernel_norm():
     """q, k L2-normalised on the host (same eps), kernel norm off: matches the oracle with the norm off."""
     w = syn.WORKLOADS["tiny"]
