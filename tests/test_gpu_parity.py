@@ -122,6 +122,20 @@ def test_strong_decay(det, mode):
     _check_all(w, inp, out)
 
 
+@pytest.mark.parametrize("det", [True, False])
+def test_no_decay_full_updates(det):
+    """g = 0 and beta = 1 on every token (no forgetting, full delta-rule updates) over a 2,000-token
+    document and a short one: the state keeps every chunk's contribution, the longest memory the
+    method allows."""
+    w = syn.custom("no_decay", [2000, 150], 2, 6, 128, "bf16", has_h0=True, want_ht=True, has_dht=True, seed=19)
+    inp = syn.make_inputs(w)
+    inp["g"] = torch.zeros_like(inp["g"])
+    inp["beta"] = torch.ones_like(inp["beta"])
+    inp = _dev(inp)
+    out = _run(w, inp, det=det)
+    _check_all(w, inp, out)
+
+
 def test_tiny_prenormalised_without_kernel_norm():
     """q, k L2-normalised on the host (same eps), kernel norm off: matches the oracle with the norm off."""
     w = syn.WORKLOADS["tiny"]
