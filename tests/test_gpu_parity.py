@@ -162,6 +162,9 @@ EDGE = [
     # intra and walk launches run apart from the others', whose chunk range wraps around it
     syn.custom("split_mid", [700, 5000, 129, 1000], 2, 6, 128, "bf16", has_h0=True, want_ht=True, has_dht=True,
                seed=13),
+    # the same two-part plan at d = 64 with f32 inputs, the longest document first
+    syn.custom("split_d64_f32", [6000, 700, 65, 1200], 2, 4, 64, "f32", has_h0=True, want_ht=True, has_dht=True,
+               seed=14),
 ]
 
 
@@ -260,6 +263,17 @@ def test_split_launch_light_full_recompute_bitwise():
     assert torch.equal(b["saved"], b["saved_recompute"])
     for k in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("det", [True, False])
+def test_split_plan_d64_f32(det):
+    """The two-part launch plan (the longest document's intra pass, walks and chunk gradients on the
+    caller's stream, the others' on the auxiliary stream, each chunk-gradient part with its own
+    work queue) at d = 64 with f32 inputs, against the oracle."""
+    w = [x for x in EDGE if x.name == "split_d64_f32"][0]
+    inp = _dev(syn.make_inputs(w))
+    out = _run(w, inp, det=det, segments=1)
+    _check_all(w, inp, out)
 
 
 def test_split_walk_in_pieces():
