@@ -144,3 +144,29 @@ def test_single8k_segmented_full_size():
     inp = syn.make_inputs(w, device=DEV)
     out = _run(w, inp, 8, bwd=False)
     _check(w, inp, out, bwd=False)
+
+
+def _regime(inp, kind):
+    """Decay regimes outside the pages' distribution: 'strong' (log decays about -4 per token, 10 %
+    of tokens at 0 and 5 % at -80: the transfer maps of a segment vanish) or 'none' (g = 0 and
+    beta = 1 everywhere: the maps are products of projections, no forgetting)."""
+    if kind == "none":
+        inp["g"] = torch.zeros_like(inp["g"])
+        inp["beta"] = torch.ones_like(inp["beta"])
+        return inp
+    gen = torch.Generator().manual_seed(172)
+    g = torch.nn.functional.logsigmoid(torch.randn(inp["g"].shape, generator=gen) - 4.0)
+    pick = torch.rand(inp["g"].shape, generator=gen)
+    inp["g"] = torch.where(pick < 0.1, torch.zeros_like(g), torch.where(pick > 0.95, torch.full_like(g, -80.0), g))
+    return inp
+
+
+@pytest.mark.parametrize("kind", ["strong", "none"])
+def test_segmented_decay_regimes(kind):
+    """Segmented walks (transfer walks, carry merge, segment re-walks, the light backward's replay
+    from the carry plane) under vanishing and under absent decay, against the oracle."""
+    w = syn.custom("seg_regime", [3000, 200, 1500], 1, 3, 128, "bf16", has_h0=True, want_ht=True, has_dht=True,
+                   seed=63)
+    inp = _dev(_regime(syn.make_inputs(w), kind))
+    out = _run(w, inp, 4)
+    _check(w, inp, out)
