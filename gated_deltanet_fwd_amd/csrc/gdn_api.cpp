@@ -741,6 +741,10 @@ int gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, c
   uint64_t words[4];
   tag_words(p, words);
   LAUNCH("gdn_tables", gdn::launch_tables(a, (const uint64_t*)saved, words, stream));
+  // the chunk-gradient launches' work-queue counters, cleared here, ahead of every launch that
+  // may run beside them: a one-wave launch queued between a running chunk-gradient launch and
+  // the next would wait for a workgroup of the running one to exit (they hold every register)
+  LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(reinterpret_cast<float*>(a.gq), 2, stream));
   if (!p->deterministic) { // accumulators of the atomic dq, dk reduction
     LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dqacc, (size_t)s.T * s.H * s.D, stream));
     LAUNCH("gdn_fill_zero", gdn::launch_fill_zero(a.dkacc, (size_t)s.T * s.H * s.D, stream));

@@ -260,7 +260,10 @@ int launch_walk_bwd(const Args& a, void* stream) {
 // 8 waves: wave w owns rows 16*(w%4).. of every 64-row product and half w/4 of its columns.
 // The state and adjoint tapes stream through LDS in 32-column value slices (the next slice is
 // prefetched into registers); every tile is stored once and read in the other orientation with
-// transpose-reads. The value-dimension contractions feed dQh and dKh directly through row-scaled
+// transpose-reads. Products that have a transpose-read operand take both operands in the
+// k-permuted order (lds_tr_kp, lds_kp, or a tile whose columns are stored permuted): its
+// transpose-reads touch 8 consecutive rows per 32 lanes, which the padded row strides spread over
+// all LDS banks, where the plain order's rows r and r + 8 share banks. The value-dimension contractions feed dQh and dKh directly through row-scaled
 // A fragments: diag(b) dO S^T, diag(exp(G_last - G)) R dSn^T and -diag(beta b) dX S^T.
 constexpr int GRAD_THREADS = 512;
 constexpr int GRAD_MAXG = 8; // value heads per q/k head whose dg, dbeta wait in LDS (more: stored per head)
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
   auto store_head = [&](int len, int tid) {
     const int r = tid >> 3, pc = tid & 7;
     *reinterpret_cast<bf16x8*>(sm.sA + r * SA + pc * 8) = keep8(nA, r < len);
-    *reinterpret_cast<bf16x8*>(sm.sP + r * SA + pc * 8) = keep8(nP, r < len);
+    lds_store_kp8(sm.sP, SA, r, pc, keep8(nP, r < len)); // k-permuted columns: lds8 reads P . dO operands
     if (tid < 2 * CH) (tid < CH ? sm.sG : sm.sB)[tid & 63] = keepf(nGB, (tid & 63) < len);
   };
   auto prefetch_head = [&](int c, int t0, int len, int h, int tid) {
@@ -482,6 +485,9 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     if (DET) asm volatile("" : "+v"(tid_o));
     const int tid = tid_o, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), rt = w & 3, half = w >> 2, row0 = 16 * rt, arow = row0 + lr;
+    // column of this lane's 4 C rows in a tile whose columns are kept k-permuted (lds_store_kp8's
+    // order), so that lds8 row reads of it pair with k-permuted transpose reads
+    const int kpcol = 32 * (rt >> 1) + 8 * lg + 4 * (rt & 1);
     __syncthreads(); // this head's A, P, G and beta are staged
     const float glast = sm.sG[len - 1];
     // per-row factors: this lane's C rows (r) and A-fragment row (arow)
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         kdv = mfma(fk, lds8(B.sdS, SK, cs + lr, ks * 32 + lg * 8), kdv);
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) pdv = mfma(lds8(sm.sP, SA, arow, k2 * 32 + lg * 8), lds_tr8(B.sdO, SDO, k2 * 32, cs), pdv);
+      for (int k2 = 0; k2 < 2; ++k2) pdv = mfma(lds8(sm.sP, SA, arow, k2 * 32 + lg * 8), lds_tr_kp(B.sdO, SDO, k2 * 32, cs), pdv);
       float xu[4], x[4], dr[4];
       const f32x4 rk_r = rk4();
       const bf16x4 vv = lds_tr4c(B.sV, SV, row0, cs);
@@ -579,24 +585,24 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       __syncthreads();
 
       // value-dimension contractions over this slice (32 = one MFMA k-step)
-      const bf16x8 aO = lds8(B.sdO, SDO, arow, lg * 8);
+      const bf16x8 aO = lds_kp(B.sdO, SDO, arow, 0);
       const bf16x8 aOb = scale8(aO, a_b);
-      const bf16x8 aR = lds_tr8(B.sRTd, SA, 0, row0);
-      const bf16x8 aX = lds_tr8(B.sdXT, SA, 0, row0);
+      const bf16x8 aR = lds_tr_kp(B.sRTd, SA, 0, row0);
+      const bf16x8 aX = lds_tr_kp(B.sdXT, SA, 0, row0);
 #pragma unroll
       for (int t = 0; t < NT2; ++t) {
         const int dcol = 16 * (half * NT2 + t);
-        const bf16x8 bS = lds_tr8(B.sS, SK, 0, dcol);
+        const bf16x8 bS = lds_tr_kp(B.sS, SK, 0, dcol);
         dQacc[t] = mfma(aOb, bS, dQacc[t]);
         dKacc[t] = mfma(aX, bS, dKacc[t]);
-        dKacc[t] = mfma(aR, lds_tr8(B.sdS, SK, 0, dcol), dKacc[t]);
+        dKacc[t] = mfma(aR, lds_tr_kp(B.sdS, SK, 0, dcol), dKacc[t]);
       }
-      const bf16x8 adR = lds_tr8(B.sdRT, SA, 0, row0);
+      const bf16x8 adR = lds_tr_kp(B.sdRT, SA, 0, row0);
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const int ct = 2 * half + c2;
-        dP[c2] = mfma(aO, lds_tr8(B.sRT, SA, 0, 16 * ct), dP[c2]);
-        dA[c2] = mfma(adR, lds_tr8(B.sXT, SA, 0, 16 * ct), dA[c2]);
+        dP[c2] = mfma(aO, lds_tr_kp(B.sRT, SA, 0, 16 * ct), dP[c2]);
+        dA[c2] = mfma(adR, lds_tr_kp(B.sXT, SA, 0, 16 * ct), dA[c2]);
       }
     }
 
@@ -659,7 +665,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
         t3[i] = dA[c2][i];
       }
       lds_store4_t(T.sT1t, SA, cc, row0 + lg * 4, t1[0], t1[1], t1[2], t1[3]); // (dQk rk)^T
-      lds_store4_t(T.sT2, SA, cc, row0 + lg * 4, t2[0], t2[1], t2[2], t2[3]);  // (dQk rq)^T
+      lds_store4_t(T.sT2, SA, cc, kpcol, t2[0], t2[1], t2[2], t2[3]);          // (dQk rq)^T
       lds_store4_t(T.sT3, SA, cc, row0 + lg * 4, t3[0], t3[1], t3[2], t3[3]);  // dA^T
     }
     __syncthreads();
@@ -677,7 +683,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int ct = 2 * half + c2;
-      lds_store4_t(T.sT3, SA, 16 * ct + lr, row0 + lg * 4, m1[c2][0], m1[c2][1], m1[c2][2], m1[c2][3]); // M1^T
+      lds_store4_t(T.sT3, SA, 16 * ct + lr, kpcol, m1[c2][0], m1[c2][1], m1[c2][2], m1[c2][3]); // M1^T
     }
     __syncthreads();
     // dL = -A^T M1 (strictly lower); dKk = dL o (beta Gam) goes to two tiles, one per term of
@@ -693,7 +699,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
-        acc = mfma(lds_tr8(sm.sA, SA, k2 * 32, row0), lds8(T.sT3, SA, 16 * ct + lr, k2 * 32 + lg * 8), acc);
+        acc = mfma(lds_tr_kp(sm.sA, SA, k2 * 32, row0), lds8(T.sT3, SA, 16 * ct + lr, k2 * 32 + lg * 8), acc);
       float e1[4], e2[4], csum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -711,7 +717,7 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
       csum = col_sum4(csum);
       if (lg == 0) sm.sCol[rt][cc] = csum;
       lds_store4_t(T.sE1t, SA, cc, row0 + lg * 4, e1[0], e1[1], e1[2], e1[3]);
-      lds_store4_t(T.sE2, SA, cc, row0 + lg * 4, e2[0], e2[1], e2[2], e2[3]);
+      lds_store4_t(T.sE2, SA, cc, kpcol, e2[0], e2[1], e2[2], e2[3]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -728,18 +734,18 @@ __global__ __launch_bounds__(GRAD_THREADS) void k_chunk_grad(Args a) {
     __syncthreads();
     // dQh += (dQk rk) K ; dKh += (dQk rq)^T Q + (dKs rk) K
     {
-      const bf16x8 a1[2] = {lds_tr8(T.sT1t, SA, 0, row0), lds_tr8(T.sT1t, SA, 32, row0)};
+      const bf16x8 a1[2] = {lds_tr_kp(T.sT1t, SA, 0, row0), lds_tr_kp(T.sT1t, SA, 32, row0)};
       const bf16x8 a2[2] = {lds8(T.sT2, SA, arow, lg * 8), lds8(T.sT2, SA, arow, 32 + lg * 8)};
-      const bf16x8 e1[2] = {lds_tr8(T.sE1t, SA, 0, row0), lds_tr8(T.sE1t, SA, 32, row0)};
+      const bf16x8 e1[2] = {lds_tr_kp(T.sE1t, SA, 0, row0), lds_tr_kp(T.sE1t, SA, 32, row0)};
       const bf16x8 e2[2] = {lds8(T.sE2, SA, arow, lg * 8), lds8(T.sE2, SA, arow, 32 + lg * 8)};
 #pragma unroll
       for (int t = 0; t < NT2; ++t) {
         const int dcol = 16 * (half * NT2 + t);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const bf16x8 bK = lds_tr8(sm.sK, SK, k2 * 32, dcol);
+          const bf16x8 bK = lds_tr_kp(sm.sK, SK, k2 * 32, dcol);
           dQacc[t] = mfma(a1[k2], bK, dQacc[t]);
-          dKacc[t] = mfma(a2[k2], lds_tr8(sm.sQ, SK, k2 * 32, dcol), dKacc[t]);
+          dKacc[t] = mfma(a2[k2], lds_tr_kp(sm.sQ, SK, k2 * 32, dcol), dKacc[t]);
           dKacc[t] = mfma(e1[k2], bK, dKacc[t]);
           dKacc[t] = mfma(e2[k2], bK, dKacc[t]);
         }
@@ -888,7 +894,6 @@ static int chunk_grad_t(const Args& a, int det, hipStream_t s) {
   }
   const long items = (long)a.c_count * (det ? a.H : a.HV);
   const dim3 grid((unsigned)(items < n ? items : n));
-  hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, s, reinterpret_cast<float*>(a.gq), (size_t)1); // queue := 0
   if (det) hipLaunchKernelGGL((k_chunk_grad<D, TI, true>), grid, dim3(GRAD_THREADS), 0, s, a);
   else hipLaunchKernelGGL((k_chunk_grad<D, TI, false>), grid, dim3(GRAD_THREADS), 0, s, a);
   return (int)hipGetLastError();

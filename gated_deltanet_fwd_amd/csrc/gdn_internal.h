@@ -78,8 +78,8 @@ struct Args {
   // middle segments (workspace), and the segments' start states (the saved set's carry plane).
   float* carry;
   float* splane;
-  // k_chunk_grad's work queue: the number of items claimed beyond the grid's first (zeroed
-  // before each launch; a launch that runs beside another has its own counter)
+  // k_chunk_grad's work queue: the number of items claimed beyond the grid's first (zeroed once
+  // per call, after the tables kernel; a launch that runs beside another has its own counter)
   int* gq;
 };
 
