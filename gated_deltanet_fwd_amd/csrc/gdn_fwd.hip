@@ -12,6 +12,8 @@
 // workgroup per (document, value head, value-column tile) and walks that document's chunks in
 // order, keeping its FP32 state tile in registers. Every contraction is a bf16 MFMA with FP32
 // accumulation; the state is rounded to bf16 only as an MFMA operand.
+#include <type_traits>
+
 #include "gdn_walks.h"
 
 namespace gdn {
@@ -180,29 +182,55 @@ __global__ __launch_bounds__(NTHREADS, 3) void k_intra(Args a) {
   const int ar = 16 * w + lr;
   const bool ok = ar < len;
   const size_t roff = ((size_t)(t0 + min(ar, len - 1)) * a.H + j) * D + lg * 8;
-  float kf[KS][8], qf[KS][8];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    IO<TI>::load8f(kp + roff + ks * 32, kf[ks]);
-    IO<TI>::load8f(qp + roff + ks * 32, qf[ks]);
-  }
   unsigned okm = ok ? ~0u : 0u;
   asm volatile("" : "+v"(okm));
   bf16x8 fk[KS], fq[KS];
   float ssk = 0.f, ssq = 0.f;
+  if constexpr (std::is_same<TI, bf16>::value) {
+    // bf16 rows stay packed: masked as 32-bit words, and the squared norms summed from exact
+    // products of bf16 pairs, two per instruction (v_dot2_f32_bf16)
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    struct Pairs { bf16x2_t p[4]; };
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float kv = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, kf[ks][e]) & okm);
-      const float qv = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, qf[ks][e]) & okm);
-      ssk += kv * kv;
-      ssq += qv * qv;
-      fk[ks][e] = (bf16)kv;
-      fq[ks][e] = (bf16)qv;
+    for (int ks = 0; ks < KS; ++ks) {
+      fk[ks] = IO<TI>::load8(kp + roff + ks * 32);
+      fq[ks] = IO<TI>::load8(qp + roff + ks * 32);
     }
-    *reinterpret_cast<bf16x8*>(u.kq.k + ar * SK + ks * 32 + lg * 8) = fk[ks];
-    *reinterpret_cast<bf16x8*>(u.kq.q + ar * SK + ks * 32 + lg * 8) = fq[ks];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      fk[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, fk[ks]) & okm);
+      fq[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, fq[ks]) & okm);
+      const Pairs pk = __builtin_bit_cast(Pairs, fk[ks]), pq = __builtin_bit_cast(Pairs, fq[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ssk = __builtin_amdgcn_fdot2_f32_bf16(pk.p[e], pk.p[e], ssk, false);
+        ssq = __builtin_amdgcn_fdot2_f32_bf16(pq.p[e], pq.p[e], ssq, false);
+      }
+      *reinterpret_cast<bf16x8*>(u.kq.k + ar * SK + ks * 32 + lg * 8) = fk[ks];
+      *reinterpret_cast<bf16x8*>(u.kq.q + ar * SK + ks * 32 + lg * 8) = fq[ks];
+    }
+  } else {
+    float kf[KS][8], qf[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      IO<TI>::load8f(kp + roff + ks * 32, kf[ks]);
+      IO<TI>::load8f(qp + roff + ks * 32, qf[ks]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kv = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, kf[ks][e]) & okm);
+        const float qv = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, qf[ks][e]) & okm);
+        ssk += kv * kv;
+        ssq += qv * qv;
+        fk[ks][e] = (bf16)kv;
+        fq[ks][e] = (bf16)qv;
+      }
+      *reinterpret_cast<bf16x8*>(u.kq.k + ar * SK + ks * 32 + lg * 8) = fk[ks];
+      *reinterpret_cast<bf16x8*>(u.kq.q + ar * SK + ks * 32 + lg * 8) = fq[ks];
+    }
   }
   ssk += __shfl_xor(ssk, 16);
   ssk += __shfl_xor(ssk, 32);
