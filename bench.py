@@ -166,39 +166,79 @@ def load_traffic(kernel, workload):
     return float(rec["bytes_per_step"])
 
 
-def cpu_baseline(w, inputs_dev):
-    """Time the FP64 oracle on a bounded sample of the workload: every document in full, for the
-    first few q/k heads (with their value heads), enough (document, head) items to occupy the host
-    cores. The oracle's cost per token and head is the same everywhere, so the whole workload's
-    rate is the sample's tokens x H / sampled heads over its time. Times fwd and bwd (the oracle's
-    reverse mode recomputes its forward) separately; fwd+bwd = both, ckpt = 2 fwd + bwd."""
-    import numpy as np
-    import torch
+def _oracle_sample(w, inputs_dev, heads, ops=("fwd", "bwd")):
+    """Times the FP64 oracle on every document of the workload for q/k heads [0, heads) with their
+    value heads. Returns (seconds per op, threads used, value heads sampled)."""
     import oracle
 
     threads = oracle.default_threads()
-    heads = max(1, min(w.H, math.ceil(threads / max(1, w.N))))
     Gg = w.HV // w.H
     vh = [j * Gg + gi for j in range(heads) for gi in range(Gg)]
     f = lambda name, idx: inputs_dev[name][:, idx].float().cpu().numpy()
     q, k = f("q", list(range(heads))), f("k", list(range(heads)))
     v, g, b, dO = (f(x, vh) for x in ("v", "g", "beta", "dO"))
     h0 = inputs_dev["h0"][:, vh].float().cpu().numpy() if inputs_dev.get("h0") is not None else None
+    dht = inputs_dev["dht"][:, vh].float().cpu().numpy() if inputs_dev.get("dht") is not None else None
     cu = inputs_dev["cu_seqlens"].cpu().numpy()
     used = min(threads, w.N * heads)  # the oracle splits work over (document, q/k head) items
-    t0 = time.time()
-    oracle.fwd(cu, q, k, v, g, b, h0, l2norm=w.l2norm, threads=threads)
-    t_f = time.time() - t0
-    t0 = time.time()
-    oracle.bwd(cu, q, k, v, g, b, dO, h0, None, l2norm=w.l2norm, threads=threads)
-    t_b = time.time() - t0
+    t = {}
+    if "fwd" in ops:
+        t0 = time.time()
+        oracle.fwd(cu, q, k, v, g, b, h0, l2norm=w.l2norm, threads=threads)
+        t["fwd"] = time.time() - t0
+    if "bwd" in ops:
+        t0 = time.time()
+        oracle.bwd(cu, q, k, v, g, b, dO, h0, dht, l2norm=w.l2norm, threads=threads)
+        t["bwd"] = time.time() - t0
+    return t, used, len(vh)
+
+
+def cpu_baseline(w, inputs_dev):
+    """Time the FP64 oracle on a bounded sample of the workload: every document in full, for the
+    first few q/k heads (with their value heads), enough (document, head) items to occupy the host
+    cores. The oracle's cost per token and head is the same everywhere, so the whole workload's
+    rate is the sample's tokens x H / sampled heads over its time. Times fwd and bwd (the oracle's
+    reverse mode recomputes its forward) separately; fwd+bwd = both, ckpt = 2 fwd + bwd."""
+    import oracle
+
+    threads = oracle.default_threads()
+    heads = max(1, min(w.H, math.ceil(threads / max(1, w.N))))
+    t, used, nvh = _oracle_sample(w, inputs_dev, heads)
+    t_f, t_b = t["fwd"], t["bwd"]
     scale = w.H / heads  # whole-workload time = sample time x this
     rate = lambda t: w.T / (t * scale)
     return {"value": rate(t_f + t_b), "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": "fwd+bwd of all %d documents (%d tokens) for q/k heads 0..%d of %d with their %d value heads, "
                       "d=%d, FP64 token recurrence: fwd %.1f s + bwd %.1f s; tokens/s scaled by %d/%d heads"
-                      % (w.N, w.T, heads - 1, w.H, len(vh), w.d, t_f, t_b, w.H, heads),
+                      % (w.N, w.T, heads - 1, w.H, nvh, w.d, t_f, t_b, w.H, heads),
             "fwd_tokens_per_s": rate(t_f), "ckpt_tokens_per_s": rate(2 * t_f + t_b), "threads": threads}
+
+
+# The other workloads' oracle rates: q/k heads sampled per workload so that each takes a few
+# seconds of host time (the oracle's cost is per token and value head).
+CPU_CONFIG_HEADS = {"tiny": 2, "single8k": 16, "cp4share": 8, "short512": 2}
+
+
+def cpu_configs(dev):
+    """The FP64 oracle's fwd, fwd+bwd and ckpt (2 fwd + bwd) rates on each other workload, on a
+    bounded sample (all documents, the first q/k heads), scaled to the whole workload."""
+    import synthetic as syn
+
+    out = {}
+    for name, heads in CPU_CONFIG_HEADS.items():
+        w = syn.WORKLOADS[name]
+        heads = min(heads, w.H)
+        inp = syn.make_inputs(w, device=dev)
+        t, used, nvh = _oracle_sample(w, inp, heads)
+        del inp
+        scale = w.H / heads
+        rate = lambda x: w.T / (x * scale)
+        out[name] = {"fwd_tokens_per_s": rate(t["fwd"]), "fwdbwd_tokens_per_s": rate(t["fwd"] + t["bwd"]),
+                     "ckpt_tokens_per_s": rate(2 * t["fwd"] + t["bwd"]), "cores": used,
+                     "sample": "all %d documents (%d tokens), q/k heads 0..%d of %d (%d value heads): fwd %.2f s, "
+                               "bwd %.2f s; scaled by %d/%d heads" % (w.N, w.T, heads - 1, w.H, nvh, t["fwd"],
+                                                                     t["bwd"], w.H, heads)}
+    return out
 
 
 COPY_BYTES = 1 << 30  # bytes read (and written) by the calibration copy
@@ -757,6 +797,8 @@ def main():
         inp = syn.make_inputs(w, device=dev)
         out["cpu_baseline"] = cpu_baseline(w, inp)
         del inp
+        if not args.no_extra:
+            out["cpu_baseline"]["configs"] = cpu_configs(dev)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

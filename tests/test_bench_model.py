@@ -79,3 +79,14 @@ def test_roofline_is_bytes_per_step_over_span():
     one = {"gdn_chunk_grad": {"launches_per_step": 1.0, "sum_ms_per_step": 10.5, "span_ms_per_step": 10.5,
                               "avg_launch_ms": 10.5}}
     assert abs(bench.roofline_of(one, models, "no-such-workload", False)["achieved"] - r["achieved"]) < 1e-9
+
+
+def test_cpu_config_rates_on_the_tiny_workload(monkeypatch):
+    """The per-workload oracle rates: every op's rate is the workload's tokens over the scaled sample
+    time, so ckpt (2 fwd + bwd) < fwd+bwd < fwd, and the sample covers the heads asked for."""
+    monkeypatch.setattr(bench, "CPU_CONFIG_HEADS", {"tiny": 1})
+    out = bench.cpu_configs("cpu")
+    r = out["tiny"]
+    assert set(r) >= {"fwd_tokens_per_s", "fwdbwd_tokens_per_s", "ckpt_tokens_per_s", "cores", "sample"}
+    assert 0 < r["ckpt_tokens_per_s"] < r["fwdbwd_tokens_per_s"] < r["fwd_tokens_per_s"]
+    assert "q/k heads 0..0 of 2 (1 value heads)" in r["sample"] and "scaled by 2/1 heads" in r["sample"]
